@@ -1,0 +1,68 @@
+// Weighted unpermute: out[t] = S(x_t) + sum_j w[t,j] * Y[row_of_pair[t*k+j]].
+//
+// "Kolibri 1 Deep Dive" (abrarakhunji.com), "Mathematical Routing & Load
+// Balancing Formulation": the layer output is the gate-weighted sum of the
+// selected experts' SwiGLU outputs; "Inside Kolibri 1" (flozi.net), section
+// "The released stack": the shared expert is added for every token.  The sum
+// runs in FP32 in a fixed order (shared, then slots 0..k-1) and is rounded
+// once to the output type; with MOE_FLAG_ACCUMULATE the old output (the
+// residual stream) is added before that rounding.
+#include "moe_common.h"
+#include "moe_plan.h"
+
+namespace fgs {
+
+template <bool BF16OUT>
+__global__ __launch_bounds__(256) void combine_kernel(
+    const float *__restrict__ Y, const float *__restrict__ tw, const int32_t *__restrict__ rop, void *out,
+    int N, int d, int k, bool accumulate) {
+    const int t = blockIdx.x;
+    __shared__ float ws[8];
+    __shared__ int rs[8];
+    if (threadIdx.x < k) {
+        ws[threadIdx.x] = tw[(size_t)t * k + threadIdx.x];
+        rs[threadIdx.x] = rop[(size_t)t * k + threadIdx.x];
+    }
+    __syncthreads();
+    const size_t shared_row = (size_t)N * k + t;
+    for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
+        float4 a = *reinterpret_cast<const float4 *>(Y + shared_row * d + c);
+        for (int j = 0; j < k; ++j) {
+            const float wj = ws[j];
+            const float4 y = *reinterpret_cast<const float4 *>(Y + (size_t)rs[j] * d + c);
+            a.x = fmaf(wj, y.x, a.x);
+            a.y = fmaf(wj, y.y, a.y);
+            a.z = fmaf(wj, y.z, a.z);
+            a.w = fmaf(wj, y.w, a.w);
+        }
+        if (BF16OUT) {
+            uint2 *o = reinterpret_cast<uint2 *>((uint16_t *)out + (size_t)t * d + c);
+            if (accumulate) {
+                uint2 old = *o;
+                a.x += bf16_lo(old.x); a.y += bf16_hi(old.x);
+                a.z += bf16_lo(old.y); a.w += bf16_hi(old.y);
+            }
+            *o = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
+        } else {
+            float4 *o = reinterpret_cast<float4 *>((float *)out + (size_t)t * d + c);
+            if (accumulate) {
+                float4 old = *o;
+                a.x += old.x; a.y += old.y; a.z += old.z; a.w += old.w;
+            }
+            *o = a;
+        }
+    }
+}
+
+hipError_t launch_combine(const Plan &p) {
+    const bool acc = (p.flags & MOE_FLAG_ACCUMULATE) != 0;
+    if (p.xdt == MOE_DTYPE_BF16)
+        hipLaunchKernelGGL((combine_kernel<true>), dim3(p.N), dim3(256), 0, p.stream, p.Y, p.tw, p.rop, p.out, p.N,
+                           p.d, p.k, acc);
+    else
+        hipLaunchKernelGGL((combine_kernel<false>), dim3(p.N), dim3(256), 0, p.stream, p.Y, p.tw, p.rop, p.out, p.N,
+                           p.d, p.k, acc);
+    return hipGetLastError();
+}
+
+}  // namespace fgs

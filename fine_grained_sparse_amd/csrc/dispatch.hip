@@ -1,0 +1,209 @@
+// Token-choice dispatch without capacity: histogram -> scan -> stable scatter.
+//
+// "Inside Kolibri 1" (flozi.net), section "Routing: selection bias and
+// mixture weights are separate": routing is token-choice top-k with no exact
+// per-batch capacity per expert, so every (token, slot) pair is kept and the
+// per-expert row counts are whatever the selection produced (zero included).
+//
+// Layout (a stable counting sort of pairs p = t*k + j by expert id):
+//   offsets[e]      first row of expert e; offsets[E] = N*k
+//   offsets[E+1]    = N*k + N: rows [N*k, N*k + N) belong to the shared
+//                   expert, token t at row N*k + t (the "group" E)
+//   pair_of_row[r]  pair stored at row r;  row_of_pair[p] its inverse
+// Within an expert, rows follow increasing token index.  The rank of a pair
+// inside its 256-token block comes from a per-expert token bitmap (popcount of
+// the lower tokens), so no atomic order ever reaches the output.
+//
+// The scan also writes the tile list of the expert kernels: one entry
+// (group, first row within the group) per `bm` rows of every non-empty group.
+#include "moe_common.h"
+#include "moe_plan.h"
+
+namespace fgs {
+
+constexpr int kBT = 256;     // tokens per dispatch block
+constexpr int kBTW = kBT / 32;
+
+// Exclusive scan of v[0..L) in LDS, L <= 2 * blockDim.x, blockDim.x == 1024.
+// Returns the total.  `wsum` needs 16 ints.
+__device__ int block_exclusive_scan_1024(int *v, int L, int *wsum) {
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int i0 = 2 * tid;
+    int a = i0 < L ? v[i0] : 0;
+    int b = i0 + 1 < L ? v[i0 + 1] : 0;
+    int local = a + b;
+    int inc = local;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+        int o = __shfl_up(inc, s, kWave);
+        if (lane >= s) inc += o;
+    }
+    if (lane == 63) wsum[wid] = inc;
+    __syncthreads();
+    if (wid == 0) {
+        int w = lane < 16 ? wsum[lane] : 0;
+        int winc = w;
+#pragma unroll
+        for (int s = 1; s < 16; s <<= 1) {
+            int o = __shfl_up(winc, s, kWave);
+            if (lane >= s) winc += o;
+        }
+        if (lane < 16) wsum[lane] = winc - w;  // exclusive wave bases
+        if (lane == 15) wsum[16] = winc;       // total
+    }
+    __syncthreads();
+    int base = wsum[wid] + inc - local;
+    if (i0 < L) v[i0] = base;
+    if (i0 + 1 < L) v[i0 + 1] = base + a;
+    int total = wsum[16];
+    __syncthreads();
+    return total;
+}
+
+// After `cnt[0..E)` holds per-expert counts (LDS): offsets, tile list.
+// `scratch` >= 2*(E+1)+... ints of LDS.  Leaves offsets in off[0..E+2).
+__device__ void offsets_and_tiles(const int *cnt, int *off, int *ntile, int *wsum, int N, int k, int E,
+                                  int bm, int32_t *g_offsets, int32_t *g_exp_off, int32_t *tiles,
+                                  int32_t *n_tiles) {
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += blockDim.x) off[e] = cnt[e];
+    __syncthreads();
+    int total = block_exclusive_scan_1024(off, E, wsum);
+    if (tid == 0) {
+        off[E] = total;          // == N*k
+        off[E + 1] = total + N;  // shared expert rows
+    }
+    __syncthreads();
+    for (int e = tid; e < E + 2; e += blockDim.x) {
+        g_offsets[e] = off[e];
+        if (g_exp_off && e <= E) g_exp_off[e] = off[e];
+    }
+    // tiles per group (routed groups 0..E-1, shared group E with N rows)
+    for (int g = tid; g <= E; g += blockDim.x) {
+        int m = off[g + 1] - off[g];
+        ntile[g] = (m + bm - 1) / bm;
+    }
+    __syncthreads();
+    int nt = block_exclusive_scan_1024(ntile, E + 1, wsum);
+    for (int g = tid; g <= E; g += blockDim.x) {
+        int m = off[g + 1] - off[g];
+        int start = ntile[g];
+        for (int i = 0; i * bm < m; ++i) {
+            tiles[2 * (start + i)] = g;
+            tiles[2 * (start + i) + 1] = i * bm;
+        }
+    }
+    if (tid == 0) *n_tiles = nt;
+}
+
+// Rank of every pair of one block inside its expert, then the scatter.
+__device__ void block_scatter(const int32_t *ids, uint32_t *bits, const int *base, int b, int N, int k, int E,
+                              int32_t *por, int32_t *rop) {
+    const int tid = threadIdx.x;
+    for (int i = tid; i < E * kBTW; i += blockDim.x) bits[i] = 0;
+    __syncthreads();
+    const int t = b * kBT + tid;
+    const bool live = tid < kBT && t < N;
+    if (live)
+        for (int j = 0; j < k; ++j) {
+            int e = ids[(size_t)t * k + j];
+            atomicOr(&bits[e * kBTW + (tid >> 5)], 1u << (tid & 31));
+        }
+    __syncthreads();
+    if (live)
+        for (int j = 0; j < k; ++j) {
+            int e = ids[(size_t)t * k + j];
+            const uint32_t *row = bits + e * kBTW;
+            int rank = __popc(row[tid >> 5] & ((1u << (tid & 31)) - 1u));
+            for (int w = 0; w < (tid >> 5); ++w) rank += __popc(row[w]);
+            int pos = base[e] + rank;
+            por[pos] = t * k + j;
+            rop[(size_t)t * k + j] = pos;
+        }
+}
+
+// ---- one-block path (N <= 256): everything in one workgroup of 1024 threads
+
+__global__ __launch_bounds__(1024) void dispatch_fused_kernel(
+    const int32_t *__restrict__ ids, int N, int k, int E, int bm, int32_t *g_offsets, int32_t *g_exp_off,
+    int32_t *tiles, int32_t *n_tiles, int32_t *por, int32_t *rop) {
+    __shared__ int cnt[1024];
+    __shared__ int off[1026];
+    __shared__ int ntile[1025];
+    __shared__ int wsum[17];
+    __shared__ uint32_t bits[1024 * kBTW];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    for (int i = tid; i < N * k; i += blockDim.x) atomicAdd(&cnt[ids[i]], 1);
+    __syncthreads();
+    offsets_and_tiles(cnt, off, ntile, wsum, N, k, E, bm, g_offsets, g_exp_off, tiles, n_tiles);
+    __syncthreads();
+    block_scatter(ids, bits, off, 0, N, k, E, por, rop);
+}
+
+// ---- multi-block path
+
+__global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t *__restrict__ ids, int N, int k, int E,
+                                                            int32_t *__restrict__ blk) {
+    __shared__ int cnt[1024];
+    const int tid = threadIdx.x, b = blockIdx.x;
+    for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    const int t = b * kBT + tid;
+    if (t < N)
+        for (int j = 0; j < k; ++j) atomicAdd(&cnt[ids[(size_t)t * k + j]], 1);
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) blk[(size_t)b * E + e] = cnt[e];
+}
+
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t *blk, int nblk, int N, int k, int E, int bm,
+                                                             int32_t *g_offsets, int32_t *g_exp_off,
+                                                             int32_t *tiles, int32_t *n_tiles) {
+    __shared__ int cnt[1024];
+    __shared__ int off[1026];
+    __shared__ int ntile[1025];
+    __shared__ int wsum[17];
+    const int tid = threadIdx.x;
+    // per expert: exclusive prefix over blocks (in place), total count
+    for (int e = tid; e < E; e += blockDim.x) {
+        int run = 0;
+        for (int b = 0; b < nblk; ++b) {
+            int c = blk[(size_t)b * E + e];
+            blk[(size_t)b * E + e] = run;
+            run += c;
+        }
+        cnt[e] = run;
+    }
+    __syncthreads();
+    offsets_and_tiles(cnt, off, ntile, wsum, N, k, E, bm, g_offsets, g_exp_off, tiles, n_tiles);
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x)
+        for (int b = 0; b < nblk; ++b) blk[(size_t)b * E + e] += off[e];
+}
+
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t *__restrict__ ids, const int32_t *blk,
+                                                               int N, int k, int E, int32_t *por, int32_t *rop) {
+    __shared__ uint32_t bits[1024 * kBTW];
+    block_scatter(ids, bits, blk + (size_t)blockIdx.x * E, blockIdx.x, N, k, E, por, rop);
+}
+
+hipError_t launch_dispatch(const Plan &p) {
+    if (p.nblk == 1) {
+        hipLaunchKernelGGL(dispatch_fused_kernel, dim3(1), dim3(1024), 0, p.stream, p.ids, p.N, p.k, p.E, p.bm,
+                           p.offsets, p.exp_off_out, p.tiles, p.n_tiles, p.por, p.rop);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(dispatch_hist_kernel, dim3(p.nblk), dim3(256), 0, p.stream, p.ids, p.N, p.k, p.E, p.blk);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, p.stream, p.blk, p.nblk, p.N, p.k, p.E, p.bm,
+                       p.offsets, p.exp_off_out, p.tiles, p.n_tiles);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(p.nblk), dim3(256), 0, p.stream, p.ids, p.blk, p.N, p.k, p.E,
+                       p.por, p.rop);
+    return hipGetLastError();
+}
+
+}  // namespace fgs

@@ -1,0 +1,194 @@
+// C ABI of the MoE layer: argument checks, workspace carving, launch order.
+// The declarations and their documentation are in include/fgs_moe.h.
+#include <atomic>
+#include <cstring>
+
+#include "moe_plan.h"
+
+namespace fgs {
+namespace {
+
+thread_local int g_last_hip_error = 0;
+std::atomic<int> g_arch_state[64];  // 0 unknown, 1 gfx950, 2 other
+
+constexpr int kStreamMaxN = 64;     // decode-shaped expert path up to this batch
+
+int check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) { g_last_hip_error = (int)e; return MOE_ERR_HIP; }
+    if (dev < 0 || dev >= 64) return MOE_ERR_UNSUPPORTED;
+    int st = g_arch_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) { g_last_hip_error = (int)e; return MOE_ERR_HIP; }
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch_state[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_desc(const moe_desc *d) {
+    if (!d) return MOE_ERR_ARG;
+    if (d->n_tokens < 0 || d->n_experts < 1 || d->n_experts > 1024) return MOE_ERR_ARG;
+    if (d->top_k < 1 || d->top_k > 8 || d->top_k > d->n_experts) return MOE_ERR_ARG;
+    if (d->d_model <= 0 || d->d_model % 64 || d->d_ff <= 0 || d->d_ff % 64 || d->d_ff_shared <= 0 ||
+        d->d_ff_shared % 64)
+        return MOE_ERR_ARG;
+    if ((long)d->n_tokens * d->top_k + d->n_tokens >= (1L << 31)) return MOE_ERR_ARG;
+    if (d->flags & ~MOE_FLAG_ACCUMULATE) return MOE_ERR_ARG;
+    if (d->x_dtype != MOE_DTYPE_F32 && d->x_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (d->w_dtype != MOE_DTYPE_BF16 && d->w_dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+    // decode-shaped expert kernels: whole rows live in registers / LDS
+    if (d->d_model > 4096 || d->d_ff > 512 || d->d_ff_shared > 512) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+struct Layout {
+    size_t partial, ids, tw, blk, offsets, tiles, n_tiles, por, rop, H, Y, total;
+    int ks, kslice, nblk, max_tiles, bm, ldh;
+};
+
+size_t take(size_t &cur, size_t bytes) {
+    size_t at = cur;
+    cur += (bytes + 255) & ~size_t(255);
+    return at;
+}
+
+Layout layout_for(const moe_desc *d) {
+    Layout L{};
+    const size_t N = d->n_tokens, E = d->n_experts, k = d->top_k;
+    if (d->x_dtype == MOE_DTYPE_F32) {
+        L.ks = 1;
+    } else {
+        L.ks = router_tiling(d->n_tokens, d->d_model, d->n_experts).ks;
+    }
+    L.kslice = d->d_model / L.ks;
+    L.nblk = (int)((N + 255) / 256);
+    if (L.nblk < 1) L.nblk = 1;
+    L.bm = d->n_tokens <= kStreamMaxN ? (d->n_tokens > 0 ? d->n_tokens : 1) : 32;
+    L.max_tiles = max_tiles_for(d->n_tokens, d->top_k, d->n_experts, L.bm);
+    L.ldh = d->d_ff > d->d_ff_shared ? d->d_ff : d->d_ff_shared;
+    const size_t rows = N * k + N;
+    size_t cur = 0;
+    L.partial = take(cur, (size_t)L.ks * N * E * 4);
+    L.ids = take(cur, N * k * 4);
+    L.tw = take(cur, N * k * 4);
+    L.blk = take(cur, (size_t)L.nblk * E * 4);
+    L.offsets = take(cur, (E + 2) * 4);
+    L.tiles = take(cur, (size_t)L.max_tiles * 2 * 4);
+    L.n_tiles = take(cur, 4);
+    L.por = take(cur, N * k * 4);
+    L.rop = take(cur, N * k * 4);
+    L.H = take(cur, rows * L.ldh * 2);
+    L.Y = take(cur, rows * (size_t)d->d_model * 4);
+    L.total = cur;
+    return L;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    uintptr_t x0 = (uintptr_t)a, x1 = x0 + na, y0 = (uintptr_t)b, y1 = y0 + nb;
+    return x0 < y1 && y0 < x1;
+}
+
+}  // namespace
+}  // namespace fgs
+
+using namespace fgs;
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_desc *desc) {
+    if (check_desc(desc) != MOE_OK) return 0;
+    return layout_for(desc).total;
+}
+
+const char *moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported configuration or device";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+int moe_forward(const moe_desc *desc, const void *x, const float *router_w, const float *router_bias,
+                const moe_weights *weights, void *out, void *workspace, size_t workspace_bytes,
+                const moe_aux *aux, void *stream) {
+    int st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    if (desc->n_tokens == 0) return MOE_OK;
+    if (!x || !router_w || !router_bias || !weights || !out || !workspace) return MOE_ERR_ARG;
+    const moe_weights &W = *weights;
+    if (!W.w_gate || !W.w_up || !W.w_down || !W.ws_gate || !W.ws_up || !W.ws_down) return MOE_ERR_ARG;
+    const bool fp8 = desc->w_dtype == MOE_DTYPE_FP8_E4M3;
+    const bool have_scales[6] = {W.s_gate != nullptr, W.s_up != nullptr, W.s_down != nullptr,
+                                 W.ss_gate != nullptr, W.ss_up != nullptr, W.ss_down != nullptr};
+    for (bool h : have_scales)
+        if (h != fp8) return MOE_ERR_ARG;
+    const void *ptrs16[] = {x, out, W.w_gate, W.w_up, W.w_down, W.ws_gate, W.ws_up, W.ws_down, router_w};
+    for (const void *q : ptrs16)
+        if (!aligned(q, 16)) return MOE_ERR_ARG;
+    if (!aligned(workspace, 256)) return MOE_ERR_ARG;
+
+    const size_t xbytes = (size_t)desc->n_tokens * desc->d_model * (desc->x_dtype == MOE_DTYPE_F32 ? 4 : 2);
+    if (overlaps(x, xbytes, out, xbytes)) {
+        if (!(desc->flags & MOE_FLAG_ACCUMULATE) || x != out) return MOE_ERR_ARG;
+    }
+    const Layout L = layout_for(desc);
+    if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+    st = check_device();
+    if (st != MOE_OK) return st;
+
+    char *ws = (char *)workspace;
+    Plan p{};
+    p.N = desc->n_tokens; p.d = desc->d_model; p.E = desc->n_experts; p.k = desc->top_k;
+    p.f = desc->d_ff; p.fs = desc->d_ff_shared; p.xdt = desc->x_dtype; p.wdt = desc->w_dtype;
+    p.flags = desc->flags;
+    p.x = x; p.rw = router_w; p.rb = router_bias; p.W = W; p.out = out;
+    p.partial = (float *)(ws + L.partial);
+    p.ks = L.ks; p.kslice = L.kslice;
+    p.logits = aux ? aux->logits : nullptr;
+    p.ids = (aux && aux->topk_ids) ? aux->topk_ids : (int32_t *)(ws + L.ids);
+    p.tw = (aux && aux->topk_w) ? aux->topk_w : (float *)(ws + L.tw);
+    p.gap = aux ? aux->gap : nullptr;
+    p.blk = (int32_t *)(ws + L.blk); p.nblk = L.nblk;
+    p.offsets = (int32_t *)(ws + L.offsets);
+    p.exp_off_out = aux ? aux->expert_offsets : nullptr;
+    p.tiles = (int32_t *)(ws + L.tiles); p.n_tiles = (int32_t *)(ws + L.n_tiles);
+    p.max_tiles = L.max_tiles; p.bm = L.bm;
+    p.por = (aux && aux->pair_of_row) ? aux->pair_of_row : (int32_t *)(ws + L.por);
+    p.rop = (aux && aux->row_of_pair) ? aux->row_of_pair : (int32_t *)(ws + L.rop);
+    p.H = (uint16_t *)(ws + L.H); p.ldh = L.ldh;
+    p.Y = (float *)(ws + L.Y);
+    p.use_stream = true;
+    p.stream = (hipStream_t)stream;
+
+    void **ev = (aux && aux->stage_events) ? aux->stage_events : nullptr;
+    typedef hipError_t (*Stage)(const Plan &);
+    const Stage stages[MOE_NUM_STAGES] = {launch_router, launch_topk, launch_dispatch,
+                                          launch_gate_up, launch_down, launch_combine};
+    for (int s = 0; s < MOE_NUM_STAGES; ++s) {
+        hipError_t e;
+        if (ev && ev[2 * s]) {
+            e = hipEventRecord((hipEvent_t)ev[2 * s], p.stream);
+            if (e != hipSuccess) { g_last_hip_error = (int)e; return MOE_ERR_HIP; }
+        }
+        e = stages[s](p);
+        if (e != hipSuccess) { g_last_hip_error = (int)e; return MOE_ERR_HIP; }
+        if (ev && ev[2 * s + 1]) {
+            e = hipEventRecord((hipEvent_t)ev[2 * s + 1], p.stream);
+            if (e != hipSuccess) { g_last_hip_error = (int)e; return MOE_ERR_HIP; }
+        }
+    }
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Host-side description of one moe_forward call, shared by the launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fgs_moe.h"
+
+namespace fgs {
+
+struct Plan {
+    // problem
+    int N, d, E, k, f, fs;
+    int xdt, wdt;
+    uint32_t flags;
+    // caller buffers
+    const void *x;
+    const float *rw, *rb;
+    moe_weights W;
+    void *out;
+    // routing buffers (caller's aux buffers when given, else workspace)
+    float *partial;      // [ks][N][E] router partial sums over k-slices
+    int ks;              // number of k-slices of the router
+    int kslice;          // k-slice length (d / ks)
+    float *logits;       // [N][E] or nullptr
+    int32_t *ids;        // [N][k]
+    float *tw;           // [N][k]
+    float *gap;          // [N] or nullptr
+    int32_t *blk;        // [nblk][E] per-block counts, then absolute bases
+    int nblk;
+    int32_t *offsets;    // [E+2]: routed groups, then the shared group's rows
+    int32_t *exp_off_out;// caller's [E+1] copy, or nullptr
+    int32_t *tiles;      // [max_tiles] packed (group << 16... see dispatch) entries
+    int32_t *n_tiles;    // [1]
+    int max_tiles;
+    int bm;              // rows per tile of the expert kernels
+    int32_t *por, *rop;  // [N*k]
+    uint16_t *H;         // [N*k + N][ldh] bfloat16 SwiGLU activations
+    int ldh;
+    float *Y;            // [N*k + N][d] float32 expert outputs
+    bool use_stream;     // decode-shaped expert path
+    hipStream_t stream;
+};
+
+// launchers (each returns the hipError_t of its launch)
+hipError_t launch_router(const Plan &p);
+hipError_t launch_topk(const Plan &p);
+hipError_t launch_dispatch(const Plan &p);
+hipError_t launch_gate_up(const Plan &p);
+hipError_t launch_down(const Plan &p);
+hipError_t launch_combine(const Plan &p);
+
+// Router tiling: wave tile of (16*MT tokens) x (16*NT experts); the k range is
+// cut into ks slices so that small batches still spread over many waves.
+struct RouterTiling { int mt, nt, ks; };
+inline RouterTiling router_tiling(int N, int d, int E) {
+    RouterTiling r;
+    if (N <= 32) { r.mt = 2; r.nt = 1; } else { r.mt = 4; r.nt = 4; }
+    long n_tb = (N + 16 * r.mt - 1) / (16 * r.mt);
+    long n_eb = (E + 16 * r.nt - 1) / (16 * r.nt);
+    long tiles = n_tb * n_eb;
+    r.ks = 1;
+    const int cands[] = {10, 8, 5, 4, 2};
+    if (tiles < 512) {
+        for (int c : cands) {
+            if ((d / 32) % c == 0 && tiles * c <= 2048) { r.ks = c; break; }
+        }
+    }
+    return r;
+}
+
+// largest tile-list length for a given row tile
+inline int max_tiles_for(int N, int k, int E, int bm) {
+    long nk = (long)N * k;
+    long routed = (nk + bm - 1) / bm + (nk < E ? nk : E);
+    long shared = (N + bm - 1) / bm;
+    return (int)(routed + shared);
+}
+
+}  // namespace fgs

@@ -1,0 +1,131 @@
+// Bias-corrected top-k selection and sigmoid mixture weights.
+//
+// "Inside Kolibri 1" (flozi.net), section "Routing: selection bias and
+// mixture weights are separate": (1) add the learned expert-correction bias to
+// the logits and select the top six ids; (2) gather the unbiased logits of
+// those ids, apply a sigmoid and use the results as mixture weights without
+// renormalising them.
+//
+// One wave per token.  Lane l owns experts l, l+64, l+128, ...  Each of the
+// k+1 rounds takes the wave-wide maximum of a 64-bit key built from the score
+// (order-preserving bit map, -0 folded onto +0) and the complemented expert
+// id, so equal scores go to the lower id and the result is independent of the
+// reduction order.  The (k+1)-th round only yields the selection gap.
+#include "moe_common.h"
+#include "moe_plan.h"
+
+namespace fgs {
+
+__device__ __forceinline__ uint32_t orderable(float s) {
+    if (s == 0.0f) s = 0.0f;  // -0 and +0 compare equal
+    uint32_t u = __float_as_uint(s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_orderable(uint32_t o) {
+    uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+    return __uint_as_float(u);
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void topk_kernel(
+    const float *__restrict__ partial, int ks, const float *__restrict__ bias,
+    float *__restrict__ logits_out, int32_t *__restrict__ ids, float *__restrict__ tw,
+    float *__restrict__ gap, int N, int E, int k) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= N) return;
+
+    float h[VPL];
+    uint64_t key[VPL];
+    const size_t slice = (size_t)N * E;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        int e = lane + 64 * v;
+        if (e < E) {
+            const float *src = partial + (size_t)t * E + e;
+            float acc = src[0];
+            for (int s = 1; s < ks; ++s) acc += src[s * slice];
+            h[v] = acc;
+            if (logits_out) logits_out[(size_t)t * E + e] = acc;
+            float sc = acc + bias[e];
+            key[v] = ((uint64_t)orderable(sc) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+        } else {
+            h[v] = 0.f;
+            key[v] = 0;  // below every real key
+        }
+    }
+
+    // k <= 8: fully unrolled rounds keep every array in registers
+    int sel[8];
+    float selh[8];
+    float sk = 0.f, sk1 = 0.f;
+    const int rounds = (k < E) ? k + 1 : k;
+#pragma unroll
+    for (int r = 0; r < 9; ++r) {
+        if (r < 8) { sel[r] = 0x7FFFFFFF; selh[r] = 0.f; }
+        if (r >= rounds) continue;
+        uint64_t best = 0;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) best = key[v] > best ? key[v] : best;
+        best = wave_max_u64(best);
+        const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+        const float sc = from_orderable((uint32_t)(best >> 32));
+        if (r < k) {
+            // the owner lane retires the winner; everybody learns its logit
+            const int owner = e & 63, slot = e >> 6;
+            float hv = 0.f;
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                if (v == slot) {
+                    hv = h[v];
+                    if (lane == owner) key[v] = 0;
+                }
+            }
+            hv = __shfl(hv, owner, kWave);
+            if (r < 8) { sel[r] = e; selh[r] = hv; }
+            sk = sc;
+        } else {
+            sk1 = sc;
+        }
+    }
+
+    // ascending id order: compare-exchange network over the 8 slots (unused
+    // slots hold INT_MAX and sink to the end)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 7 - i; ++j) {
+            if (sel[j] > sel[j + 1]) {
+                int te = sel[j]; sel[j] = sel[j + 1]; sel[j + 1] = te;
+                float th = selh[j]; selh[j] = selh[j + 1]; selh[j + 1] = th;
+            }
+        }
+    if (lane < k) {
+        int e = 0;
+        float hv = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j == lane) { e = sel[j]; hv = selh[j]; }
+        ids[(size_t)t * k + lane] = e;
+        tw[(size_t)t * k + lane] = sigmoidf_(hv);
+    }
+    if (gap && lane == 0) gap[t] = (k < E) ? sk - sk1 : __builtin_inff();
+}
+
+hipError_t launch_topk(const Plan &p) {
+    dim3 grid((p.N + 3) / 4), block(256);
+    int vpl = (p.E + 63) / 64;
+#define FGS_TOPK(V)                                                                              \
+    hipLaunchKernelGGL((topk_kernel<V>), grid, block, 0, p.stream, p.partial, p.ks, p.rb,       \
+                       p.logits, p.ids, p.tw, p.gap, p.N, p.E, p.k)
+    if (vpl <= 1) FGS_TOPK(1);
+    else if (vpl <= 2) FGS_TOPK(2);
+    else if (vpl <= 4) FGS_TOPK(4);
+    else if (vpl <= 6) FGS_TOPK(6);
+    else if (vpl <= 8) FGS_TOPK(8);
+    else FGS_TOPK(16);
+#undef FGS_TOPK
+    return hipGetLastError();
+}
+
+}  // namespace fgs

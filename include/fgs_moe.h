@@ -1,0 +1,166 @@
+/*
+ * fgs_moe.h - C ABI of the fine-grained MoE feed-forward layer for MI355X
+ * (gfx950).  Plain pointers and sizes only; no C++ or framework types.
+ *
+ * The layer (one call = one MoE sublayer over N flattened tokens):
+ *
+ *   "Inside Kolibri 1: Hybrid RNoPE Attention, Sparse MoE, and FP8 Serving"
+ *   (flozi.net), section "Routing: selection bias and mixture weights are
+ *   separate":
+ *     1. logits h = x W_r^T in FP32, x [N, d], W_r [E, d];
+ *     2. the learned correction bias b is added, s = h + b, and the top_k
+ *        expert ids with the largest s are selected;
+ *     3. mixture weights are sigmoid(h) of the selected ids, from the
+ *        UNBIASED logits, not renormalised to sum one;
+ *     4. every selected (token, expert) pair is processed; there is no
+ *        per-expert capacity and no token is dropped;
+ *     5. each routed or shared expert is a SwiGLU MLP
+ *        W_down (SiLU(W_gate x) * (W_up x)), without biases.
+ *   Same page, section "The released stack": one shared expert is evaluated
+ *   for every token besides the routed ones.  Same page, section "The FP8 path
+ *   is explicitly mixed precision": FP8 E4M3 weights with FP32 scales, which
+ *   are applied exactly (never rounded to powers of two).
+ *   "Kolibri 1 Deep Dive" (abrarakhunji.com), "Mathematical Routing & Load
+ *   Balancing Formulation": the output is the gate-weighted sum of the
+ *   selected experts' outputs, added to the residual stream (the residual add
+ *   is the caller's, or MOE_FLAG_ACCUMULATE).
+ *
+ *   out[t] = S(x_t) + sum_{j<k} w[t,j] * E_{ids[t,j]}(x_t)
+ *
+ * Conventions fixed by this library where the pages are silent:
+ *   - equal scores select the lower expert id; the k ids of a token are
+ *     stored in ascending id order (slot j = j-th smallest id);
+ *   - the shared expert has coefficient 1;
+ *   - FP8 is OCP E4M3FN (bias 7, max 448, no infinities); a weight is
+ *     code * scale with one FP32 scale per output channel (row);
+ *   - the expert matmuls take bfloat16 activations (an FP32 x is rounded to
+ *     bfloat16 for the experts; the router always uses x as given);
+ *   - dispatch is a stable counting sort of pairs by (expert, token).
+ *
+ * Memory: every pointer is device memory owned by the caller.  The library
+ * allocates nothing, frees nothing and keeps no mutable global state besides
+ * a once-per-device cache of the device architecture check.
+ *
+ * Execution: all work is enqueued on `stream` (a hipStream_t; NULL = the
+ * default stream) without host synchronisation; results are valid once the
+ * stream reaches that point.  Device faults surface at the caller's next
+ * synchronisation.  Calls that share a workspace must be ordered on one
+ * stream.
+ */
+#ifndef FGS_MOE_H
+#define FGS_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_OK               0
+#define MOE_ERR_ARG         -1   /* null pointer, bad size, misaligned pointer, bad flag */
+#define MOE_ERR_UNSUPPORTED -2   /* dtype combination, or the device is not gfx950 */
+#define MOE_ERR_WORKSPACE   -3   /* workspace smaller than moe_workspace_size() */
+#define MOE_ERR_HIP         -4   /* a HIP call failed; see moe_last_hip_error() */
+
+/* element types */
+#define MOE_DTYPE_F32       0
+#define MOE_DTYPE_BF16      1
+#define MOE_DTYPE_FP8_E4M3  2
+
+/* flags */
+#define MOE_FLAG_ACCUMULATE  (1u << 0)  /* out = round(out + y) instead of out = round(y) */
+
+/* pipeline stages, for optional timing events */
+#define MOE_STAGE_ROUTER    0   /* router logits */
+#define MOE_STAGE_TOPK      1   /* bias-corrected top-k, sigmoid weights */
+#define MOE_STAGE_DISPATCH  2   /* histogram, scan, scatter */
+#define MOE_STAGE_GATE_UP   3   /* routed + shared gate/up projections and SwiGLU */
+#define MOE_STAGE_DOWN      4   /* routed + shared down projections */
+#define MOE_STAGE_COMBINE   5   /* weighted unpermute into out */
+#define MOE_NUM_STAGES      6
+
+/* Problem description.
+ * Limits: n_tokens >= 0 (0 is a no-op); 1 <= top_k <= min(n_experts, 8);
+ * 1 <= n_experts <= 1024; d_model, d_ff and d_ff_shared positive multiples
+ * of 64; n_tokens * top_k < 2^31.
+ * x_dtype: MOE_DTYPE_F32 or MOE_DTYPE_BF16 (out has the same type).
+ * w_dtype: MOE_DTYPE_BF16 or MOE_DTYPE_FP8_E4M3 (routed and shared experts). */
+typedef struct moe_desc {
+    int32_t  n_tokens;     /* N */
+    int32_t  d_model;      /* d (2560 in the pages' layer) */
+    int32_t  n_experts;    /* E routed experts (384) */
+    int32_t  top_k;        /* k (6) */
+    int32_t  d_ff;         /* routed expert width f (512) */
+    int32_t  d_ff_shared;  /* shared expert width f_s (512) */
+    int32_t  x_dtype;
+    int32_t  w_dtype;
+    uint32_t flags;
+} moe_desc;
+
+/* Expert weights, row-major [out][in], element type desc->w_dtype.
+ * Scales (FP32, one per output channel) are required for FP8 and must be
+ * NULL for bfloat16.  All weight pointers 16-byte aligned. */
+typedef struct moe_weights {
+    const void  *w_gate;   /* [E][f][d] */
+    const void  *w_up;     /* [E][f][d] */
+    const void  *w_down;   /* [E][d][f] */
+    const float *s_gate;   /* [E][f]   FP8 only */
+    const float *s_up;     /* [E][f]   FP8 only */
+    const float *s_down;   /* [E][d]   FP8 only */
+    const void  *ws_gate;  /* [f_s][d] shared expert */
+    const void  *ws_up;    /* [f_s][d] */
+    const void  *ws_down;  /* [d][f_s] */
+    const float *ss_gate;  /* [f_s]    FP8 only */
+    const float *ss_up;    /* [f_s]    FP8 only */
+    const float *ss_down;  /* [d]      FP8 only */
+} moe_weights;
+
+/* Optional outputs (every member may be NULL; the struct pointer may be NULL).
+ * They expose the intermediate results of the call for inspection. */
+typedef struct moe_aux {
+    float   *logits;          /* [N][E] FP32 router logits h (unbiased) */
+    int32_t *topk_ids;        /* [N][k] selected ids, ascending per token */
+    float   *topk_w;          /* [N][k] sigmoid(h) at those ids */
+    float   *gap;             /* [N] k-th minus (k+1)-th best biased score (+inf if k == E) */
+    int32_t *expert_offsets;  /* [E+1] start row of each expert in the sorted buffer */
+    int32_t *pair_of_row;     /* [N*k] pair t*k+j stored at each sorted row */
+    int32_t *row_of_pair;     /* [N*k] sorted row of each pair t*k+j */
+    void   **stage_events;    /* [2*MOE_NUM_STAGES] hipEvent_t or NULL each: recorded on
+                                 `stream` before (2s) and after (2s+1) stage s */
+} moe_aux;
+
+/* Workspace bytes moe_forward needs for this description (0 on a bad
+ * description).  Pure host function; touches no device. */
+size_t moe_workspace_size(const moe_desc *desc);
+
+/* One MoE sublayer:  out[t] = S(x_t) + sum_j w[t,j] E_{ids[t,j]}(x_t)
+ * (plus the old out[t] with MOE_FLAG_ACCUMULATE), rounded once to x_dtype.
+ *   x           [N][d]  x_dtype, 16-byte aligned
+ *   router_w    [E][d]  FP32
+ *   router_bias [E]     FP32 expert-correction bias
+ *   weights     expert and shared-expert weights (above)
+ *   out         [N][d]  x_dtype; must not overlap x unless ACCUMULATE is set
+ *               and x == out (in-place residual)
+ *   workspace   >= moe_workspace_size(desc) bytes, 256-byte aligned; its
+ *               contents need no initialisation and are clobbered
+ *   aux         optional intermediate outputs, may be NULL
+ *   stream      hipStream_t
+ * Returns MOE_OK or a negative status; on an error nothing is enqueued
+ * except for MOE_ERR_HIP, where a launch failed part-way. */
+int moe_forward(const moe_desc *desc, const void *x, const float *router_w,
+                const float *router_bias, const moe_weights *weights, void *out,
+                void *workspace, size_t workspace_bytes, const moe_aux *aux,
+                void *stream);
+
+/* Static text for a status code. */
+const char *moe_status_string(int status);
+
+/* The hipError_t of the most recent MOE_ERR_HIP on the calling thread (0 if none). */
+int moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FGS_MOE_H */

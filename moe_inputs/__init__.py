@@ -154,12 +154,19 @@ def _weight(shape, cfg: LayerConfig, seed: int, device: str, chunk_first_dim: bo
     return w.to(torch.bfloat16), None
 
 
+# Expert weights do not depend on the token count; the last few weight sets
+# drawn are kept (read-only use) so that cases differing only in N reuse them.
+_WEIGHT_CACHE: "Dict[tuple, Dict[str, torch.Tensor]]" = {}
+_WEIGHT_CACHE_MAX = 2
+
+
 def generate(cfg: LayerConfig, seed: int = 0, device: str = "cpu",
-             n_tokens: Optional[int] = None) -> Dict[str, torch.Tensor]:
+             n_tokens: Optional[int] = None, cache: bool = True) -> Dict[str, torch.Tensor]:
     """Draw every input of one layer call.  Returns torch tensors on `device`.
 
     Keys: x, router_w, router_b, w_gate, w_up, w_down, ws_gate, ws_up, ws_down
     and, for FP8 weights, s_gate, s_up, s_down, ss_gate, ss_up, ss_down.
+    The weight tensors may be shared with earlier calls: do not modify them.
     """
     n = cfg.n_tokens if n_tokens is None else n_tokens
     seeds = _child_seeds(seed)
@@ -177,12 +184,22 @@ def generate(cfg: LayerConfig, seed: int = 0, device: str = "cpu",
     else:
         out["router_b"] = _randn((E,), cfg.bias_std, seeds["router_b"], device)
 
+    wkey = (d, E, f, fs, cfg.w_dtype, cfg.w_std, seed, str(device))
+    if cache and wkey in _WEIGHT_CACHE:
+        out.update(_WEIGHT_CACHE[wkey])
+        return out
+    wts: Dict[str, torch.Tensor] = {}
     for key, shape in (("w_gate", (E, f, d)), ("w_up", (E, f, d)), ("w_down", (E, d, f)),
                        ("ws_gate", (fs, d)), ("ws_up", (fs, d)), ("ws_down", (d, fs))):
         w, s = _weight(shape, cfg, seeds[key], device, chunk_first_dim=True)
-        out[key] = w
+        wts[key] = w
         if s is not None:
-            out["s" + key[1:] if key.startswith("w_") else "ss" + key[2:]] = s
+            wts["s" + key[1:] if key.startswith("w_") else "ss" + key[2:]] = s
+    if cache:
+        while len(_WEIGHT_CACHE) >= _WEIGHT_CACHE_MAX:
+            _WEIGHT_CACHE.pop(next(iter(_WEIGHT_CACHE)))
+        _WEIGHT_CACHE[wkey] = wts
+    out.update(wts)
     return out
 
 

@@ -1,0 +1,139 @@
+"""Helpers for comparing the HIP library with the CPU oracle.
+
+The criteria:
+  * selected expert ids: bit-exact, except tokens whose oracle gap between the
+    k-th and (k+1)-th biased score is below 1e-5 (counted, and checked to be a
+    valid selection within that gap; their output is compared with the oracle
+    evaluated on the GPU's ids);
+  * dispatch layout (offsets, pair_of_row, row_of_pair): bit-exact against the
+    oracle's dispatch applied to the GPU's ids;
+  * logits and mixture weights: within float32 accumulation error;
+  * output: max over tokens of ||y_gpu[t] - y_ref[t]||_inf / ||y_ref[t]||_inf
+    within 2e-2 for bfloat16 weights and 6e-2 for FP8 weights.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+import oracle.moe_oracle as O
+from fine_grained_sparse_amd import binding as B
+from moe_inputs import LayerConfig, to_numpy
+
+NEAR_TIE = 1e-5
+OUT_TOL = {"bf16": 2e-2, "fp8": 6e-2}
+# |logit| ~ 1 summed over d = 2560 products in float32: a few 1e-6 at most
+LOGIT_ATOL = 2e-5
+
+
+def to_device(inputs: Dict[str, torch.Tensor], device="cuda") -> Dict[str, torch.Tensor]:
+    return {k: v.to(device) for k, v in inputs.items()}
+
+
+def run_gpu(cfg: LayerConfig, dev_inputs: Dict[str, torch.Tensor], residual: Optional[torch.Tensor] = None,
+            n_tokens: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """One moe_forward call with every optional output requested."""
+    x = dev_inputs["x"]
+    n = x.shape[0] if n_tokens is None else n_tokens
+    layer = B.MoeLayer(cfg.top_k, dev_inputs, max(n, 1), x.dtype)
+    bufs = B.route_outputs(n, cfg.n_experts, cfg.top_k, x.device)
+    aux = B.aux_struct(bufs)
+    if residual is not None:
+        out = residual.clone()
+        layer.forward(x, out=out, accumulate=True, aux=aux)
+    else:
+        out = torch.full_like(x, float("nan"))
+        layer.forward(x, out=out, aux=aux)
+    torch.cuda.synchronize()
+    res = {k: v.cpu().numpy() for k, v in bufs.items()}
+    res["out"] = out.float().cpu().numpy().astype(np.float64)
+    return res
+
+
+def check_routing(cfg: LayerConfig, g: Dict[str, np.ndarray], ref: Dict[str, np.ndarray]) -> Dict[str, int]:
+    """Compare logits, ids, weights and layout; returns counts for reporting."""
+    n = g["topk_ids"].shape[0]
+    k, E = cfg.top_k, cfg.n_experts
+    assert np.allclose(g["logits"], ref["logits"], rtol=0, atol=LOGIT_ATOL), \
+        f"logits max err {np.abs(g['logits'] - ref['logits']).max()}"
+    near = ref["gap"] < NEAR_TIE
+    ids_eq = np.all(g["topk_ids"] == ref["ids"], axis=1)
+    bad = ~ids_eq & ~near
+    assert not bad.any(), f"{bad.sum()} tokens differ in selection with gap >= {NEAR_TIE}: {np.nonzero(bad)[0][:10]}"
+    # differing near-tie tokens: the GPU's set must be a valid top-k within the gap
+    for t in np.nonzero(~ids_eq)[0]:
+        s = ref["scores"][t].astype(np.float64)
+        gi = g["topk_ids"][t]
+        assert len(set(gi.tolist())) == k and np.all(np.diff(gi) > 0)
+        kth = np.sort(s)[::-1][k - 1]
+        assert np.all(s[gi] >= kth - NEAR_TIE)
+    # ids ascending, distinct, in range
+    assert np.all(np.diff(g["topk_ids"], axis=1) > 0) and g["topk_ids"].min() >= 0 and g["topk_ids"].max() < E
+    # weights = sigmoid of the unbiased logit at the GPU's ids
+    w_ref = O.mixture_weights(ref["logits"], g["topk_ids"])
+    assert np.allclose(g["topk_w"], w_ref, rtol=0, atol=2e-6), f"weights err {np.abs(g['topk_w'] - w_ref).max()}"
+    # gap (diagnostic value) is close to the oracle's where the ids agree
+    if k < E:
+        assert np.allclose(g["gap"][ids_eq], ref["gap"][ids_eq], rtol=0, atol=4 * LOGIT_ATOL)
+    else:
+        assert np.all(np.isinf(g["gap"]))
+    # dispatch layout: bit-exact against the oracle's dispatch of the GPU's ids
+    counts, offsets, por, rop = O.dispatch(g["topk_ids"], E)
+    assert np.array_equal(g["expert_offsets"], offsets), "expert_offsets differ"
+    assert np.array_equal(g["pair_of_row"], por), "pair_of_row differs"
+    assert np.array_equal(g["row_of_pair"], rop), "row_of_pair differs"
+    return dict(tokens=n, near_tie=int(near.sum()), differing_ids=int((~ids_eq).sum()))
+
+
+def rel_err(out: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per token ||out - ref||_inf / ||ref||_inf."""
+    num = np.abs(out - ref).max(axis=1)
+    den = np.abs(ref).max(axis=1)
+    return num / np.maximum(den, 1e-30)
+
+
+def check_output(cfg: LayerConfig, gpu_out: np.ndarray, ref_out: np.ndarray, tokens: Optional[Sequence[int]] = None):
+    tol = OUT_TOL[cfg.w_dtype]
+    assert np.all(np.isfinite(gpu_out)), "non-finite output"
+    e = rel_err(gpu_out, ref_out)
+    worst = float(e.max()) if e.size else 0.0
+    assert worst <= tol, f"max relative error {worst:.3e} > {tol} (token {int(np.argmax(e))})"
+    return worst
+
+
+def full_check(cfg: LayerConfig, host_inputs: Dict[str, torch.Tensor], g: Dict[str, np.ndarray],
+               residual: Optional[np.ndarray] = None) -> Dict[str, float]:
+    """Whole-layer oracle on every token (small and decode-sized cases)."""
+    npi = to_numpy(host_inputs)
+    ref = O.moe_forward(npi, cfg.top_k, cfg.w_dtype, cfg.x_dtype, residual=residual)
+    stats = check_routing(cfg, g, ref)
+    ref_out = ref["out64"].copy()
+    diff = np.nonzero(np.any(g["topk_ids"] != ref["ids"], axis=1))[0]
+    if diff.size:
+        alt = O.token_outputs(npi, diff, cfg.top_k, cfg.w_dtype, ids=g["topk_ids"])["out64"]
+        if residual is not None:
+            alt = alt + (O.decode_bf16(residual[diff]) if residual.dtype == np.uint16 else residual[diff])
+        ref_out[diff] = alt
+    stats["max_rel_err"] = check_output(cfg, g["out"], ref_out)
+    return stats
+
+
+def sampled_check(cfg: LayerConfig, host_inputs: Dict[str, torch.Tensor], g: Dict[str, np.ndarray],
+                  n_sample: int = 24, seed: int = 0) -> Dict[str, float]:
+    """Full-size cases: routing of every token, output of sampled tokens."""
+    npi = to_numpy(host_inputs)
+    n = g["topk_ids"].shape[0]
+    rng = np.random.default_rng(seed)
+    toks = np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=min(n, n_sample), replace=False)]))
+    part = O.token_outputs(npi, toks, cfg.top_k, cfg.w_dtype, ids=g["topk_ids"])
+    x64 = O.decode_bf16(npi["x"]) if npi["x"].dtype == np.uint16 else npi["x"].astype(np.float64)
+    h32 = part["logits"]
+    _, gap, s = O.select_topk(h32, npi["router_b"], cfg.top_k)
+    ref = dict(logits=h32, ids=part["ids"], gap=gap, scores=s)
+    stats = check_routing(cfg, g, ref)
+    stats["max_rel_err"] = check_output(cfg, g["out"][toks], part["out64"])
+    stats["sampled"] = int(len(toks))
+    del x64
+    return stats

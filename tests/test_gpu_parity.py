@@ -1,0 +1,88 @@
+"""HIP library vs the CPU oracle, through the C ABI (needs an MI355X)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from moe_inputs import generate, get_config
+from tests import parity as PA
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fine_grained_sparse_amd import binding
+    binding.lib()  # raises if the library is missing
+
+
+def _run_full(cfg, seed=0, residual=False):
+    _say(f"case {cfg.name} N={cfg.n_tokens} d={cfg.d_model} E={cfg.n_experts} k={cfg.top_k} "
+         f"f={cfg.d_ff} x={cfg.x_dtype} w={cfg.w_dtype} seed={seed} residual={residual}")
+    host = generate(cfg, seed=seed)
+    dev = PA.to_device(host)
+    res_t = res_np = None
+    if residual:
+        g = torch.Generator().manual_seed(seed + 99)
+        r = torch.randn(host["x"].shape, generator=g).to(host["x"].dtype)
+        res_t = r.cuda()
+        res_np = r.view(torch.int16).numpy().view(np.uint16) if r.dtype == torch.bfloat16 else r.numpy()
+    g = PA.run_gpu(cfg, dev, residual=res_t)
+    stats = PA.full_check(cfg, host, g, residual=res_np)
+    _say(f"  -> {stats}")
+    return stats
+
+
+def test_toy():
+    _run_full(get_config("toy"))
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 32, 64])
+def test_decode_full_shape(n):
+    _run_full(get_config("decode", n_tokens=n))
+
+
+def test_decode_fp8_weights():
+    _run_full(get_config("decode", w_dtype="fp8", n_tokens=16))
+
+
+@pytest.mark.parametrize("over", [
+    dict(top_k=1), dict(top_k=8), dict(n_experts=6, top_k=6), dict(n_experts=40),
+    dict(d_model=192, d_ff=128, d_ff_shared=64), dict(x_dtype="bf16", w_dtype="fp8"),
+    dict(n_tokens=1), dict(n_tokens=600), dict(n_tokens=257, n_experts=1024, top_k=8),
+])
+def test_toy_variants(over):
+    _run_full(get_config("toy", **over))
+
+
+def test_accumulate_into_residual():
+    _run_full(get_config("toy", x_dtype="bf16", n_tokens=50), residual=True)
+    _run_full(get_config("toy", n_tokens=20), residual=True)
+
+
+def test_deterministic():
+    cfg = get_config("decode", n_tokens=32)
+    dev = PA.to_device(generate(cfg, seed=5))
+    a = PA.run_gpu(cfg, dev)
+    b = PA.run_gpu(cfg, dev)
+    for key in a:
+        assert np.array_equal(a[key], b[key], equal_nan=True), key
+
+
+def test_zero_tokens_is_noop():
+    from fine_grained_sparse_amd import binding as B
+    cfg = get_config("toy")
+    dev = PA.to_device(generate(cfg, seed=0, n_tokens=4))
+    layer = B.MoeLayer(cfg.top_k, dev, 4, torch.float32)
+    x = dev["x"][:0]
+    out = torch.empty_like(x)
+    layer.forward(x, out=out)
+    torch.cuda.synchronize()
