@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     }
     __syncthreads();
     const size_t shared_row = (size_t)N * k + t;
-    for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
+    for (int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4; c < d; c += gridDim.y * blockDim.x * 4) {
         float4 a = *reinterpret_cast<const float4 *>(Y + shared_row * d + c);
         for (int j = 0; j < k; ++j) {
             const float wj = ws[j];
@@ -57,10 +57,10 @@ __global__ __launch_bounds__(256) void combine_kernel(
 hipError_t launch_combine(const Plan &p) {
     const bool acc = (p.flags & MOE_FLAG_ACCUMULATE) != 0;
     if (p.xdt == MOE_DTYPE_BF16)
-        hipLaunchKernelGGL((combine_kernel<true>), dim3(p.N), dim3(256), 0, p.stream, p.Y, p.tw, p.rop, p.out, p.N,
+        hipLaunchKernelGGL((combine_kernel<true>), dim3(p.N, (p.d + 1023) / 1024), dim3(256), 0, p.stream, p.Y, p.tw, p.rop, p.out, p.N,
                            p.d, p.k, acc);
     else
-        hipLaunchKernelGGL((combine_kernel<false>), dim3(p.N), dim3(256), 0, p.stream, p.Y, p.tw, p.rop, p.out, p.N,
+        hipLaunchKernelGGL((combine_kernel<false>), dim3(p.N, (p.d + 1023) / 1024), dim3(256), 0, p.stream, p.Y, p.tw, p.rop, p.out, p.N,
                            p.d, p.k, acc);
     return hipGetLastError();
 }

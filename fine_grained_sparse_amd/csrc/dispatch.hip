@@ -15,7 +15,8 @@
 // the lower tokens), so no atomic order ever reaches the output.
 //
 // The scan also writes the tile list of the expert kernels: one entry
-// (group, first row within the group) per `bm` rows of every non-empty group.
+// (group, first row within the group) per `bm` rows of every non-empty group,
+// shared group first, then routed experts in id order.
 #include "moe_common.h"
 #include "moe_plan.h"
 
@@ -78,16 +79,20 @@ __device__ void offsets_and_tiles(const int *cnt, int *off, int *ntile, int *wsu
         g_offsets[e] = off[e];
         if (g_exp_off && e <= E) g_exp_off[e] = off[e];
     }
-    // tiles per group (routed groups 0..E-1, shared group E with N rows)
-    for (int g = tid; g <= E; g += blockDim.x) {
-        int m = off[g + 1] - off[g];
-        ntile[g] = (m + bm - 1) / bm;
+    // tiles per group; the shared group (E, N rows, the most rows per expert
+    // at small N) is listed first so its workgroups start first.  Slot 0 of
+    // ntile[] is the shared group, slot 1 + e the routed expert e.
+    for (int q = tid; q <= E; q += blockDim.x) {
+        const int g = q == 0 ? E : q - 1;
+        const int m = off[g + 1] - off[g];
+        ntile[q] = (m + bm - 1) / bm;
     }
     __syncthreads();
     int nt = block_exclusive_scan_1024(ntile, E + 1, wsum);
-    for (int g = tid; g <= E; g += blockDim.x) {
-        int m = off[g + 1] - off[g];
-        int start = ntile[g];
+    for (int q = tid; q <= E; q += blockDim.x) {
+        const int g = q == 0 ? E : q - 1;
+        const int m = off[g + 1] - off[g];
+        const int start = ntile[q];
         for (int i = 0; i * bm < m; ++i) {
             tiles[2 * (start + i)] = g;
             tiles[2 * (start + i) + 1] = i * bm;

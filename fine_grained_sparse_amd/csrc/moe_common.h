@@ -12,6 +12,19 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
+// ---------------------------------------------------------------- loads
+// Streaming (non-temporal) loads for weights that are read exactly once.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_stream16(const void *p) {
+    u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_stream8(const void *p) {
+    u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+    return make_uint2(v.x, v.y);
+}
+
 // ---------------------------------------------------------------- bfloat16
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -81,6 +94,96 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
         v = o > v ? o : v;
     }
     return v;
+}
+
+// ---------------------------------------------------------------- butterfly
+// Reduce-scatter of V partial sums (V a power of two <= 64) over a wave: at
+// each halving step a lane keeps half of its values and adds its partner's
+// copy of that half, so after log2(V) steps lane l holds one fully reduced
+// value, index butterfly_index<V>(l); the remaining steps sum the last value.
+// Lane pairing per step: distance 32 and 16 through v_permlane32_swap /
+// v_permlane16_swap (one instruction exchanges the halves of two registers),
+// then DPP row_mirror (lane i <-> 15-i), row_half_mirror (i <-> 7-i) and quad
+// permutes (xor 2, xor 1).  Each pairing flips exactly the step's lane bit,
+// and the partners' contribution sets are disjoint, so every value ends up
+// summed over all 64 lanes.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppRowMirror = 0x140, kDppHalfMirror = 0x141, kDppXor2 = 0x4E, kDppXor1 = 0xB1;
+
+template <int S>
+__device__ __forceinline__ float pair_get(float v) {  // partner's value across lane bit log2(S)
+    if constexpr (S == 8) return dpp_f<kDppRowMirror>(v);
+    else if constexpr (S == 4) return dpp_f<kDppHalfMirror>(v);
+    else if constexpr (S == 2) return dpp_f<kDppXor2>(v);
+    else return dpp_f<kDppXor1>(v);
+}
+
+template <int S, int V>
+__device__ __forceinline__ void bfly_step(float (&v)[V], int &n) {
+    if (n > 1) {
+        const int h = n / 2;
+        if constexpr (S == 32 || S == 16) {
+#pragma unroll
+            for (int i = 0; i < V / 2; ++i) {
+                if (i < h) {
+                    uint32_t a = __float_as_uint(v[i]), b = __float_as_uint(v[i + h]);
+                    auto r = (S == 32) ? __builtin_amdgcn_permlane32_swap(a, b, false, false)
+                                       : __builtin_amdgcn_permlane16_swap(a, b, false, false);
+                    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+                }
+            }
+        } else {
+            const bool upper = (threadIdx.x & S) != 0;
+#pragma unroll
+            for (int i = 0; i < V / 2; ++i) {
+                if (i < h) {
+                    const float send = upper ? v[i] : v[i + h];
+                    const float keep = upper ? v[i + h] : v[i];
+                    v[i] = keep + pair_get<S>(send);
+                }
+            }
+        }
+        n = h;
+    } else {
+        if constexpr (S == 32 || S == 16) {
+            uint32_t a = __float_as_uint(v[0]);
+            auto r = (S == 32) ? __builtin_amdgcn_permlane32_swap(a, a, false, false)
+                               : __builtin_amdgcn_permlane16_swap(a, a, false, false);
+            // after swapping a register with itself each lane sees its partner's copy in one output
+            const bool upper = (threadIdx.x & S) != 0;
+            v[0] += __uint_as_float(upper ? r[0] : r[1]);
+        } else {
+            v[0] += pair_get<S>(v[0]);
+        }
+    }
+}
+
+template <int V>
+__device__ __forceinline__ void butterfly_reduce(float (&v)[V]) {
+    int n = V;
+    bfly_step<32>(v, n);
+    bfly_step<16>(v, n);
+    bfly_step<8>(v, n);
+    bfly_step<4>(v, n);
+    bfly_step<2>(v, n);
+    bfly_step<1>(v, n);
+}
+
+template <int V>
+__device__ __forceinline__ int butterfly_index(int lane) {
+    int idx = 0, n = V;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+        if (n > 1) {
+            if (lane & s) idx += n / 2;
+            n /= 2;
+        }
+    }
+    return idx;
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }

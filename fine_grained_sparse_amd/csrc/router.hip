@@ -89,6 +89,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+#pragma unroll 8
     for (int kk = 0; kk < kslice; kk += 32) {
         uint4 a[MT];
 #pragma unroll

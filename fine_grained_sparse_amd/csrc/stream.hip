@@ -23,52 +23,14 @@
 
 namespace fgs {
 
-// Reduce-scatter V partial sums (V a power of two <= 64) over the wave.
-// On return v[0] of lane l holds the full sum of value index
-// butterfly_index<V>(l).
-template <int V>
-__device__ __forceinline__ void butterfly_reduce(float (&v)[V]) {
-    int n = V;
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-        if (n > 1) {
-            const bool upper = (threadIdx.x & s) != 0;
-            const int h = n / 2;
-#pragma unroll
-            for (int i = 0; i < V / 2; ++i) {
-                if (i < h) {
-                    float send = upper ? v[i] : v[i + h];
-                    float keep = upper ? v[i + h] : v[i];
-                    v[i] = keep + __shfl_xor(send, s, kWave);
-                }
-            }
-            n = h;
-        } else {
-            v[0] += __shfl_xor(v[0], s, kWave);
-        }
-    }
-}
-template <int V>
-__device__ __forceinline__ int butterfly_index(int lane) {
-    int idx = 0, n = V;
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-        if (n > 1) {
-            if (lane & s) idx += n / 2;
-            n /= 2;
-        }
-    }
-    return idx;
-}
-
 template <bool FP8> struct WChunk;            // 8 weights of one row
 template <> struct WChunk<false> { typedef uint4 T; };
 template <> struct WChunk<true> { typedef uint2 T; };
 
 template <bool FP8>
 __device__ __forceinline__ typename WChunk<FP8>::T load_chunk(const void *base, size_t elem_off) {
-    if constexpr (FP8) return *reinterpret_cast<const uint2 *>((const uint8_t *)base + elem_off);
-    else return *reinterpret_cast<const uint4 *>((const uint16_t *)base + elem_off);
+    if constexpr (FP8) return ld_stream8((const uint8_t *)base + elem_off);
+    else return ld_stream16((const uint16_t *)base + elem_off);
 }
 template <bool FP8>
 __device__ __forceinline__ float dot8(const typename WChunk<FP8>::T &w, const uint4 &x, float c) {
@@ -84,10 +46,23 @@ __device__ __forceinline__ uint4 load_x8(const void *x, int xdt, size_t elem_off
     return make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
 }
 
-constexpr int kGuTC = 8;   // token rows staged per pass (gate/up)
 constexpr int kGuRB = 8;   // H columns per workgroup (2 per wave)
 
-// grid: (tile list capacity, ceil(max(f, fs) / 8)); block 256; dynamic LDS kGuTC*d*2 bytes
+template <int CPL>
+__device__ __forceinline__ void load_x_row(uint4 (&xv)[CPL], const void *x, int xdt, int t, int d, int lane,
+                                           int nch) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int ch = lane + 64 * i;
+        xv[i] = ch < nch ? load_x8(x, xdt, (size_t)t * d + (size_t)ch * 8) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+// grid: (ceil(max(f, fs) / 8) column blocks, tile list capacity); block 256.
+// Column blocks run fastest, so the workgroups in flight together cover a few
+// experts' matrices completely (page and DRAM-row locality).  No LDS and no
+// barrier: each lane reads its slice of a token row straight from L2, with
+// the next token's row in flight while the current one is reduced.
 template <int CPL, bool FP8>
 __global__ __launch_bounds__(256) void gate_up_stream_kernel(
     const void *__restrict__ x, int xdt, const void *__restrict__ wg, const void *__restrict__ wu,
@@ -96,141 +71,120 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ por, uint16_t *__restrict__ H, int ldh, int d, int E, int k, int f, int fs,
     int bm) {
-    extern __shared__ uint4 xs[];  // [kGuTC][d/8]
-    const int u = blockIdx.x;
+    const int u = blockIdx.y;
     if (u >= *n_tiles) return;
-    const int g = tiles[2 * u];
+    const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
     const bool shared = g == E;
     const int fg = shared ? fs : f;
-    if ((int)blockIdx.y * kGuRB >= fg) return;
+    if ((int)blockIdx.x * kGuRB >= fg) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int c0 = blockIdx.y * kGuRB + wave * 2;
-    const int gstart = offsets[g], m0 = tiles[2 * u + 1];
-    const int row0 = gstart + m0, m = min(bm, offsets[g + 1] - row0);
+    const int c0 = blockIdx.x * kGuRB + wave * 2;
     const int nch = d / 8;
 
-    // this wave's 4 weight rows: gate c0, c0+1, up c0, c0+1
+    // this wave's 4 weight rows: gate c0, c0+1, up c0, c0+1 (issued first)
     const void *gbase = shared ? wsg : wg;
     const void *ubase = shared ? wsu : wu;
     const size_t rbase = shared ? 0 : (size_t)g * f;
+    // lanes past the row end read chunk 0 again (finite weights) and are
+    // multiplied by a zero activation chunk; no select on loaded values, so
+    // nothing waits for these loads before the token rows are requested
     typename WChunk<FP8>::T w[4][CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int ch = lane + 64 * i;
-        const bool ok = ch < nch;
-        const int chc = ok ? ch : 0;
+        const int chc = ch < nch ? ch : 0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const void *b = r < 2 ? gbase : ubase;
             w[r][i] = load_chunk<FP8>(b, (rbase + c0 + (r & 1)) * (size_t)d + (size_t)chc * 8);
-            if (!ok) w[r][i] = typename WChunk<FP8>::T{};
         }
     }
-    float scl[4] = {1.f, 1.f, 1.f, 1.f};
+
+    const int gstart = offsets[g];
+    const int row0 = gstart + m0, m = min(bm, offsets[g + 1] - row0);
+    // lane j holds the token of row row0 + j (m <= 64)
+    int tok = 0;
+    if (lane < m) tok = shared ? (m0 + lane) : por[row0 + lane] / k;
+
+    float gsc = 1.f, usc = 1.f;
+    const int r_out = (lane >> 4) & 1;  // after the reduction lanes 0 and 16 own gate columns c0, c0+1
     if (FP8) {
         const float *gs = shared ? ssg : sg + (size_t)g * f;
         const float *us = shared ? ssu : su + (size_t)g * f;
-        scl[0] = gs[c0]; scl[1] = gs[c0 + 1]; scl[2] = us[c0]; scl[3] = us[c0 + 1];
+        gsc = gs[c0 + r_out];
+        usc = us[c0 + r_out];
     }
 
-    for (int tc0 = 0; tc0 < m; tc0 += kGuTC) {
-        const int mc = min(kGuTC, m - tc0);
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < mc * nch; idx += blockDim.x) {
-            const int tok = idx / nch, ch = idx - tok * nch;
-            const int r = row0 + tc0 + tok;
-            const int t = shared ? (r - gstart) : por[r] / k;
-            xs[tok * nch + ch] = load_x8(x, xdt, (size_t)t * d + (size_t)ch * 8);
+    uint4 xa[CPL], xb[CPL];
+    load_x_row<CPL>(xa, x, xdt, __shfl(tok, 0, kWave), d, lane, nch);
+    for (int t = 0; t < m; ++t) {
+        if (t + 1 < m) load_x_row<CPL>(xb, x, xdt, __shfl(tok, t + 1, kWave), d, lane, nch);
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = dot8<FP8>(w[r][i], xa[i], acc[r]);
+        butterfly_reduce<4>(acc);
+        // value index = 2*bit5 + bit4 of the lane: gate rows 0,1 then up rows 2,3
+        const float upv = __shfl_xor(acc[0], 32, kWave);
+        if ((lane & 47) == 0) {  // lanes 0 and 16
+            const float hv = silu(acc[0] * gsc) * (upv * usc);
+            H[(size_t)(row0 + t) * ldh + c0 + r_out] = (uint16_t)f32_to_bf16_rne(hv);
         }
-        __syncthreads();
-        float acc[4 * kGuTC];
 #pragma unroll
-        for (int i = 0; i < 4 * kGuTC; ++i) acc[i] = 0.f;
-#pragma unroll
-        for (int t = 0; t < kGuTC; ++t) {
-            if (t < mc) {
-#pragma unroll
-                for (int i = 0; i < CPL; ++i) {
-                    const int ch = lane + 64 * i;
-                    if (ch < nch) {
-                        const uint4 xv = xs[t * nch + ch];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[r * kGuTC + t] = dot8<FP8>(w[r][i], xv, acc[r * kGuTC + t]);
-                    }
-                }
-            }
-        }
-        butterfly_reduce<4 * kGuTC>(acc);
-        // lane holds value (r, t) = idx / kGuTC, idx % kGuTC; gate r in {0,1}, up r + 2
-        const int idx = butterfly_index<4 * kGuTC>(lane);
-        const float upv = __shfl_xor(acc[0], 32, kWave);  // up partner differs in the top index bit
-        const int r = idx / kGuTC, t = idx % kGuTC;
-        if (r < 2 && (lane & 1) == 0 && t < mc) {
-            const float gv = acc[0] * (r ? scl[1] : scl[0]);
-            const float uv = upv * (r ? scl[3] : scl[2]);
-            const float hv = silu(gv) * uv;
-            H[(size_t)(row0 + tc0 + t) * ldh + c0 + r] = (uint16_t)f32_to_bf16_rne(hv);
-        }
+        for (int i = 0; i < CPL; ++i) xa[i] = xb[i];
     }
 }
 
-constexpr int kDnTC = 16;  // H rows staged per pass (down)
-constexpr int kDnRW = 16;  // output rows per wave
+constexpr int kDnRW = 8;   // output rows per wave
+constexpr int kDnRB = 4 * kDnRW;  // output rows per workgroup
 
-// grid: (tile list capacity, d / 64); block 256.  Needs f, fs <= 512.
+// grid: (d / kDnRB, tile list capacity); block 256.  Needs f, fs <= 512.
 template <bool FP8>
 __global__ __launch_bounds__(256) void down_stream_kernel(
     const uint16_t *__restrict__ H, int ldh, const void *__restrict__ wd, const float *__restrict__ sd,
     const void *__restrict__ wsd, const float *__restrict__ ssd, const int32_t *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets, float *__restrict__ Y, int d, int E,
     int f, int fs, int bm) {
-    __shared__ uint4 hs[kDnTC * 64];  // [kDnTC][fg/8], fg <= 512
-    const int u = blockIdx.x;
+    const int u = blockIdx.y;
     if (u >= *n_tiles) return;
-    const int g = tiles[2 * u];
+    const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
     const bool shared = g == E;
     const int fg = shared ? fs : f;
     const int nch = fg / 8;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int o0 = blockIdx.y * 64 + wave * kDnRW;
-    const int row0 = offsets[g] + tiles[2 * u + 1], m = min(bm, offsets[g + 1] - row0);
+    const int o0 = blockIdx.x * kDnRB + wave * kDnRW;
 
     const void *base = shared ? wsd : wd;
     const size_t obase = shared ? 0 : (size_t)g * d;
-    const bool ok = lane < nch;
+    const bool ok = lane < nch;  // masked lanes: chunk 0 again, times a zero H chunk
     typename WChunk<FP8>::T w[kDnRW];
 #pragma unroll
-    for (int r = 0; r < kDnRW; ++r) {
+    for (int r = 0; r < kDnRW; ++r)
         w[r] = load_chunk<FP8>(base, (obase + o0 + r) * (size_t)fg + (size_t)(ok ? lane : 0) * 8);
-        if (!ok) w[r] = typename WChunk<FP8>::T{};
-    }
     const int myrow = butterfly_index<kDnRW>(lane);
     float scl = 1.f;
     if (FP8) scl = shared ? ssd[o0 + myrow] : sd[obase + o0 + myrow];
 
-    for (int tc0 = 0; tc0 < m; tc0 += kDnTC) {
-        const int mc = min(kDnTC, m - tc0);
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < mc * nch; idx += blockDim.x) {
-            const int tok = idx / nch, ch = idx - tok * nch;
-            hs[tok * 64 + ch] = *reinterpret_cast<const uint4 *>(H + (size_t)(row0 + tc0 + tok) * ldh + ch * 8);
-        }
-        __syncthreads();
-        for (int t = 0; t < mc; ++t) {
-            const uint4 hv = ok ? hs[t * 64 + lane] : make_uint4(0, 0, 0, 0);
-            float p[kDnRW];
+    const int row0 = offsets[g] + m0, m = min(bm, offsets[g + 1] - row0);
+    const uint16_t *hp = H + (size_t)row0 * ldh + (size_t)(ok ? lane : 0) * 8;
+    uint4 ha = ok ? *reinterpret_cast<const uint4 *>(hp) : make_uint4(0, 0, 0, 0);
+    for (int t = 0; t < m; ++t) {
+        uint4 hb = make_uint4(0, 0, 0, 0);
+        if (t + 1 < m && ok) hb = *reinterpret_cast<const uint4 *>(hp + (size_t)(t + 1) * ldh);
+        float p[kDnRW];
 #pragma unroll
-            for (int r = 0; r < kDnRW; ++r) p[r] = dot8<FP8>(w[r], hv, 0.f);
-            butterfly_reduce<kDnRW>(p);
-            if ((lane & 3) == 0) Y[(size_t)(row0 + tc0 + t) * d + o0 + myrow] = p[0] * scl;
-        }
+        for (int r = 0; r < kDnRW; ++r) p[r] = dot8<FP8>(w[r], ha, 0.f);
+        butterfly_reduce<kDnRW>(p);
+        if ((lane & (64 / kDnRW - 1)) == 0) Y[(size_t)(row0 + t) * d + o0 + myrow] = p[0] * scl;
+        ha = hb;
     }
 }
 
 hipError_t launch_gate_up(const Plan &p) {
     const int fmax = p.f > p.fs ? p.f : p.fs;
-    dim3 grid(p.max_tiles, (fmax + kGuRB - 1) / kGuRB), block(256);
-    const size_t lds = (size_t)kGuTC * p.d * 2;
+    dim3 grid((fmax + kGuRB - 1) / kGuRB, p.max_tiles), block(256);
+    const size_t lds = 0;
     const int cpl = (p.d / 8 + 63) / 64;
     const bool fp8 = p.wdt == MOE_DTYPE_FP8_E4M3;
 #define FGS_GU(C, F8)                                                                                          \
@@ -255,7 +209,7 @@ hipError_t launch_gate_up(const Plan &p) {
 }
 
 hipError_t launch_down(const Plan &p) {
-    dim3 grid(p.max_tiles, p.d / 64), block(256);
+    dim3 grid(p.d / kDnRB, p.max_tiles), block(256);
     if (p.wdt == MOE_DTYPE_FP8_E4M3)
         hipLaunchKernelGGL((down_stream_kernel<true>), grid, block, 0, p.stream, p.H, p.ldh, p.W.w_down, p.W.s_down,
                            p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, p.Y, p.d, p.E, p.f, p.fs, p.bm);

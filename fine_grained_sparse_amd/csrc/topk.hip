@@ -43,8 +43,14 @@ __global__ __launch_bounds__(256) void topk_kernel(
         int e = lane + 64 * v;
         if (e < E) {
             const float *src = partial + (size_t)t * E + e;
-            float acc = src[0];
-            for (int s = 1; s < ks; ++s) acc += src[s * slice];
+            // slices added in order 0, 1, ..., ks-1 (ks <= 10); loads issued together
+            float part[10];
+#pragma unroll
+            for (int s = 0; s < 10; ++s) part[s] = s < ks ? src[s * slice] : 0.f;
+            float acc = part[0];
+#pragma unroll
+            for (int s = 1; s < 10; ++s)
+                if (s < ks) acc += part[s];
             h[v] = acc;
             if (logits_out) logits_out[(size_t)t * E + e] = acc;
             float sc = acc + bias[e];
