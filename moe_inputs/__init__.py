@@ -130,8 +130,12 @@ def _fp8_per_channel(w: torch.Tensor):
 
 
 def _weight(shape, cfg: LayerConfig, seed: int, device: str, chunk_first_dim: bool):
-    """bf16 tensor, or (uint8 codes, fp32 scales) for FP8."""
-    if chunk_first_dim and len(shape) == 3:
+    """bf16 tensor, or (uint8 codes, fp32 scales) for FP8.
+
+    On the host the experts are drawn one at a time (bounded memory); on a GPU
+    the whole tensor is drawn at once (a different, equally seeded stream).
+    """
+    if chunk_first_dim and len(shape) == 3 and not str(device).startswith("cuda"):
         # draw one expert at a time to bound peak host memory
         g = torch.Generator(device=device)
         g.manual_seed(seed)
