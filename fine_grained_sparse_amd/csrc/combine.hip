@@ -12,9 +12,19 @@
 
 namespace fgs {
 
-template <bool BF16OUT>
+template <bool YBF16>
+__device__ __forceinline__ float4 load_y4(const void *Y, size_t elem) {
+    if constexpr (YBF16) {
+        const uint2 v = *reinterpret_cast<const uint2 *>((const uint16_t *)Y + elem);
+        return make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+    } else {
+        return *reinterpret_cast<const float4 *>((const float *)Y + elem);
+    }
+}
+
+template <bool BF16OUT, bool YBF16>
 __global__ __launch_bounds__(256) void combine_kernel(
-    const float *__restrict__ Y, const float *__restrict__ tw, const int32_t *__restrict__ rop, void *out,
+    const void *__restrict__ Y, const float *__restrict__ tw, const int32_t *__restrict__ rop, void *out,
     int N, int d, int k, bool accumulate) {
     const int t = blockIdx.x;
     __shared__ float ws[8];
@@ -26,10 +36,10 @@ __global__ __launch_bounds__(256) void combine_kernel(
     __syncthreads();
     const size_t shared_row = (size_t)N * k + t;
     for (int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4; c < d; c += gridDim.y * blockDim.x * 4) {
-        float4 a = *reinterpret_cast<const float4 *>(Y + shared_row * d + c);
+        float4 a = load_y4<YBF16>(Y, shared_row * d + c);
         for (int j = 0; j < k; ++j) {
             const float wj = ws[j];
-            const float4 y = *reinterpret_cast<const float4 *>(Y + (size_t)rs[j] * d + c);
+            const float4 y = load_y4<YBF16>(Y, (size_t)rs[j] * d + c);
             a.x = fmaf(wj, y.x, a.x);
             a.y = fmaf(wj, y.y, a.y);
             a.z = fmaf(wj, y.z, a.z);
@@ -56,12 +66,16 @@ __global__ __launch_bounds__(256) void combine_kernel(
 
 hipError_t launch_combine(const Plan &p) {
     const bool acc = (p.flags & MOE_FLAG_ACCUMULATE) != 0;
-    if (p.xdt == MOE_DTYPE_BF16)
-        hipLaunchKernelGGL((combine_kernel<true>), dim3(p.N, (p.d + 1023) / 1024), dim3(256), 0, p.stream, p.Y, p.tw, p.rop, p.out, p.N,
-                           p.d, p.k, acc);
-    else
-        hipLaunchKernelGGL((combine_kernel<false>), dim3(p.N, (p.d + 1023) / 1024), dim3(256), 0, p.stream, p.Y, p.tw, p.rop, p.out, p.N,
-                           p.d, p.k, acc);
+    const bool ybf16 = !p.use_stream;  // the grouped GEMMs store Y in bfloat16
+    dim3 grid(p.N, (p.d + 1023) / 1024), block(256);
+#define FGS_COMBINE(OB, YB) hipLaunchKernelGGL((combine_kernel<OB, YB>), grid, block, 0, p.stream, p.Y, p.tw, p.rop, \
+                                             p.out, p.N, p.d, p.k, acc)
+    if (p.xdt == MOE_DTYPE_BF16) {
+        if (ybf16) FGS_COMBINE(true, true); else FGS_COMBINE(true, false);
+    } else {
+        if (ybf16) FGS_COMBINE(false, true); else FGS_COMBINE(false, false);
+    }
+#undef FGS_COMBINE
     return hipGetLastError();
 }
 

@@ -1,0 +1,395 @@
+// Grouped expert GEMMs on bf16 matrix cores (batches larger than the decode path).
+//
+// "Inside Kolibri 1" (flozi.net), section "Routing: selection bias and
+// mixture weights are separate": every routed or shared expert is a SwiGLU
+// MLP (two 2560 -> 512 projections forming SiLU(gate) x up, then 512 -> 2560)
+// and there is no per-expert capacity, so the rows per expert vary from zero
+// to most of the batch.  Section "The FP8 path is explicitly mixed precision":
+// FP8 E4M3 weights with FP32 scales; here the scale is per output channel, so
+// it factors out of the dot product and is applied exactly in the epilogue.
+//
+// Work list: the dispatch scan writes one tile per 128 rows of every
+// non-empty group (shared expert first).  The grid is (column blocks, tiles)
+// with column blocks fastest, so the workgroups of one expert run together and
+// its weight slices are fetched from HBM once and re-read from cache by the
+// expert's other row tiles.  Skewed routing just yields more row tiles for the
+// popular experts.
+//
+// Workgroup tile: 128 rows x 128 GEMM columns, K step 64, 4 waves in a 2 x 2
+// layout, each wave 64 x 64 with 16 MFMA 16x16x32 bf16 accumulators.  Operand
+// tiles pass through double-buffered LDS with rows padded to 72 elements (144
+// bytes), which puts the 16-byte fragment reads of 8 consecutive lanes on 32
+// distinct banks.
+//   gate/up: A = x rows gathered through pair_of_row; B rows 0..63 are gate
+//            rows c0..c0+63 and B rows 64..127 the matching up rows, so every
+//            lane holds a gate and an up result of the same (row, column) and
+//            the SwiGLU epilogue is lane-local.  Writes H (bf16).
+//   down:    A = H rows of the group (contiguous), B = down rows; writes Y
+//            (bf16) for the combine kernel.
+// FP8 weights are decoded to bf16 (exact: E4M3 values are bf16 values) while
+// being written to LDS.
+#include "moe_common.h"
+#include "moe_plan.h"
+
+namespace fgs {
+
+constexpr int kBM = 128;       // rows per tile (the dispatch row tile)
+constexpr int kBN = 128;       // GEMM columns per tile
+constexpr int kBK = 64;        // K per stage
+constexpr int kLdsStride = 72; // padded row length in LDS (elements)
+constexpr int kTileElems = 128 * kLdsStride;
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const uint4 &a, const uint4 &b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// 8 E4M3 codes -> 8 bf16, exact (v_cvt_scalef32_pk_bf16_fp8 with scale 1; this
+// conversion was checked against the format definition for all 256 codes)
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(const uint2 &q) {
+    return make_uint4(e4m3x2_to_bf16x2<false>(q.x), e4m3x2_to_bf16x2<true>(q.x), e4m3x2_to_bf16x2<false>(q.y),
+                      e4m3x2_to_bf16x2<true>(q.y));
+}
+
+template <bool FP8> struct WRaw;
+template <> struct WRaw<false> { typedef uint4 T; };   // 8 bf16
+template <> struct WRaw<true> { typedef uint2 T; };    // 8 e4m3
+
+template <bool FP8>
+__device__ __forceinline__ typename WRaw<FP8>::T load_w8(const void *base, size_t elem) {
+    if constexpr (FP8) return *reinterpret_cast<const uint2 *>((const uint8_t *)base + elem);
+    else return *reinterpret_cast<const uint4 *>((const uint16_t *)base + elem);
+}
+template <bool FP8>
+__device__ __forceinline__ uint4 w8_to_bf16(const typename WRaw<FP8>::T &v) {
+    if constexpr (FP8) return e4m3x8_to_bf16x8(v);
+    else return v;
+}
+
+// Raw activation chunk of 8 elements: bf16 (one uint4) or FP32 (two float4,
+// rounded to bf16 when written to LDS)
+template <bool XF32> struct ARaw;
+template <> struct ARaw<false> { uint4 v; };
+template <> struct ARaw<true> { float4 lo, hi; };
+
+template <bool XF32>
+__device__ __forceinline__ ARaw<XF32> load_a8(const void *base, size_t elem) {
+    ARaw<XF32> r;
+    if constexpr (XF32) {
+        const float4 *p = reinterpret_cast<const float4 *>((const float *)base + elem);
+        r.lo = p[0];
+        r.hi = p[1];
+    } else {
+        r.v = *reinterpret_cast<const uint4 *>((const uint16_t *)base + elem);
+    }
+    return r;
+}
+template <bool XF32>
+__device__ __forceinline__ uint4 a8_to_bf16(const ARaw<XF32> &r, bool ok) {
+    uint4 v;
+    if constexpr (XF32)
+        v = make_uint4(pack_bf16x2(r.lo.x, r.lo.y), pack_bf16x2(r.lo.z, r.lo.w), pack_bf16x2(r.hi.x, r.hi.y),
+                       pack_bf16x2(r.hi.z, r.hi.w));
+    else
+        v = r.v;
+    return ok ? v : make_uint4(0, 0, 0, 0);
+}
+
+// Barrier for LDS hand-off only: waits for this wave's LDS operations, not
+// for its global loads, so prefetches stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One 128 x 128 x K tile product.  Per K stage each thread fetches 4 rows x 16
+// bytes of A and of B (tile row r = tid/8 + 32*j, chunk tid%8) into one of
+// two register slots, two stages ahead of their use; LDS holds two stages.
+// Stage kt: issue the loads of stage kt+2, multiply stage kt from LDS, write
+// stage kt+1 (loaded one stage earlier) to the other LDS buffer, barrier.
+// Fetches are plain loads from valid addresses (rows past the tile end read a
+// valid row); masking and format conversion happen when a stage is written
+// to LDS, so no instruction waits on a load before its stage is due.
+template <bool FP8, bool XF32>
+struct Stage {
+    ARaw<XF32> a[4];
+    typename WRaw<FP8>::T b[4];
+};
+
+template <bool FP8, bool XF32>
+__device__ __forceinline__ void tile_mma(const void *a_base, const size_t (&a_off)[4], const bool (&a_ok)[4],
+                                         const void *const (&b_base)[4], const size_t (&b_off)[4], int K,
+                                         uint16_t *lds, f32x4_t (&acc)[4][4]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int chunk = (tid & 7) * 8;
+    const int r0 = tid >> 3;
+    uint16_t *const As[2] = {lds, lds + 2 * kTileElems};
+    uint16_t *const Bs[2] = {lds + kTileElems, lds + 3 * kTileElems};
+    const int fr = lane & 15, fk = (lane >> 4) * 8;
+
+    auto fetch = [&](Stage<FP8, XF32> &st, int k0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            st.a[j] = load_a8<XF32>(a_base, a_off[j] + k0 + chunk);
+            st.b[j] = load_w8<FP8>(b_base[j], b_off[j] + k0 + chunk);
+        }
+    };
+    auto stash = [&](const Stage<FP8, XF32> &st, int buf) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = r0 + 32 * j;
+            *reinterpret_cast<uint4 *>(As[buf] + r * kLdsStride + chunk) = a8_to_bf16<XF32>(st.a[j], a_ok[j]);
+            *reinterpret_cast<uint4 *>(Bs[buf] + r * kLdsStride + chunk) = w8_to_bf16<FP8>(st.b[j]);
+        }
+    };
+    auto compute = [&](int buf) {
+#pragma unroll
+        for (int kk = 0; kk < kBK; kk += 32) {
+            uint4 af[4], bf[4];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                af[mi] = *reinterpret_cast<const uint4 *>(As[buf] + (wm * 64 + mi * 16 + fr) * kLdsStride + kk + fk);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                // wave wn owns B rows [wn*32, wn*32+32) and [64 + wn*32, 64 + wn*32 + 32)
+                const int brow = (ni < 2 ? wn * 32 + ni * 16 : 64 + wn * 32 + (ni - 2) * 16) + fr;
+                bf[ni] = *reinterpret_cast<const uint4 *>(Bs[buf] + brow * kLdsStride + kk + fk);
+            }
+            // B fragment as the MFMA's first operand: the result tile is
+            // transposed, so a lane holds 4 consecutive output columns of one
+            // row (lane % 16 = row, 4 * (lane / 16) + q = column)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_bf16(bf[ni], af[mi], acc[mi][ni]);
+        }
+    };
+
+    const int nk = K / kBK;
+    Stage<FP8, XF32> s0, s1;
+    fetch(s0, 0);
+    if (nk > 1) fetch(s1, kBK);
+    stash(s0, 0);
+    lds_barrier();
+    // Steady state, two stages per trip with no conditional loads or stores
+    // (slot s1 holds stage kt+1, issued one trip half earlier).  Keeping the
+    // body branch-free lets the compiler's load counters see that only the
+    // other slot's loads are outstanding, so it never waits on them early.
+    // sched_barrier(0) pins the phase order: the loads are issued first, so
+    // they are in flight through both multiply phases before their stage is
+    // written to LDS.
+    int kt = 0;
+    for (; kt + 3 < nk; kt += 2) {
+        fetch(s0, (kt + 2) * kBK);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(0);
+        __builtin_amdgcn_sched_barrier(0);
+        stash(s1, 1);
+        lds_barrier();
+        fetch(s1, (kt + 3) * kBK);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1);
+        __builtin_amdgcn_sched_barrier(0);
+        stash(s0, 0);
+        lds_barrier();
+    }
+    // tail: 1, 2 or 3 stages left (stage kt in LDS buffer 0, stage kt+1 in s1)
+    const int left = nk - kt;
+    if (left == 3) fetch(s0, (kt + 2) * kBK);
+    compute(0);
+    if (left >= 2) {
+        stash(s1, 1);
+        lds_barrier();
+        compute(1);
+        if (left == 3) {
+            stash(s0, 0);
+            lds_barrier();
+            compute(0);
+        }
+    }
+}
+
+// grid: (ceil(max(f, fs) / 64), tile capacity); block 256; LDS 4 * kTileElems * 2 bytes
+template <bool FP8, bool XF32>
+__global__ __launch_bounds__(256, 2) void gate_up_gemm_kernel(
+    const void *__restrict__ x, const void *__restrict__ wg, const void *__restrict__ wu,
+    const float *__restrict__ sg, const float *__restrict__ su, const void *__restrict__ wsg,
+    const void *__restrict__ wsu, const float *__restrict__ ssg, const float *__restrict__ ssu,
+    const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ por, uint16_t *__restrict__ H, int ldh, int d, int E, int k, int f, int fs) {
+    extern __shared__ uint16_t lds[];
+    const int u = blockIdx.y;
+    if (u >= *n_tiles) return;
+    const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
+    const bool shared = g == E;
+    const int fg = shared ? fs : f;
+    const int c0 = blockIdx.x * 64;
+    if (c0 >= fg) return;
+    const int gstart = offsets[g];
+    const int row0 = gstart + m0, m = min(kBM, offsets[g + 1] - row0);
+    const int tid = threadIdx.x;
+
+    size_t a_off[4], b_off[4];
+    bool a_ok[4];
+    const void *b_base[4];
+    const size_t wrow0 = shared ? 0 : (size_t)g * f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = (tid >> 3) + 32 * j;
+        a_ok[j] = r < m;
+        const int rr = a_ok[j] ? r : 0;  // rows past the tile end read row 0 (masked when stored)
+        const int t = shared ? (row0 + rr - gstart) : por[row0 + rr] / k;
+        a_off[j] = (size_t)t * d;
+        const bool up = r >= 64;
+        b_base[j] = up ? (shared ? wsu : wu) : (shared ? wsg : wg);
+        b_off[j] = (wrow0 + c0 + (r & 63)) * (size_t)d;
+    }
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    tile_mma<FP8, XF32>(x, a_off, a_ok, b_base, b_off, d, lds, acc);
+
+    // epilogue: acc[mi][ni][q] is row wm*64 + mi*16 + lane%16, GEMM column
+    // (B row) base(ni) + 4*(lane/16) + q; gate tile ni and up tile ni+2 share
+    // (row, column), so each lane writes 4 consecutive H values (8 bytes)
+    const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+        const int col = c0 + wn * 32 + ni * 16 + (lane >> 4) * 4;
+        float gs[4] = {1.f, 1.f, 1.f, 1.f}, us[4] = {1.f, 1.f, 1.f, 1.f};
+        if (FP8) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                gs[q] = shared ? ssg[col + q] : sg[wrow0 + col + q];
+                us[q] = shared ? ssu[col + q] : su[wrow0 + col + q];
+            }
+        }
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int r = wm * 64 + mi * 16 + (lane & 15);
+            if (r < m) {
+                float hv[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) hv[q] = silu(acc[mi][ni][q] * gs[q]) * (acc[mi][ni + 2][q] * us[q]);
+                *reinterpret_cast<uint2 *>(H + (size_t)(row0 + r) * ldh + col) =
+                    make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+            }
+        }
+    }
+}
+
+// grid: (d / 128, tile capacity); block 256
+template <bool FP8>
+__global__ __launch_bounds__(256, 2) void down_gemm_kernel(
+    const uint16_t *__restrict__ H, int ldh, const void *__restrict__ wd, const float *__restrict__ sd,
+    const void *__restrict__ wsd, const float *__restrict__ ssd, const int32_t *__restrict__ tiles,
+    const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets, uint16_t *__restrict__ Y, int d, int E,
+    int f, int fs) {
+    extern __shared__ uint16_t lds[];
+    const int u = blockIdx.y;
+    if (u >= *n_tiles) return;
+    const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
+    const bool shared = g == E;
+    const int fg = shared ? fs : f;
+    const int o0 = blockIdx.x * kBN;
+    const int row0 = offsets[g] + m0, m = min(kBM, offsets[g + 1] - row0);
+    const int tid = threadIdx.x;
+    const void *base = shared ? wsd : wd;
+    const size_t obase = shared ? 0 : (size_t)g * d;
+
+    size_t a_off[4], b_off[4];
+    bool a_ok[4];
+    const void *b_base[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = (tid >> 3) + 32 * j;
+        a_ok[j] = r < m;
+        a_off[j] = (size_t)(row0 + (a_ok[j] ? r : 0)) * ldh;
+        b_base[j] = base;
+        // B row r is output row o0 + r (rows past d re-read row 0; never stored)
+        b_off[j] = (obase + (o0 + r < d ? o0 + r : 0)) * (size_t)fg;
+    }
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    tile_mma<FP8, false>(H, a_off, a_ok, b_base, b_off, fg, lds, acc);
+
+    const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+        // B tile row (= output column) of this lane's 4 values, as in the fragment reads
+        const int o = o0 + (ni < 2 ? wn * 32 + ni * 16 : 64 + wn * 32 + (ni - 2) * 16) + (lane >> 4) * 4;
+        if (o >= d) continue;  // d is a multiple of 64, so o..o+3 are all in range or all out
+        float sc[4] = {1.f, 1.f, 1.f, 1.f};
+        if (FP8) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sc[q] = shared ? ssd[o + q] : sd[obase + o + q];
+        }
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int r = wm * 64 + mi * 16 + (lane & 15);
+            if (r < m)
+                *reinterpret_cast<uint2 *>(Y + (size_t)(row0 + r) * d + o) =
+                    make_uint2(pack_bf16x2(acc[mi][ni][0] * sc[0], acc[mi][ni][1] * sc[1]),
+                               pack_bf16x2(acc[mi][ni][2] * sc[2], acc[mi][ni][3] * sc[3]));
+        }
+    }
+}
+
+constexpr size_t kGemmLds = 4 * kTileElems * sizeof(uint16_t);  // 72 KiB: above the 64 KiB default
+
+template <typename K>
+static hipError_t allow_lds(K kernel) {
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)kGemmLds);
+}
+
+hipError_t gemm_kernels_init() {
+    hipError_t e;
+    if ((e = allow_lds(gate_up_gemm_kernel<true, false>)) != hipSuccess) return e;
+    if ((e = allow_lds(gate_up_gemm_kernel<false, false>)) != hipSuccess) return e;
+    if ((e = allow_lds(gate_up_gemm_kernel<true, true>)) != hipSuccess) return e;
+    if ((e = allow_lds(gate_up_gemm_kernel<false, true>)) != hipSuccess) return e;
+    if ((e = allow_lds(down_gemm_kernel<true>)) != hipSuccess) return e;
+    return allow_lds(down_gemm_kernel<false>);
+}
+
+hipError_t launch_gate_up_gemm(const Plan &p) {
+    const int fmax = p.f > p.fs ? p.f : p.fs;
+    dim3 grid((fmax + 63) / 64, p.max_tiles), block(256);
+#define FGS_GUG(F8, XF)                                                                                         \
+    hipLaunchKernelGGL((gate_up_gemm_kernel<F8, XF>), grid, block, kGemmLds, p.stream, p.x, p.W.w_gate, p.W.w_up, \
+                       p.W.s_gate, p.W.s_up, p.W.ws_gate, p.W.ws_up, p.W.ss_gate, p.W.ss_up, p.tiles, p.n_tiles,  \
+                       p.offsets, p.por, p.H, p.ldh, p.d, p.E, p.k, p.f, p.fs)
+    const bool fp8 = p.wdt == MOE_DTYPE_FP8_E4M3, xf32 = p.xdt == MOE_DTYPE_F32;
+    if (fp8) { if (xf32) FGS_GUG(true, true); else FGS_GUG(true, false); }
+    else { if (xf32) FGS_GUG(false, true); else FGS_GUG(false, false); }
+#undef FGS_GUG
+    return hipGetLastError();
+}
+
+hipError_t launch_down_gemm(const Plan &p) {
+    dim3 grid((p.d + kBN - 1) / kBN, p.max_tiles), block(256);
+    uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y);
+    if (p.wdt == MOE_DTYPE_FP8_E4M3)
+        hipLaunchKernelGGL((down_gemm_kernel<true>), grid, block, kGemmLds, p.stream, p.H, p.ldh, p.W.w_down,
+                           p.W.s_down, p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, Y, p.d, p.E, p.f,
+                           p.fs);
+    else
+        hipLaunchKernelGGL((down_gemm_kernel<false>), grid, block, kGemmLds, p.stream, p.H, p.ldh, p.W.w_down,
+                           p.W.s_down, p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, Y, p.d, p.E, p.f,
+                           p.fs);
+    return hipGetLastError();
+}
+
+}  // namespace fgs

@@ -11,7 +11,7 @@ namespace {
 thread_local int g_last_hip_error = 0;
 std::atomic<int> g_arch_state[64];  // 0 unknown, 1 gfx950, 2 other
 
-constexpr int kStreamMaxN = 64;     // decode-shaped expert path up to this batch
+std::atomic<int> g_gemm_init{0};    // 0 not yet, 1 done, -1 failed
 
 int check_device() {
     int dev = 0;
@@ -42,14 +42,13 @@ int check_desc(const moe_desc *d) {
     if (d->flags & ~MOE_FLAG_ACCUMULATE) return MOE_ERR_ARG;
     if (d->x_dtype != MOE_DTYPE_F32 && d->x_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
     if (d->w_dtype != MOE_DTYPE_BF16 && d->w_dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
-    // decode-shaped expert kernels: whole rows live in registers / LDS
-    if (d->d_model > 4096 || d->d_ff > 512 || d->d_ff_shared > 512) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
 struct Layout {
     size_t partial, ids, tw, blk, offsets, tiles, n_tiles, por, rop, H, Y, total;
     int ks, kslice, nblk, max_tiles, bm, ldh;
+    bool stream;
 };
 
 size_t take(size_t &cur, size_t bytes) {
@@ -69,7 +68,8 @@ Layout layout_for(const moe_desc *d) {
     L.kslice = d->d_model / L.ks;
     L.nblk = (int)((N + 255) / 256);
     if (L.nblk < 1) L.nblk = 1;
-    L.bm = d->n_tokens <= kStreamMaxN ? (d->n_tokens > 0 ? d->n_tokens : 1) : 32;
+    L.stream = stream_path(d->n_tokens, d->d_model, d->d_ff, d->d_ff_shared);
+    L.bm = L.stream ? (d->n_tokens > 0 ? d->n_tokens : 1) : kGemmBM;
     L.max_tiles = max_tiles_for(d->n_tokens, d->top_k, d->n_experts, L.bm);
     L.ldh = d->d_ff > d->d_ff_shared ? d->d_ff : d->d_ff_shared;
     const size_t rows = N * k + N;
@@ -146,6 +146,11 @@ int moe_forward(const moe_desc *desc, const void *x, const float *router_w, cons
     if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
     st = check_device();
     if (st != MOE_OK) return st;
+    if (!L.stream && g_gemm_init.load(std::memory_order_acquire) != 1) {
+        hipError_t e = gemm_kernels_init();
+        if (e != hipSuccess) { g_last_hip_error = (int)e; return MOE_ERR_HIP; }
+        g_gemm_init.store(1, std::memory_order_release);
+    }
 
     char *ws = (char *)workspace;
     Plan p{};
@@ -168,13 +173,14 @@ int moe_forward(const moe_desc *desc, const void *x, const float *router_w, cons
     p.rop = (aux && aux->row_of_pair) ? aux->row_of_pair : (int32_t *)(ws + L.rop);
     p.H = (uint16_t *)(ws + L.H); p.ldh = L.ldh;
     p.Y = (float *)(ws + L.Y);
-    p.use_stream = true;
+    p.use_stream = L.stream;
     p.stream = (hipStream_t)stream;
 
     void **ev = (aux && aux->stage_events) ? aux->stage_events : nullptr;
     typedef hipError_t (*Stage)(const Plan &);
     const Stage stages[MOE_NUM_STAGES] = {launch_router, launch_topk, launch_dispatch,
-                                          launch_gate_up, launch_down, launch_combine};
+                                          p.use_stream ? launch_gate_up : launch_gate_up_gemm,
+                                          p.use_stream ? launch_down : launch_down_gemm, launch_combine};
     for (int s = 0; s < MOE_NUM_STAGES; ++s) {
         hipError_t e;
         if (ev && ev[2 * s]) {

@@ -37,8 +37,8 @@ struct Plan {
     int32_t *por, *rop;  // [N*k]
     uint16_t *H;         // [N*k + N][ldh] bfloat16 SwiGLU activations
     int ldh;
-    float *Y;            // [N*k + N][d] float32 expert outputs
-    bool use_stream;     // decode-shaped expert path
+    float *Y;            // [N*k + N][d] expert outputs: float32 (stream path) or bfloat16 (GEMM path)
+    bool use_stream;     // decode-shaped expert path; otherwise the grouped GEMMs
     hipStream_t stream;
 };
 
@@ -49,6 +49,16 @@ hipError_t launch_dispatch(const Plan &p);
 hipError_t launch_gate_up(const Plan &p);
 hipError_t launch_down(const Plan &p);
 hipError_t launch_combine(const Plan &p);
+hipError_t launch_gate_up_gemm(const Plan &p);
+hipError_t launch_down_gemm(const Plan &p);
+hipError_t gemm_kernels_init();  // once per process: raise the kernels' LDS limit
+
+// Decode-shaped expert kernels keep whole weight rows in registers.
+constexpr int kStreamMaxN = 64;
+inline bool stream_path(int N, int d, int f, int fs) {
+    return N <= kStreamMaxN && d <= 4096 && f <= 512 && fs <= 512;
+}
+constexpr int kGemmBM = 128;  // rows per tile of the grouped GEMMs
 
 // Router tiling: wave tile of (16*MT tokens) x (16*NT experts); the k range is
 // cut into ks slices so that small batches still spread over many waves.

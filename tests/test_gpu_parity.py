@@ -86,3 +86,20 @@ def test_zero_tokens_is_noop():
     out = torch.empty_like(x)
     layer.forward(x, out=out)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["prefill", "fp8", "zipf"])
+def test_full_size_sampled(name):
+    """Full-size workloads: routing and layout of every token, output of a sample."""
+    cfg = get_config(name)
+    _say(f"case {name} N={cfg.n_tokens} w={cfg.w_dtype} bias={cfg.bias_kind} (sampled outputs)")
+    host = generate(cfg, seed=0)
+    g = PA.run_gpu(cfg, PA.to_device(host))
+    stats = PA.sampled_check(cfg, host, g, n_sample=24)
+    counts = np.diff(g["expert_offsets"])
+    stats["empty_experts"] = int((counts == 0).sum())
+    stats["max_expert_rows"] = int(counts.max())
+    _say(f"  -> {stats}")
+    if name == "zipf":
+        # skewed routing: some experts receive no token, one receives most
+        assert stats["empty_experts"] > 0 and stats["max_expert_rows"] > cfg.n_tokens // 2
