@@ -15,15 +15,16 @@
 // expert's other row tiles.  Skewed routing just yields more row tiles for the
 // popular experts.
 //
-// Workgroup tile: 128 rows x 128 GEMM columns, K step 64, 4 waves in a 2 x 2
-// layout, each wave 64 x 64 with 16 MFMA 16x16x32 bf16 accumulators.  Operand
-// tiles pass through double-buffered LDS with rows padded to 72 elements (144
-// bytes), which puts the 16-byte fragment reads of 8 consecutive lanes on 32
-// distinct banks.
-//   gate/up: A = x rows gathered through pair_of_row; B rows 0..63 are gate
-//            rows c0..c0+63 and B rows 64..127 the matching up rows, so every
-//            lane holds a gate and an up result of the same (row, column) and
-//            the SwiGLU epilogue is lane-local.  Writes H (bf16).
+// Workgroup tile: 128 rows x 256 GEMM columns, K step 64, 512 threads = 8
+// waves in a 2 (rows) x 4 (columns) layout, each wave 64 x 64 with 16 MFMA
+// 16x16x32 bf16 accumulators.  A 128 x 256 x 64 stage moves 48 KB for 4.2
+// MFLOP (87 flop per byte of L2 traffic).  Operand tiles pass through
+// double-buffered LDS (rows padded to 72 elements); a wave skips the 16-row
+// MFMA sub-tiles that lie entirely past the group's last row.
+//   gate/up: A = x rows gathered through pair_of_row; B rows 0..127 are gate
+//            rows c0..c0+127 and B rows 128..255 the matching up rows, so
+//            every lane holds a gate and an up result of the same (row,
+//            column) and the SwiGLU epilogue is lane-local.  Writes H (bf16).
 //   down:    A = H rows of the group (contiguous), B = down rows; writes Y
 //            (bf16) for the combine kernel.
 // FP8 weights are decoded to bf16 (exact: E4M3 values are bf16 values) while
@@ -33,11 +34,29 @@
 
 namespace fgs {
 
-constexpr int kBM = 128;       // rows per tile (the dispatch row tile)
-constexpr int kBN = 128;       // GEMM columns per tile
-constexpr int kBK = 64;        // K per stage
-constexpr int kLdsStride = 72; // padded row length in LDS (elements)
-constexpr int kTileElems = 128 * kLdsStride;
+constexpr int kBM = 128;        // rows per tile (the dispatch row tile)
+constexpr int kBK = 64;         // K per stage
+constexpr int kLdsStride = 72;  // padded row length in LDS (elements)
+
+// Tile geometry for WN column waves: 2 x WN waves (128 * WN threads), tile
+// 128 rows x 64*WN columns.  Expert GEMMs use WN = 4, the router WN = 2.
+template <int WN>
+struct Geo {
+    static constexpr int kThreads = 128 * WN;
+    static constexpr int kBN = 64 * WN;
+    static constexpr int kAElems = kBM * kLdsStride;
+    static constexpr int kBElems = kBN * kLdsStride;
+    static constexpr int kStageElems = kAElems + kBElems;
+    static constexpr int kAPer = kBM * 8 / kThreads;  // 16-byte A chunks per thread per stage
+    static constexpr int kBPer = kBN * 8 / kThreads;  // 16-byte B chunks per thread per stage (4)
+    static constexpr size_t kLds = 2 * kStageElems * sizeof(uint16_t);
+};
+constexpr int kWN = 4;
+constexpr int kThreads = Geo<kWN>::kThreads;  // 512
+constexpr int kBN = Geo<kWN>::kBN;            // 256
+constexpr int kAPer = Geo<kWN>::kAPer;
+constexpr int kBPer = Geo<kWN>::kBPer;
+constexpr size_t kGemmLds = Geo<kWN>::kLds;   // 108 KiB
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const uint4 &a, const uint4 &b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -107,83 +126,97 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// One 128 x 128 x K tile product.  Per K stage each thread fetches 4 rows x 16
-// bytes of A and of B (tile row r = tid/8 + 32*j, chunk tid%8) into one of
-// two register slots, two stages ahead of their use; LDS holds two stages.
-// Stage kt: issue the loads of stage kt+2, multiply stage kt from LDS, write
-// stage kt+1 (loaded one stage earlier) to the other LDS buffer, barrier.
-// Fetches are plain loads from valid addresses (rows past the tile end read a
-// valid row); masking and format conversion happen when a stage is written
-// to LDS, so no instruction waits on a load before its stage is due.
-template <bool FP8, bool XF32>
+// B tile row of a wave's column fragment ni: the wave in column wn owns B rows
+// [wn*32, wn*32+32) (first half: gate rows for gate/up) and the rows
+// kBN/2 + [wn*32, wn*32+32) (second half: the matching up rows).
+template <int WN = kWN>
+__device__ __forceinline__ int b_row_of(int wn, int ni) {
+    return ni < 2 ? wn * 32 + ni * 16 : Geo<WN>::kBN / 2 + wn * 32 + (ni - 2) * 16;
+}
+
+// One 128 x 256 x K tile product.  Per K stage each thread fetches kAPer A
+// chunks and kBPer B chunks of 16 bytes (tile row r = tid/8 + 64*j, chunk
+// tid%8) into one of two register slots, two stages ahead of their use; LDS
+// holds two stages.  Stage kt: issue the loads of stage kt+2, multiply stage
+// kt from LDS, write stage kt+1 (loaded one stage earlier) to the other LDS
+// buffer, barrier.  Fetches are plain loads from valid addresses (rows past
+// the tile end read a valid row); masking and format conversion happen when a
+// stage is written to LDS, so no instruction waits on a load early.
+template <bool FP8, bool XF32, int WN>
 struct Stage {
-    ARaw<XF32> a[4];
-    typename WRaw<FP8>::T b[4];
+    ARaw<XF32> a[Geo<WN>::kAPer];
+    typename WRaw<FP8>::T b[Geo<WN>::kBPer];
 };
 
-template <bool FP8, bool XF32>
-__device__ __forceinline__ void tile_mma(const void *a_base, const size_t (&a_off)[4], const bool (&a_ok)[4],
-                                         const void *const (&b_base)[4], const size_t (&b_off)[4], int K,
-                                         uint16_t *lds, f32x4_t (&acc)[4][4]) {
+// The product covers GEMM columns [k_base, k_base + K).  `a_kmod`: the A
+// column read for GEMM column k is k mod a_kmod (the router repeats x three
+// times along K); pass a value above every k for a plain product.
+template <bool FP8, bool XF32, int WN = kWN>
+__device__ __forceinline__ void tile_mma(const void *a_base, const size_t (&a_off)[Geo<WN>::kAPer],
+                                         const bool (&a_ok)[Geo<WN>::kAPer], const void *const (&b_base)[Geo<WN>::kBPer],
+                                         const size_t (&b_off)[Geo<WN>::kBPer], int k_base, int K, int a_kmod,
+                                         int m, uint16_t *lds, f32x4_t (&acc)[4][4]) {
+    using G = Geo<WN>;
+    constexpr int kRowStep = G::kThreads / 8;  // tile rows covered by one pass of the loader
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int chunk = (tid & 7) * 8;
     const int r0 = tid >> 3;
-    uint16_t *const As[2] = {lds, lds + 2 * kTileElems};
-    uint16_t *const Bs[2] = {lds + kTileElems, lds + 3 * kTileElems};
+    uint16_t *const As[2] = {lds, lds + G::kStageElems};
+    uint16_t *const Bs[2] = {lds + G::kAElems, lds + G::kStageElems + G::kAElems};
     const int fr = lane & 15, fk = (lane >> 4) * 8;
+    // 16-row sub-tiles of this wave that hold at least one row of the group
+    const int live = min(4, max(0, (m - wm * 64 + 15) / 16));
 
-    auto fetch = [&](Stage<FP8, XF32> &st, int k0) {
+    auto fetch = [&](Stage<FP8, XF32, WN> &st, int kl) {
+        const int k0 = k_base + kl;
+        const int ka = k0 % a_kmod;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            st.a[j] = load_a8<XF32>(a_base, a_off[j] + k0 + chunk);
-            st.b[j] = load_w8<FP8>(b_base[j], b_off[j] + k0 + chunk);
-        }
+        for (int j = 0; j < G::kAPer; ++j) st.a[j] = load_a8<XF32>(a_base, a_off[j] + ka + chunk);
+#pragma unroll
+        for (int j = 0; j < G::kBPer; ++j) st.b[j] = load_w8<FP8>(b_base[j], b_off[j] + k0 + chunk);
     };
-    auto stash = [&](const Stage<FP8, XF32> &st, int buf) {
+    auto stash = [&](const Stage<FP8, XF32, WN> &st, int buf) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = r0 + 32 * j;
-            *reinterpret_cast<uint4 *>(As[buf] + r * kLdsStride + chunk) = a8_to_bf16<XF32>(st.a[j], a_ok[j]);
-            *reinterpret_cast<uint4 *>(Bs[buf] + r * kLdsStride + chunk) = w8_to_bf16<FP8>(st.b[j]);
-        }
+        for (int j = 0; j < G::kAPer; ++j)
+            *reinterpret_cast<uint4 *>(As[buf] + (r0 + kRowStep * j) * kLdsStride + chunk) =
+                a8_to_bf16<XF32>(st.a[j], a_ok[j]);
+#pragma unroll
+        for (int j = 0; j < G::kBPer; ++j)
+            *reinterpret_cast<uint4 *>(Bs[buf] + (r0 + kRowStep * j) * kLdsStride + chunk) = w8_to_bf16<FP8>(st.b[j]);
     };
     auto compute = [&](int buf) {
 #pragma unroll
         for (int kk = 0; kk < kBK; kk += 32) {
             uint4 af[4], bf[4];
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-                af[mi] = *reinterpret_cast<const uint4 *>(As[buf] + (wm * 64 + mi * 16 + fr) * kLdsStride + kk + fk);
+            for (int ni = 0; ni < 4; ++ni)
+                bf[ni] = *reinterpret_cast<const uint4 *>(Bs[buf] + (b_row_of<WN>(wn, ni) + fr) * kLdsStride + kk + fk);
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                // wave wn owns B rows [wn*32, wn*32+32) and [64 + wn*32, 64 + wn*32 + 32)
-                const int brow = (ni < 2 ? wn * 32 + ni * 16 : 64 + wn * 32 + (ni - 2) * 16) + fr;
-                bf[ni] = *reinterpret_cast<const uint4 *>(Bs[buf] + brow * kLdsStride + kk + fk);
+            for (int mi = 0; mi < 4; ++mi) {
+                if (mi < live) {  // wave-uniform
+                    af[mi] = *reinterpret_cast<const uint4 *>(As[buf] + (wm * 64 + mi * 16 + fr) * kLdsStride + kk + fk);
+                    // B fragment as the MFMA's first operand: the result is
+                    // transposed, so a lane holds 4 consecutive output columns
+                    // of one row (lane % 16 = row, 4 * (lane / 16) + q = column)
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_bf16(bf[ni], af[mi], acc[mi][ni]);
+                }
             }
-            // B fragment as the MFMA's first operand: the result tile is
-            // transposed, so a lane holds 4 consecutive output columns of one
-            // row (lane % 16 = row, 4 * (lane / 16) + q = column)
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_bf16(bf[ni], af[mi], acc[mi][ni]);
         }
     };
 
     const int nk = K / kBK;
-    Stage<FP8, XF32> s0, s1;
+    Stage<FP8, XF32, WN> s0, s1;
     fetch(s0, 0);
     if (nk > 1) fetch(s1, kBK);
     stash(s0, 0);
     lds_barrier();
     // Steady state, two stages per trip with no conditional loads or stores
-    // (slot s1 holds stage kt+1, issued one trip half earlier).  Keeping the
-    // body branch-free lets the compiler's load counters see that only the
-    // other slot's loads are outstanding, so it never waits on them early.
-    // sched_barrier(0) pins the phase order: the loads are issued first, so
-    // they are in flight through both multiply phases before their stage is
-    // written to LDS.
+    // (slot s1 holds stage kt+1, issued one trip half earlier).  A branch-free
+    // body lets the compiler's load counters see that only the other slot's
+    // loads are outstanding; sched_barrier(0) pins the phase order so the
+    // loads are issued first and stay in flight through two multiply phases.
     int kt = 0;
     for (; kt + 3 < nk; kt += 2) {
         fetch(s0, (kt + 2) * kBK);
@@ -215,9 +248,9 @@ __device__ __forceinline__ void tile_mma(const void *a_base, const size_t (&a_of
     }
 }
 
-// grid: (ceil(max(f, fs) / 64), tile capacity); block 256; LDS 4 * kTileElems * 2 bytes
+// grid: (ceil(max(f, fs) / 128), tile capacity); block 512; LDS kGemmLds
 template <bool FP8, bool XF32>
-__global__ __launch_bounds__(256, 2) void gate_up_gemm_kernel(
+__global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
     const void *__restrict__ x, const void *__restrict__ wg, const void *__restrict__ wu,
     const float *__restrict__ sg, const float *__restrict__ su, const void *__restrict__ wsg,
     const void *__restrict__ wsu, const float *__restrict__ ssg, const float *__restrict__ ssu,
@@ -229,41 +262,49 @@ __global__ __launch_bounds__(256, 2) void gate_up_gemm_kernel(
     const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
     const bool shared = g == E;
     const int fg = shared ? fs : f;
-    const int c0 = blockIdx.x * 64;
+    constexpr int kHalf = kBN / 2;  // H columns per tile
+    const int c0 = blockIdx.x * kHalf;
     if (c0 >= fg) return;
     const int gstart = offsets[g];
     const int row0 = gstart + m0, m = min(kBM, offsets[g + 1] - row0);
     const int tid = threadIdx.x;
 
-    size_t a_off[4], b_off[4];
-    bool a_ok[4];
-    const void *b_base[4];
+    size_t a_off[kAPer], b_off[kBPer];
+    bool a_ok[kAPer];
+    const void *b_base[kBPer];
     const size_t wrow0 = shared ? 0 : (size_t)g * f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = (tid >> 3) + 32 * j;
+    for (int j = 0; j < kAPer; ++j) {
+        const int r = (tid >> 3) + 64 * j;
         a_ok[j] = r < m;
-        const int rr = a_ok[j] ? r : 0;  // rows past the tile end read row 0 (masked when stored)
+        const int rr = a_ok[j] ? r : 0;  // rows past the group end read row 0 (masked when stored)
         const int t = shared ? (row0 + rr - gstart) : por[row0 + rr] / k;
         a_off[j] = (size_t)t * d;
-        const bool up = r >= 64;
+    }
+#pragma unroll
+    for (int j = 0; j < kBPer; ++j) {
+        const int r = (tid >> 3) + 64 * j;
+        const bool up = r >= kHalf;
+        // columns past f_g (only when f_g is not a multiple of 128) re-read column c0; never stored
+        const int c = c0 + (r & (kHalf - 1));
         b_base[j] = up ? (shared ? wsu : wu) : (shared ? wsg : wg);
-        b_off[j] = (wrow0 + c0 + (r & 63)) * (size_t)d;
+        b_off[j] = (wrow0 + (c < fg ? c : c0)) * (size_t)d;
     }
     f32x4_t acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    tile_mma<FP8, XF32>(x, a_off, a_ok, b_base, b_off, d, lds, acc);
+    tile_mma<FP8, XF32>(x, a_off, a_ok, b_base, b_off, 0, d, d, m, lds, acc);
 
     // epilogue: acc[mi][ni][q] is row wm*64 + mi*16 + lane%16, GEMM column
-    // (B row) base(ni) + 4*(lane/16) + q; gate tile ni and up tile ni+2 share
-    // (row, column), so each lane writes 4 consecutive H values (8 bytes)
-    const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+    // (B row) b_row_of(wn, ni) + 4*(lane/16) + q; gate tile ni and up tile
+    // ni+2 share (row, H column), so each lane writes 4 consecutive H values
+    const int lane = tid & 63, wave = tid >> 6, wm = wave >> 2, wn = wave & 3;
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
         const int col = c0 + wn * 32 + ni * 16 + (lane >> 4) * 4;
+        if (col >= fg) continue;  // f_g is a multiple of 64: all four in range or all out
         float gs[4] = {1.f, 1.f, 1.f, 1.f}, us[4] = {1.f, 1.f, 1.f, 1.f};
         if (FP8) {
 #pragma unroll
@@ -286,9 +327,9 @@ __global__ __launch_bounds__(256, 2) void gate_up_gemm_kernel(
     }
 }
 
-// grid: (d / 128, tile capacity); block 256
+// grid: (ceil(d / 256), tile capacity); block 512; LDS kGemmLds
 template <bool FP8>
-__global__ __launch_bounds__(256, 2) void down_gemm_kernel(
+__global__ __launch_bounds__(kThreads) void down_gemm_kernel(
     const uint16_t *__restrict__ H, int ldh, const void *__restrict__ wd, const float *__restrict__ sd,
     const void *__restrict__ wsd, const float *__restrict__ ssd, const int32_t *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets, uint16_t *__restrict__ Y, int d, int E,
@@ -305,14 +346,18 @@ __global__ __launch_bounds__(256, 2) void down_gemm_kernel(
     const void *base = shared ? wsd : wd;
     const size_t obase = shared ? 0 : (size_t)g * d;
 
-    size_t a_off[4], b_off[4];
-    bool a_ok[4];
-    const void *b_base[4];
+    size_t a_off[kAPer], b_off[kBPer];
+    bool a_ok[kAPer];
+    const void *b_base[kBPer];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = (tid >> 3) + 32 * j;
+    for (int j = 0; j < kAPer; ++j) {
+        const int r = (tid >> 3) + 64 * j;
         a_ok[j] = r < m;
         a_off[j] = (size_t)(row0 + (a_ok[j] ? r : 0)) * ldh;
+    }
+#pragma unroll
+    for (int j = 0; j < kBPer; ++j) {
+        const int r = (tid >> 3) + 64 * j;
         b_base[j] = base;
         // B row r is output row o0 + r (rows past d re-read row 0; never stored)
         b_off[j] = (obase + (o0 + r < d ? o0 + r : 0)) * (size_t)fg;
@@ -322,14 +367,14 @@ __global__ __launch_bounds__(256, 2) void down_gemm_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    tile_mma<FP8, false>(H, a_off, a_ok, b_base, b_off, fg, lds, acc);
+    tile_mma<FP8, false>(H, a_off, a_ok, b_base, b_off, 0, fg, fg, m, lds, acc);
 
-    const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+    const int lane = tid & 63, wave = tid >> 6, wm = wave >> 2, wn = wave & 3;
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
-        // B tile row (= output column) of this lane's 4 values, as in the fragment reads
-        const int o = o0 + (ni < 2 ? wn * 32 + ni * 16 : 64 + wn * 32 + (ni - 2) * 16) + (lane >> 4) * 4;
-        if (o >= d) continue;  // d is a multiple of 64, so o..o+3 are all in range or all out
+        // B tile row (= output column) of this lane's 4 values
+        const int o = o0 + b_row_of(wn, ni) + (lane >> 4) * 4;
+        if (o >= d) continue;  // d is a multiple of 64: o..o+3 all in range or all out
         float sc[4] = {1.f, 1.f, 1.f, 1.f};
         if (FP8) {
 #pragma unroll
@@ -346,7 +391,97 @@ __global__ __launch_bounds__(256, 2) void down_gemm_kernel(
     }
 }
 
-constexpr size_t kGemmLds = 4 * kTileElems * sizeof(uint16_t);  // 72 KiB: above the 64 KiB default
+// ---------------------------------------------------------------- router
+// "Inside Kolibri 1" (flozi.net), section "Routing: selection bias and
+// mixture weights are separate": FP32 logits [N, 384] from the flattened
+// tokens.  For larger batches the router is one bf16 GEMM: each FP32 router
+// weight is split exactly into three bf16 terms (hi and mid by truncation,
+// lo = the rest, at most 8 significant bits) laid side by side along K,
+// W3[e] = [hi(W_r[e]) | mid(W_r[e]) | lo(W_r[e])], and the A loader reads x
+// three times along K.  Products of bf16 values are exact in FP32 and all 3d
+// terms of a logit accumulate in one FP32 accumulator.
+
+__global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ rw, uint16_t *__restrict__ w3,
+                                                           int E, int d) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (long)E * d) return;
+    const int e = (int)(i / d), kx = (int)(i % d);
+    const float v = rw[i];
+    const uint32_t uh = __float_as_uint(v) & 0xFFFF0000u;
+    const float r1 = v - __uint_as_float(uh);
+    const uint32_t um = __float_as_uint(r1) & 0xFFFF0000u;
+    const float r2 = r1 - __uint_as_float(um);
+    uint16_t *row = w3 + (size_t)e * 3 * d;
+    row[kx] = (uint16_t)(uh >> 16);
+    row[d + kx] = (uint16_t)(um >> 16);
+    row[2 * d + kx] = (uint16_t)f32_to_bf16_rne(r2);
+}
+
+// grid: (ceil(E / 128), ceil(N / 128), ks); block 256; LDS Geo<2>::kLds.
+// Slice z covers GEMM columns [z*3d/ks, (z+1)*3d/ks) and writes partial[z].
+__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__restrict__ x,
+                                                          const uint16_t *__restrict__ w3, float *__restrict__ partial,
+                                                          int N, int d, int E) {
+    using G = Geo<2>;
+    extern __shared__ uint16_t lds[];
+    const int t0 = blockIdx.y * kBM, e0 = blockIdx.x * G::kBN;
+    const int m = min(kBM, N - t0);
+    const int tid = threadIdx.x;
+    size_t a_off[G::kAPer], b_off[G::kBPer];
+    bool a_ok[G::kAPer];
+    const void *b_base[G::kBPer];
+#pragma unroll
+    for (int j = 0; j < G::kAPer; ++j) {
+        const int r = (tid >> 3) + (G::kThreads / 8) * j;
+        a_ok[j] = r < m;
+        a_off[j] = (size_t)(t0 + (a_ok[j] ? r : 0)) * d;
+    }
+#pragma unroll
+    for (int j = 0; j < G::kBPer; ++j) {
+        const int r = (tid >> 3) + (G::kThreads / 8) * j;
+        b_base[j] = w3;
+        b_off[j] = (size_t)(e0 + r < E ? e0 + r : 0) * 3 * d;  // rows past E re-read row 0; never stored
+    }
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int kslice = 3 * d / (int)gridDim.z;
+    tile_mma<false, false, 2>(x, a_off, a_ok, b_base, b_off, (int)blockIdx.z * kslice, kslice, d, m, lds, acc);
+    float *logits = partial + (size_t)blockIdx.z * N * E;
+
+    const int lane = tid & 63, wave = tid >> 6, wm = wave / 2, wn = wave % 2;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+        const int e = e0 + b_row_of<2>(wn, ni) + (lane >> 4) * 4;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int r = wm * 64 + mi * 16 + (lane & 15);
+            if (r >= m) continue;
+            float *dst = logits + (size_t)(t0 + r) * E + e;
+            if (e + 3 < E && (E & 3) == 0) {
+                *reinterpret_cast<float4 *>(dst) = make_float4(acc[mi][ni][0], acc[mi][ni][1], acc[mi][ni][2], acc[mi][ni][3]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (e + q < E) dst[q] = acc[mi][ni][q];
+            }
+        }
+    }
+}
+
+hipError_t launch_router_gemm(const Plan &p, uint16_t *w3) {
+    const long total = (long)p.E * p.d;
+    hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, p.stream, p.rw, w3,
+                       p.E, p.d);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 grid((p.E + Geo<2>::kBN - 1) / Geo<2>::kBN, (p.N + kBM - 1) / kBM, p.ks);
+    hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(Geo<2>::kThreads), Geo<2>::kLds, p.stream,
+                       (const uint16_t *)p.x, w3, p.partial, p.N, p.d, p.E);
+    return hipGetLastError();
+}
 
 template <typename K>
 static hipError_t allow_lds(K kernel) {
@@ -361,12 +496,15 @@ hipError_t gemm_kernels_init() {
     if ((e = allow_lds(gate_up_gemm_kernel<true, true>)) != hipSuccess) return e;
     if ((e = allow_lds(gate_up_gemm_kernel<false, true>)) != hipSuccess) return e;
     if ((e = allow_lds(down_gemm_kernel<true>)) != hipSuccess) return e;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(router_gemm_kernel),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)Geo<2>::kLds)) != hipSuccess)
+        return e;
     return allow_lds(down_gemm_kernel<false>);
 }
 
 hipError_t launch_gate_up_gemm(const Plan &p) {
     const int fmax = p.f > p.fs ? p.f : p.fs;
-    dim3 grid((fmax + 63) / 64, p.max_tiles), block(256);
+    dim3 grid((fmax + kBN / 2 - 1) / (kBN / 2), p.max_tiles), block(kThreads);
 #define FGS_GUG(F8, XF)                                                                                         \
     hipLaunchKernelGGL((gate_up_gemm_kernel<F8, XF>), grid, block, kGemmLds, p.stream, p.x, p.W.w_gate, p.W.w_up, \
                        p.W.s_gate, p.W.s_up, p.W.ws_gate, p.W.ws_up, p.W.ss_gate, p.W.ss_up, p.tiles, p.n_tiles,  \
@@ -379,7 +517,7 @@ hipError_t launch_gate_up_gemm(const Plan &p) {
 }
 
 hipError_t launch_down_gemm(const Plan &p) {
-    dim3 grid((p.d + kBN - 1) / kBN, p.max_tiles), block(256);
+    dim3 grid((p.d + kBN - 1) / kBN, p.max_tiles), block(kThreads);
     uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y);
     if (p.wdt == MOE_DTYPE_FP8_E4M3)
         hipLaunchKernelGGL((down_gemm_kernel<true>), grid, block, kGemmLds, p.stream, p.H, p.ldh, p.W.w_down,

@@ -46,9 +46,9 @@ int check_desc(const moe_desc *d) {
 }
 
 struct Layout {
-    size_t partial, ids, tw, blk, offsets, tiles, n_tiles, por, rop, H, Y, total;
+    size_t partial, ids, tw, blk, offsets, tiles, n_tiles, por, rop, H, Y, w3, total;
     int ks, kslice, nblk, max_tiles, bm, ldh;
-    bool stream;
+    bool stream, rgemm;
 };
 
 size_t take(size_t &cur, size_t bytes) {
@@ -60,8 +60,11 @@ size_t take(size_t &cur, size_t bytes) {
 Layout layout_for(const moe_desc *d) {
     Layout L{};
     const size_t N = d->n_tokens, E = d->n_experts, k = d->top_k;
+    L.rgemm = router_gemm(d->n_tokens, d->x_dtype);
     if (d->x_dtype == MOE_DTYPE_F32) {
         L.ks = 1;
+    } else if (L.rgemm) {
+        L.ks = router_gemm_ks(d->n_tokens, d->d_model, d->n_experts);
     } else {
         L.ks = router_tiling(d->n_tokens, d->d_model, d->n_experts).ks;
     }
@@ -85,6 +88,7 @@ Layout layout_for(const moe_desc *d) {
     L.rop = take(cur, N * k * 4);
     L.H = take(cur, rows * L.ldh * 2);
     L.Y = take(cur, rows * (size_t)d->d_model * 4);
+    L.w3 = take(cur, L.rgemm ? E * 3 * (size_t)d->d_model * 2 : 0);
     L.total = cur;
     return L;
 }
@@ -146,7 +150,7 @@ int moe_forward(const moe_desc *desc, const void *x, const float *router_w, cons
     if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
     st = check_device();
     if (st != MOE_OK) return st;
-    if (!L.stream && g_gemm_init.load(std::memory_order_acquire) != 1) {
+    if ((!L.stream || L.rgemm) && g_gemm_init.load(std::memory_order_acquire) != 1) {
         hipError_t e = gemm_kernels_init();
         if (e != hipSuccess) { g_last_hip_error = (int)e; return MOE_ERR_HIP; }
         g_gemm_init.store(1, std::memory_order_release);
@@ -173,6 +177,7 @@ int moe_forward(const moe_desc *desc, const void *x, const float *router_w, cons
     p.rop = (aux && aux->row_of_pair) ? aux->row_of_pair : (int32_t *)(ws + L.rop);
     p.H = (uint16_t *)(ws + L.H); p.ldh = L.ldh;
     p.Y = (float *)(ws + L.Y);
+    p.w3 = (uint16_t *)(ws + L.w3);
     p.use_stream = L.stream;
     p.stream = (hipStream_t)stream;
 

@@ -38,6 +38,7 @@ struct Plan {
     uint16_t *H;         // [N*k + N][ldh] bfloat16 SwiGLU activations
     int ldh;
     float *Y;            // [N*k + N][d] expert outputs: float32 (stream path) or bfloat16 (GEMM path)
+    uint16_t *w3;        // [E][3d] bf16 split of the router weights (router GEMM only)
     bool use_stream;     // decode-shaped expert path; otherwise the grouped GEMMs
     hipStream_t stream;
 };
@@ -51,6 +52,7 @@ hipError_t launch_down(const Plan &p);
 hipError_t launch_combine(const Plan &p);
 hipError_t launch_gate_up_gemm(const Plan &p);
 hipError_t launch_down_gemm(const Plan &p);
+hipError_t launch_router_gemm(const Plan &p, uint16_t *w3);
 hipError_t gemm_kernels_init();  // once per process: raise the kernels' LDS limit
 
 // Decode-shaped expert kernels keep whole weight rows in registers.
@@ -63,9 +65,24 @@ constexpr int kGemmBM = 128;  // rows per tile of the grouped GEMMs
 // Router tiling: wave tile of (16*MT tokens) x (16*NT experts); the k range is
 // cut into ks slices so that small batches still spread over many waves.
 struct RouterTiling { int mt, nt, ks; };
+// Batches above kRouterGemmN (bf16 activations) use the router GEMM instead
+// (one k-slice, W_r split into three bf16 terms along K).
+constexpr int kRouterGemmN = 64;
+inline bool router_gemm(int N, int xdt) { return xdt == MOE_DTYPE_BF16 && N > kRouterGemmN; }
+// k-slices of the router GEMM: enough workgroups to cover the chip; the slice
+// count divides the 3d/64 K stages
+inline int router_gemm_ks(int N, int d, int E) {
+    const long wgs = (long)((N + 127) / 128) * ((E + 127) / 128);
+    const int stages = 3 * d / 64;
+    const int cands[] = {1, 2, 3, 4, 5, 6, 8, 10};
+    int ks = 1;
+    for (int c : cands)
+        if (stages % c == 0 && ks < c && wgs * ks < 512) ks = c;
+    return ks;
+}
 inline RouterTiling router_tiling(int N, int d, int E) {
     RouterTiling r;
-    if (N <= 32) { r.mt = 2; r.nt = 1; } else { r.mt = 4; r.nt = 4; }
+    if (N <= kRouterGemmN) { r.mt = 2; r.nt = 1; } else { r.mt = 4; r.nt = 4; }
     long n_tb = (N + 16 * r.mt - 1) / (16 * r.mt);
     long n_eb = (E + 16 * r.nt - 1) / (16 * r.nt);
     long tiles = n_tb * n_eb;

@@ -13,6 +13,9 @@
 //
 // FP32 x: a plain FP32 FMA loop (small problems only).
 //
+// Batches above 64 tokens use the router GEMM of the expert-GEMM file (same
+// split, with the operands staged through LDS).
+//
 // The logits are written as partial sums over `ks` contiguous k-slices,
 // partial[s][t][e]; the top-k kernel adds the slices in a fixed order.  Small
 // token counts use several slices so that the 3.9 MB router matrix is read by
@@ -155,6 +158,7 @@ hipError_t launch_router(const Plan &p) {
                            (const float *)p.x, p.rw, p.partial, p.N, p.d, p.E);
         return hipGetLastError();
     }
+    if (router_gemm(p.N, p.xdt)) return launch_router_gemm(p, p.w3);
     const uint16_t *x = (const uint16_t *)p.x;
     RouterTiling rt = router_tiling(p.N, p.d, p.E);
     int n_tb = (p.N + 16 * rt.mt - 1) / (16 * rt.mt);
