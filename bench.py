@@ -200,38 +200,65 @@ def main():
     sw = 1 if cfg.w_dtype == "fp8" else 2
     sx = 4 if cfg.x_dtype == "f32" else 2
     sc = 4 if cfg.w_dtype == "fp8" else 0   # one FP32 scale per output channel
+    stream_path = N <= 64 and d <= 4096 and f <= 512 and fs <= 512
+    kind = "stream" if stream_path else "gemm"
 
+    # algorithmic bytes and flops per launch of the two expert kernels, for U
+    # touched routed experts (+ the shared expert)
     def gu_bytes(U):   # touched experts' gate+up rows (+ shared), x read once
         return (U * 2 * f * (d * sw + sc) + 2 * fs * (d * sw + sc) + N * d * sx)
 
     def dn_bytes(U):   # touched experts' down rows (+ shared)
         return (U * d * (f * sw + sc) + d * (fs * sw + sc))
 
+    gu_flops = 2.0 * (N * k * 2 * f + N * 2 * fs) * d
+    dn_flops = 2.0 * (N * k * f + N * fs) * d
+    mfma_peak = MFMA_PEAK_TFLOPS["bf16"]   # the expert matmuls run bf16 (FP8 weights are decoded)
+
+    def roof(name, bytes_sum, flops_sum, secs, n):
+        t_hbm = bytes_sum / (HBM_PEAK_GBS * 1e9)
+        t_mfma = flops_sum / (mfma_peak * 1e12)
+        hbm_frac = bytes_sum / secs / 1e9 / HBM_PEAK_GBS
+        mfma_frac = flops_sum / secs / 1e12 / mfma_peak
+        if t_hbm >= t_mfma:
+            r = {"bound": "hbm", "achieved": round(bytes_sum / secs / 1e9, 1), "peak": HBM_PEAK_GBS,
+                 "unit": "GB/s", "frac": round(hbm_frac, 4)}
+        else:
+            r = {"bound": "mfma", "achieved": round(flops_sum / secs / 1e12, 1), "peak": mfma_peak,
+                 "unit": "TFLOP/s", "frac": round(mfma_frac, 4)}
+        r.update({"kernel": name, "avg_launch_us": round(secs / n * 1e6, 2),
+                  "algorithmic_bytes_per_launch": int(bytes_sum / n), "flops_per_launch": int(flops_sum / n),
+                  "hbm_frac": round(hbm_frac, 4), "mfma_frac_bf16": round(mfma_frac, 4)})
+        return r
+
     gu_b = sum(gu_bytes(touched[i % L]) for i in range(args.steps))
     dn_b = sum(dn_bytes(touched[i % L]) for i in range(args.steps))
     gu_t, dn_t = sum(gu_ms) * 1e-3, sum(dn_ms) * 1e-3
-    dominant = ("gate_up_stream", gu_b, gu_t, len(gu_ms)) if gu_t >= dn_t else ("down_stream", dn_b, dn_t, len(dn_ms))
-    name, nbytes, secs, nl = dominant
-    achieved = nbytes / secs / 1e9
+    r_gu = roof(f"gate_up_{kind}", gu_b, gu_flops * args.steps, gu_t, len(gu_ms))
+    r_dn = roof(f"down_{kind}", dn_b, dn_flops * args.steps, dn_t, len(dn_ms))
+    dom = r_gu if gu_t >= dn_t else r_dn
 
     layer_bytes = [N * d * sx + E * d * 4 + E * 4 + touched[li] * 3 * (d * f * sw) + touched[li] * (2 * f + d) * sc
                    + 3 * d * fs * sw + (2 * fs + d) * sc + N * d * sx for li in range(L)]
     layer_b = sum(layer_bytes[i % L] for i in range(args.steps))
+    layer_flops = (2.0 * N * d * E + gu_flops + dn_flops) * args.steps
 
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.json")
     if os.path.exists(tpath):
         with open(tpath) as fh:
             tr = json.load(fh)
-        if tr.get("kernel_sources_hash") == kernel_sources_hash() and tr.get("kernel") == name:
+        if tr.get("kernel_sources_hash") == kernel_sources_hash() and tr.get("kernel") == dom["kernel"]:
             traffic = tr.get("bytes_per_launch")
 
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": name, "avg_launch_us": round(secs / nl * 1e6, 2),
-                "algorithmic_bytes_per_launch": int(nbytes / nl),
-                "whole_step_hbm_frac": round(layer_b / elapsed / 1e9 / HBM_PEAK_GBS, 4),
-                "gate_up_us": round(gu_t / len(gu_ms) * 1e6, 2), "down_us": round(dn_t / len(dn_ms) * 1e6, 2)}
+    roofline = {k2: dom[k2] for k2 in ("bound", "achieved", "peak", "unit", "frac")}
+    roofline["traffic"] = traffic
+    roofline.update({k2: v for k2, v in dom.items() if k2 not in roofline})
+    roofline["other_expert_kernel"] = r_dn if dom is r_gu else r_gu
+    roofline["whole_step"] = {"hbm_frac": round(layer_b / elapsed / 1e9 / HBM_PEAK_GBS, 4),
+                              "mfma_frac_bf16": round(layer_flops / elapsed / 1e12 / mfma_peak, 4),
+                              "algorithmic_bytes": int(layer_b / args.steps),
+                              "flops": int(layer_flops / args.steps)}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -240,7 +267,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: N={N} d={d} E={E} top_k={k} f={f} f_shared={fs} "
                                f"x={cfg.x_dtype} w={cfg.w_dtype} bias={cfg.bias_kind}",
-                   "n_tokens": N, "layers_cycled": L, "touched_experts": touched},
+                   "n_tokens": N, "layers_cycled": L, "touched_experts": touched, "expert_path": kind},
         "roofline": roofline,
     }
 
