@@ -87,13 +87,36 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int s = 32; s > 0; s >>= 1) {
-        uint64_t o = __shfl_xor(v, s, kWave);
-        v = o > v ? o : v;
+// partner lane's copy of a 32-bit value across lane bit log2(S): distance 32
+// and 16 by swapping a register with itself (v_permlane32_swap /
+// v_permlane16_swap), below that by DPP row_mirror, row_half_mirror and quad
+// permutes (the same pairings as the butterfly below)
+template <int S>
+__device__ __forceinline__ uint32_t partner_u32(uint32_t v) {
+    if constexpr (S == 32 || S == 16) {
+        auto r = (S == 32) ? __builtin_amdgcn_permlane32_swap(v, v, false, false)
+                           : __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (threadIdx.x & S) ? r[0] : r[1];
+    } else {
+        constexpr int ctrl = S == 8 ? 0x140 : S == 4 ? 0x141 : S == 2 ? 0x4E : 0xB1;
+        return __builtin_amdgcn_update_dpp(0u, v, ctrl, 0xF, 0xF, false);
     }
-    return v;
+}
+
+template <int S>
+__device__ __forceinline__ uint64_t max_step_u64(uint64_t v) {
+    const uint64_t o = ((uint64_t)partner_u32<S>((uint32_t)(v >> 32)) << 32) | partner_u32<S>((uint32_t)v);
+    return o > v ? o : v;
+}
+
+// wave-wide maximum of a 64-bit key, result in every lane
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = max_step_u64<32>(v);
+    v = max_step_u64<16>(v);
+    v = max_step_u64<8>(v);
+    v = max_step_u64<4>(v);
+    v = max_step_u64<2>(v);
+    return max_step_u64<1>(v);
 }
 
 // ---------------------------------------------------------------- butterfly

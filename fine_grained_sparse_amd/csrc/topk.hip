@@ -35,28 +35,41 @@ __global__ __launch_bounds__(256) void topk_kernel(
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= N) return;
 
+    // Logits: slices added in order 0..ks-1 (ks <= 10).  Every load is issued
+    // up front from a valid address (experts past E read expert 0, slices past
+    // ks re-read slice ks-1) and masked afterwards, so the loads of all slices
+    // and experts are in flight together.
     float h[VPL];
     uint64_t key[VPL];
     const size_t slice = (size_t)N * E;
+    const float *row = partial + (size_t)t * E;
+    constexpr int kMaxSlices = 10;
+    constexpr bool kAllAtOnce = VPL * kMaxSlices <= 60;
+    float part[kAllAtOnce ? VPL : 1][kMaxSlices];
+    if constexpr (kAllAtOnce) {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const int e = lane + 64 * v, ec = e < E ? e : 0;
+#pragma unroll
+            for (int s = 0; s < kMaxSlices; ++s) part[v][s] = row[(size_t)min(s, ks - 1) * slice + ec];
+        }
+    }
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
-        int e = lane + 64 * v;
+        const int e = lane + 64 * v, ec = e < E ? e : 0;
+        float p[kMaxSlices];
+#pragma unroll
+        for (int s = 0; s < kMaxSlices; ++s)
+            p[s] = kAllAtOnce ? part[kAllAtOnce ? v : 0][s] : row[(size_t)min(s, ks - 1) * slice + ec];
+        float acc = p[0];
+#pragma unroll
+        for (int s = 1; s < kMaxSlices; ++s) acc += s < ks ? p[s] : 0.0f;
+        h[v] = acc;
         if (e < E) {
-            const float *src = partial + (size_t)t * E + e;
-            // slices added in order 0, 1, ..., ks-1 (ks <= 10); loads issued together
-            float part[10];
-#pragma unroll
-            for (int s = 0; s < 10; ++s) part[s] = s < ks ? src[s * slice] : 0.f;
-            float acc = part[0];
-#pragma unroll
-            for (int s = 1; s < 10; ++s)
-                if (s < ks) acc += part[s];
-            h[v] = acc;
             if (logits_out) logits_out[(size_t)t * E + e] = acc;
-            float sc = acc + bias[e];
+            const float sc = acc + bias[e];
             key[v] = ((uint64_t)orderable(sc) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
         } else {
-            h[v] = 0.f;
             key[v] = 0;  // below every real key
         }
     }
@@ -87,7 +100,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
                     if (lane == owner) key[v] = 0;
                 }
             }
-            hv = __shfl(hv, owner, kWave);
+            hv = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(hv), owner));
             if (r < 8) { sel[r] = e; selh[r] = hv; }
             sk = sc;
         } else {
