@@ -19,7 +19,8 @@
 // waves in a 2 (rows) x 4 (columns) layout, each wave 64 x 64 with 16 MFMA
 // 16x16x32 bf16 accumulators.  A 128 x 256 x 64 stage moves 48 KB for 4.2
 // MFLOP (87 flop per byte of L2 traffic).  Operand tiles pass through
-// double-buffered LDS (rows padded to 72 elements); a wave skips the 16-row
+// double-buffered LDS (rows padded to 80 elements, which measured free of bank conflicts
+// for the 16-byte fragment reads); a wave skips the 16-row
 // MFMA sub-tiles that lie entirely past the group's last row.
 //   gate/up: A = x rows gathered through pair_of_row; B rows 0..127 are gate
 //            rows c0..c0+127 and B rows 128..255 the matching up rows, so
@@ -36,7 +37,7 @@ namespace fgs {
 
 constexpr int kBM = 128;        // rows per tile (the dispatch row tile)
 constexpr int kBK = 64;         // K per stage
-constexpr int kLdsStride = 72;  // padded row length in LDS (elements)
+constexpr int kLdsStride = 80;  // padded row length in LDS (elements): conflict-free 16-byte fragment reads
 
 // Tile geometry for WN column waves: 2 x WN waves (128 * WN threads), tile
 // 128 rows x 64*WN columns.  Expert GEMMs use WN = 4, the router WN = 2.
