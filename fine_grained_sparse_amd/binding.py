@@ -19,6 +19,7 @@ LIB_PATH = os.environ.get("FGS_MOE_LIB") or os.path.join(HERE, "libfgs_moe.so")
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3 = 0, 1, 2
 MOE_FLAG_ACCUMULATE = 1
+MOE_FLAG_RENORMALIZE = 2
 STAGES = ("router", "topk", "dispatch", "gate_up", "down", "combine")
 MOE_NUM_STAGES = len(STAGES)
 
@@ -136,11 +137,12 @@ class MoeLayer:
 
     def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, accumulate: bool = False,
                 aux: Optional[MoeAux] = None, router_w: Optional[torch.Tensor] = None,
-                router_b: Optional[torch.Tensor] = None) -> torch.Tensor:
+                router_b: Optional[torch.Tensor] = None, renormalize: bool = False) -> torch.Tensor:
         n = x.shape[0]
         if out is None:
             out = torch.empty_like(x)
-        desc = self.desc(n, MOE_FLAG_ACCUMULATE if accumulate else 0)
+        flags = (MOE_FLAG_ACCUMULATE if accumulate else 0) | (MOE_FLAG_RENORMALIZE if renormalize else 0)
+        desc = self.desc(n, flags)
         need = workspace_size(desc)
         if need > self.workspace.numel():
             self.workspace = torch.empty(need, dtype=torch.uint8, device=x.device)

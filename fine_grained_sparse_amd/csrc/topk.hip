@@ -4,7 +4,9 @@
 // mixture weights are separate": (1) add the learned expert-correction bias to
 // the logits and select the top six ids; (2) gather the unbiased logits of
 // those ids, apply a sigmoid and use the results as mixture weights without
-// renormalising them.
+// renormalising them.  With MOE_FLAG_RENORMALIZE the weights are instead the
+// softmax of the selected unbiased logits ("Kolibri 1 Deep Dive",
+// "Mathematical Routing & Load Balancing Formulation").
 //
 // One wave per token.  Lane l owns experts l, l+64, l+128, ...  Each of the
 // k+1 rounds takes the wave-wide maximum of a 64-bit key built from the score
@@ -30,7 +32,7 @@ template <int VPL>
 __global__ __launch_bounds__(256) void topk_kernel(
     const float *__restrict__ partial, int ks, const float *__restrict__ bias,
     float *__restrict__ logits_out, int32_t *__restrict__ ids, float *__restrict__ tw,
-    float *__restrict__ gap, int N, int E, int k) {
+    float *__restrict__ gap, int N, int E, int k, bool renorm) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= N) return;
@@ -119,6 +121,16 @@ __global__ __launch_bounds__(256) void topk_kernel(
                 float th = selh[j]; selh[j] = selh[j + 1]; selh[j + 1] = th;
             }
         }
+    // renormalised variant: exp(h_j - max) / sum over the selected ids, summed in slot order
+    float hmax = -__builtin_inff(), zsum = 0.f;
+    if (renorm) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < k) hmax = fmaxf(hmax, selh[j]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < k) zsum += expf(selh[j] - hmax);
+    }
     if (lane < k) {
         int e = 0;
         float hv = 0.f;
@@ -126,7 +138,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
         for (int j = 0; j < 8; ++j)
             if (j == lane) { e = sel[j]; hv = selh[j]; }
         ids[(size_t)t * k + lane] = e;
-        tw[(size_t)t * k + lane] = sigmoidf_(hv);
+        tw[(size_t)t * k + lane] = renorm ? expf(hv - hmax) / zsum : sigmoidf_(hv);
     }
     if (gap && lane == 0) gap[t] = (k < E) ? sk - sk1 : __builtin_inff();
 }
@@ -136,7 +148,7 @@ hipError_t launch_topk(const Plan &p) {
     int vpl = (p.E + 63) / 64;
 #define FGS_TOPK(V)                                                                              \
     hipLaunchKernelGGL((topk_kernel<V>), grid, block, 0, p.stream, p.partial, p.ks, p.rb,       \
-                       p.logits, p.ids, p.tw, p.gap, p.N, p.E, p.k)
+                       p.logits, p.ids, p.tw, p.gap, p.N, p.E, p.k, (p.flags & MOE_FLAG_RENORMALIZE) != 0)
     if (vpl <= 1) FGS_TOPK(1);
     else if (vpl <= 2) FGS_TOPK(2);
     else if (vpl <= 4) FGS_TOPK(4);

@@ -71,6 +71,11 @@ extern "C" {
 
 /* flags */
 #define MOE_FLAG_ACCUMULATE  (1u << 0)  /* out = round(out + y) instead of out = round(y) */
+#define MOE_FLAG_RENORMALIZE (1u << 1)  /* mixture weights = softmax of the selected unbiased
+                                           logits (sum to one), the gate of "Kolibri 1 Deep
+                                           Dive", "Mathematical Routing & Load Balancing
+                                           Formulation"; default off (sigmoid, not
+                                           renormalised) */
 
 /* pipeline stages, for optional timing events */
 #define MOE_STAGE_ROUTER    0   /* router logits */

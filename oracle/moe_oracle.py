@@ -168,13 +168,21 @@ def select_topk(h32: np.ndarray, bias: np.ndarray, k: int):
     return ids, gap, s
 
 
-def mixture_weights(h32: np.ndarray, ids: np.ndarray) -> np.ndarray:
+def mixture_weights(h32: np.ndarray, ids: np.ndarray, renormalize: bool = False) -> np.ndarray:
     """Rule step 2: sigmoid of the *unbiased* logits of the chosen ids.
 
     w[t, j] = 1 / (1 + exp(-h[t, ids[t, j]])), float64, not renormalised.
+
+    With `renormalize` the weights follow the other page's gate instead ("Kolibri
+    1 Deep Dive", "Mathematical Routing & Load Balancing Formulation"): the
+    exponentials of the selected logits divided by their sum over the selected
+    set, so they sum to one.  Still computed from the unbiased logits.
     """
     h = np.take_along_axis(np.asarray(h32, dtype=np.float32), ids.astype(np.int64), axis=1)
     h = h.astype(np.float64)
+    if renormalize:
+        z = np.exp(h - h.max(axis=1, keepdims=True))
+        return z / z.sum(axis=1, keepdims=True)
     return 1.0 / (1.0 + np.exp(-h))
 
 
@@ -264,7 +272,7 @@ def _finish(out64: np.ndarray, x_dtype: str, residual: Optional[np.ndarray]):
 
 
 def moe_forward(inp: Dict[str, np.ndarray], top_k: int, w_dtype: str, x_dtype: str,
-                residual: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                residual: Optional[np.ndarray] = None, renormalize: bool = False) -> Dict[str, np.ndarray]:
     """The whole layer for every token.
 
     `inp` holds numpy arrays as produced by moe_inputs.to_numpy.  With
@@ -277,7 +285,7 @@ def moe_forward(inp: Dict[str, np.ndarray], top_k: int, w_dtype: str, x_dtype: s
     n_exp = inp["router_w"].shape[0]
     h32 = router_logits(x64, inp["router_w"])
     ids, gap, s = select_topk(h32, inp["router_b"], top_k)
-    w = mixture_weights(h32, ids)
+    w = mixture_weights(h32, ids, renormalize)
     counts, offsets, pair_of_row, row_of_pair = dispatch(ids, n_exp)
 
     d = x64.shape[1]
@@ -299,7 +307,8 @@ def moe_forward(inp: Dict[str, np.ndarray], top_k: int, w_dtype: str, x_dtype: s
 
 
 def token_outputs(inp: Dict[str, np.ndarray], tokens: Sequence[int], top_k: int,
-                  w_dtype: str, ids: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                  w_dtype: str, ids: Optional[np.ndarray] = None,
+                  renormalize: bool = False) -> Dict[str, np.ndarray]:
     """Routing of every token, and the output of the listed tokens only.
 
     For full-size checks: the layer output of token t depends only on x[t],
@@ -312,7 +321,7 @@ def token_outputs(inp: Dict[str, np.ndarray], tokens: Sequence[int], top_k: int,
     h32 = router_logits(x64, inp["router_w"])
     own_ids, gap, _ = select_topk(h32, inp["router_b"], top_k)
     use_ids = own_ids if ids is None else np.asarray(ids)
-    w = mixture_weights(h32, use_ids)
+    w = mixture_weights(h32, use_ids, renormalize)
     shared = _shared_weights(inp, w_dtype)
     cache: Dict[int, tuple] = {}
     outs = []

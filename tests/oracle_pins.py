@@ -306,6 +306,36 @@ def pin_token_outputs_match_full(o):
     assert np.allclose(part["out64"], full["out64"][toks], rtol=1e-12, atol=1e-14)
 
 
+def pin_renormalized_weights(o):
+    """Renormalised gate: softmax over the selected unbiased logits.
+
+    Weights sum to one, their ratios are exp of logit differences, the bias
+    never scales them, and the hand-worked instance gives sigmoid(+-3).
+    """
+    rng = np.random.default_rng(9)
+    h = rng.standard_normal((30, 16)).astype(np.float32)
+    b = (rng.standard_normal(16) * 0.1).astype(np.float32)
+    ids, _, _ = o.select_topk(h, b, 5)
+    w = o.mixture_weights(h, ids, renormalize=True)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    hs = np.take_along_axis(h, ids.astype(np.int64), axis=1).astype(np.float64)
+    assert np.allclose(w[:, 0] / w[:, 1], np.exp(hs[:, 0] - hs[:, 1]), rtol=1e-12)
+    ids2, _, _ = o.select_topk(h, b + np.float32(0.5), 5)
+    assert np.array_equal(o.mixture_weights(h, ids2, renormalize=True), w)
+    # the worked example: selected logits 2 and -1
+    with open(os.path.join(GOLDEN, "worked_example.json")) as fh:
+        g = json.load(fh)
+    inp = dict(x=np.array(g["x"], np.float32), router_w=np.array(g["router_w"], np.float32),
+               router_b=np.array(g["router_b"], np.float32))
+    for key in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+        inp[key] = _bf16_bits(np.array(g[key], np.float32))
+    res = o.moe_forward(inp, 2, "bf16", "f32", renormalize=True)
+    assert np.allclose(res["w"][0], [_sig(3.0), _sig(-3.0)], rtol=1e-15, atol=0)
+    s1, s2, sm1 = _sig(1.0), _sig(3.0), _sig(-1.0)
+    want = [s1 + s2 * 2 * s1 - _sig(-3.0) * 2 * sm1, -s2 * s1 - _sig(-3.0) * 2 * sm1]
+    assert np.allclose(res["out64"][0], want, rtol=1e-14, atol=1e-15)
+
+
 def pin_page_arithmetic(o):
     """Expert parameter counts printed on the pages."""
     with open(os.path.join(GOLDEN, "page_arithmetic.json")) as fh:

@@ -33,7 +33,7 @@ def to_device(inputs: Dict[str, torch.Tensor], device="cuda") -> Dict[str, torch
 
 
 def run_gpu(cfg: LayerConfig, dev_inputs: Dict[str, torch.Tensor], residual: Optional[torch.Tensor] = None,
-            n_tokens: Optional[int] = None) -> Dict[str, np.ndarray]:
+            n_tokens: Optional[int] = None, renormalize: bool = False) -> Dict[str, np.ndarray]:
     """One moe_forward call with every optional output requested."""
     x = dev_inputs["x"]
     n = x.shape[0] if n_tokens is None else n_tokens
@@ -42,17 +42,18 @@ def run_gpu(cfg: LayerConfig, dev_inputs: Dict[str, torch.Tensor], residual: Opt
     aux = B.aux_struct(bufs)
     if residual is not None:
         out = residual.clone()
-        layer.forward(x, out=out, accumulate=True, aux=aux)
+        layer.forward(x, out=out, accumulate=True, aux=aux, renormalize=renormalize)
     else:
         out = torch.full_like(x, float("nan"))
-        layer.forward(x, out=out, aux=aux)
+        layer.forward(x, out=out, aux=aux, renormalize=renormalize)
     torch.cuda.synchronize()
     res = {k: v.cpu().numpy() for k, v in bufs.items()}
     res["out"] = out.float().cpu().numpy().astype(np.float64)
     return res
 
 
-def check_routing(cfg: LayerConfig, g: Dict[str, np.ndarray], ref: Dict[str, np.ndarray]) -> Dict[str, int]:
+def check_routing(cfg: LayerConfig, g: Dict[str, np.ndarray], ref: Dict[str, np.ndarray],
+                  renormalize: bool = False) -> Dict[str, int]:
     """Compare logits, ids, weights and layout; returns counts for reporting."""
     n = g["topk_ids"].shape[0]
     k, E = cfg.top_k, cfg.n_experts
@@ -72,7 +73,7 @@ def check_routing(cfg: LayerConfig, g: Dict[str, np.ndarray], ref: Dict[str, np.
     # ids ascending, distinct, in range
     assert np.all(np.diff(g["topk_ids"], axis=1) > 0) and g["topk_ids"].min() >= 0 and g["topk_ids"].max() < E
     # weights = sigmoid of the unbiased logit at the GPU's ids
-    w_ref = O.mixture_weights(ref["logits"], g["topk_ids"])
+    w_ref = O.mixture_weights(ref["logits"], g["topk_ids"], renormalize)
     assert np.allclose(g["topk_w"], w_ref, rtol=0, atol=2e-6), f"weights err {np.abs(g['topk_w'] - w_ref).max()}"
     # gap (diagnostic value) is close to the oracle's where the ids agree
     if k < E:
@@ -104,15 +105,15 @@ def check_output(cfg: LayerConfig, gpu_out: np.ndarray, ref_out: np.ndarray, tok
 
 
 def full_check(cfg: LayerConfig, host_inputs: Dict[str, torch.Tensor], g: Dict[str, np.ndarray],
-               residual: Optional[np.ndarray] = None) -> Dict[str, float]:
+               residual: Optional[np.ndarray] = None, renormalize: bool = False) -> Dict[str, float]:
     """Whole-layer oracle on every token (small and decode-sized cases)."""
     npi = to_numpy(host_inputs)
-    ref = O.moe_forward(npi, cfg.top_k, cfg.w_dtype, cfg.x_dtype, residual=residual)
-    stats = check_routing(cfg, g, ref)
+    ref = O.moe_forward(npi, cfg.top_k, cfg.w_dtype, cfg.x_dtype, residual=residual, renormalize=renormalize)
+    stats = check_routing(cfg, g, ref, renormalize)
     ref_out = ref["out64"].copy()
     diff = np.nonzero(np.any(g["topk_ids"] != ref["ids"], axis=1))[0]
     if diff.size:
-        alt = O.token_outputs(npi, diff, cfg.top_k, cfg.w_dtype, ids=g["topk_ids"])["out64"]
+        alt = O.token_outputs(npi, diff, cfg.top_k, cfg.w_dtype, ids=g["topk_ids"], renormalize=renormalize)["out64"]
         if residual is not None:
             alt = alt + (O.decode_bf16(residual[diff]) if residual.dtype == np.uint16 else residual[diff])
         ref_out[diff] = alt

@@ -51,7 +51,7 @@ def test_workspace_size_host_only(lib):
     assert B.workspace_size(_desc(n_tokens=64)) > n
     # invalid descriptions give 0
     for bad in (dict(top_k=0), dict(top_k=9), dict(n_experts=4, top_k=6), dict(d_model=100),
-                dict(d_ff=0), dict(n_tokens=-1), dict(flags=2), dict(n_experts=2000)):
+                dict(d_ff=0), dict(n_tokens=-1), dict(flags=4), dict(n_experts=2000)):
         assert B.workspace_size(_desc(**bad)) == 0, bad
 
 

@@ -24,9 +24,9 @@ def _need_gpu():
     binding.lib()  # raises if the library is missing
 
 
-def _run_full(cfg, seed=0, residual=False):
+def _run_full(cfg, seed=0, residual=False, renormalize=False):
     _say(f"case {cfg.name} N={cfg.n_tokens} d={cfg.d_model} E={cfg.n_experts} k={cfg.top_k} "
-         f"f={cfg.d_ff} x={cfg.x_dtype} w={cfg.w_dtype} seed={seed} residual={residual}")
+         f"f={cfg.d_ff} x={cfg.x_dtype} w={cfg.w_dtype} seed={seed} residual={residual} renorm={renormalize}")
     host = generate(cfg, seed=seed)
     dev = PA.to_device(host)
     res_t = res_np = None
@@ -35,8 +35,8 @@ def _run_full(cfg, seed=0, residual=False):
         r = torch.randn(host["x"].shape, generator=g).to(host["x"].dtype)
         res_t = r.cuda()
         res_np = r.view(torch.int16).numpy().view(np.uint16) if r.dtype == torch.bfloat16 else r.numpy()
-    g = PA.run_gpu(cfg, dev, residual=res_t)
-    stats = PA.full_check(cfg, host, g, residual=res_np)
+    g = PA.run_gpu(cfg, dev, residual=res_t, renormalize=renormalize)
+    stats = PA.full_check(cfg, host, g, residual=res_np, renormalize=renormalize)
     _say(f"  -> {stats}")
     return stats
 
@@ -66,6 +66,20 @@ def test_toy_variants(over):
 def test_accumulate_into_residual():
     _run_full(get_config("toy", x_dtype="bf16", n_tokens=50), residual=True)
     _run_full(get_config("toy", n_tokens=20), residual=True)
+
+
+@pytest.mark.parametrize("cfg_name,over", [
+    ("toy", {}), ("toy", dict(x_dtype="bf16", n_tokens=300)), ("decode", dict(n_tokens=8)),
+])
+def test_renormalized_gate(cfg_name, over):
+    """The softmax-over-selected gate variant (MOE_FLAG_RENORMALIZE)."""
+    _run_full(get_config(cfg_name, **over), renormalize=True)
+
+
+@pytest.mark.parametrize("n", [16, 200])
+def test_128_experts(n):
+    """The 128-expert shape of the predecessor model, top-6, full hidden size."""
+    _run_full(get_config("decode", n_experts=128, n_tokens=n))
 
 
 def test_deterministic():

@@ -19,11 +19,11 @@ MUTATIONS = {
                   "s = (h32 - b32[None, :]).astype(np.float32)"),
     "select_on_unbiased": ("s = (h32 + b32[None, :]).astype(np.float32)",
                            "s = (h32 + 0 * b32[None, :]).astype(np.float32)"),
-    "weights_renormalised": ("    h = h.astype(np.float64)\n    return 1.0 / (1.0 + np.exp(-h))",
-                             "    h = h.astype(np.float64)\n    w = 1.0 / (1.0 + np.exp(-h))\n"
+    "weights_renormalised": ("        return z / z.sum(axis=1, keepdims=True)\n    return 1.0 / (1.0 + np.exp(-h))",
+                             "        return z / z.sum(axis=1, keepdims=True)\n    w = 1.0 / (1.0 + np.exp(-h))\n"
                              "    return w / w.sum(axis=1, keepdims=True)"),
-    "weights_sign": ("    h = h.astype(np.float64)\n    return 1.0 / (1.0 + np.exp(-h))",
-                     "    h = h.astype(np.float64)\n    return 1.0 / (1.0 + np.exp(h))"),
+    "weights_sign": ("        return z / z.sum(axis=1, keepdims=True)\n    return 1.0 / (1.0 + np.exp(-h))",
+                     "        return z / z.sum(axis=1, keepdims=True)\n    return 1.0 / (1.0 + np.exp(h))"),
     "tie_to_higher_id": ("order = np.argsort(-s.astype(np.float64), axis=1, kind=\"stable\")",
                          "order = n_exp - 1 - np.argsort(-s[:, ::-1].astype(np.float64), axis=1, kind=\"stable\")"),
     "slots_by_score": ("ids = np.sort(chosen, axis=1).astype(np.int32)",
@@ -44,6 +44,10 @@ MUTATIONS = {
     "bf16_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
     "param_count": ("per_expert = 3 * d_model * d_ff", "per_expert = 2 * d_model * d_ff"),
     "residual_dropped": ("out64 = out64 + _x_to_f64(residual)", "out64 = out64"),
+    "renorm_no_max_shift_sign": ("z = np.exp(h - h.max(axis=1, keepdims=True))",
+                                 "z = np.exp(h.max(axis=1, keepdims=True) - h)"),
+    "renorm_ignored": ("    w = mixture_weights(h32, ids, renormalize)\n    counts,",
+                       "    w = mixture_weights(h32, ids)\n    counts,"),
 }
 
 
