@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "fp8", "zipf", "toy"])
     ap.add_argument("--tokens", type=int, default=None, help="override the batch size")
     ap.add_argument("--layers", type=int, default=4, help="independent layer instances cycled by the steps")
+    ap.add_argument("--variant", default="plain", choices=["plain", "renorm", "block"],
+                    help="plain moe_forward; renormalised gate; or moe_block_forward (sandwich RMSNorms, "
+                         "residual updated in place)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -134,7 +137,16 @@ def main():
     for m in mods[1:]:
         m.workspace = ws  # one workspace, calls are stream-ordered
     outs = [torch.empty_like(inp["x"]) for inp in layers]
-    descs = [m.desc(N) for m in mods]
+    flags = B.MOE_FLAG_RENORMALIZE if args.variant == "renorm" else 0
+    descs = [m.desc(N, flags) for m in mods]
+    if args.variant == "block":
+        need = max(int(B.lib().moe_block_workspace_size(ctypes.byref(dsc))) for dsc in descs)
+        if need > ws.numel():
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        gen = torch.Generator(device="cuda").manual_seed(77)
+        norms = [((1.0 + 0.1 * torch.randn(d, generator=gen, device="cuda")).to(torch.bfloat16).float(),
+                  (1.0 + 0.1 * torch.randn(d, generator=gen, device="cuda")).to(torch.bfloat16).float())
+                 for _ in range(L)]
     stream = torch.cuda.current_stream(dev).cuda_stream
 
     # routing of each instance (outside the timed region): touched experts
@@ -169,6 +181,16 @@ def main():
     def step(i, aux=None):
         li = i % L
         m = mods[li]
+        if args.variant == "block":
+            # the layer instance's token batch is its residual stream, updated in place
+            st = B.lib().moe_block_forward(ctypes.byref(descs[li]), layers[li]["x"].data_ptr(),
+                                           norms[li][0].data_ptr(), norms[li][1].data_ptr(), 1e-6,
+                                           layers[li]["router_w"].data_ptr(), layers[li]["router_b"].data_ptr(),
+                                           ctypes.byref(m.weights), ws.data_ptr(), ws.numel(),
+                                           ctypes.byref(aux) if aux is not None else None, stream)
+            if st != B.MOE_OK:
+                raise B.MoeError(st, "moe_block_forward")
+            return
         st = B.lib().moe_forward(ctypes.byref(descs[li]), layers[li]["x"].data_ptr(),
                                  layers[li]["router_w"].data_ptr(), layers[li]["router_b"].data_ptr(),
                                  ctypes.byref(m.weights), outs[li].data_ptr(), ws.data_ptr(), ws.numel(),
@@ -267,11 +289,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: N={N} d={d} E={E} top_k={k} f={f} f_shared={fs} "
                                f"x={cfg.x_dtype} w={cfg.w_dtype} bias={cfg.bias_kind}",
-                   "n_tokens": N, "layers_cycled": L, "touched_experts": touched, "expert_path": kind},
+                   "n_tokens": N, "layers_cycled": L, "touched_experts": touched, "expert_path": kind,
+                   "variant": args.variant},
         "roofline": roofline,
     }
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.variant == "plain":
         result["cpu_baseline"], result["parity_step0"] = cpu_baseline(cfg, layers[0], outs, mods, descs, ws, stream,
                                                                        args.cpu_seconds)
     print(json.dumps(result), flush=True)

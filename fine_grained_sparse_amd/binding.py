@@ -23,7 +23,8 @@ MOE_FLAG_RENORMALIZE = 2
 STAGES = ("router", "topk", "dispatch", "gate_up", "down", "combine")
 MOE_NUM_STAGES = len(STAGES)
 
-EXPORTED = ("moe_workspace_size", "moe_forward", "moe_status_string", "moe_last_hip_error")
+EXPORTED = ("moe_workspace_size", "moe_forward", "moe_status_string", "moe_last_hip_error",
+            "moe_block_workspace_size", "moe_block_forward")
 
 
 class MoeDesc(ctypes.Structure):
@@ -65,6 +66,12 @@ def lib() -> ctypes.CDLL:
                                   ctypes.POINTER(MoeWeights), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                   ctypes.POINTER(MoeAux), ctypes.c_void_p]
         L.moe_forward.restype = ctypes.c_int
+        L.moe_block_workspace_size.argtypes = [ctypes.POINTER(MoeDesc)]
+        L.moe_block_workspace_size.restype = ctypes.c_size_t
+        L.moe_block_forward.argtypes = [ctypes.POINTER(MoeDesc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(MoeWeights),
+                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(MoeAux), ctypes.c_void_p]
+        L.moe_block_forward.restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_hip_error.argtypes = []
@@ -152,6 +159,26 @@ class MoeLayer:
         if st != MOE_OK:
             raise MoeError(st, "moe_forward")
         return out
+
+
+    def block_forward(self, resid: torch.Tensor, norm_pre: torch.Tensor, norm_post: torch.Tensor, eps: float,
+                      aux: Optional[MoeAux] = None, renormalize: bool = False) -> torch.Tensor:
+        """Sandwich-normalised MoE sublayer; updates `resid` in place and returns it."""
+        n = resid.shape[0]
+        desc = self.desc(n, MOE_FLAG_RENORMALIZE if renormalize else 0)
+        need = int(lib().moe_block_workspace_size(ctypes.byref(desc)))
+        if need == 0:
+            raise MoeError(MOE_ERR_ARG, "moe_block_workspace_size")
+        if need > self.workspace.numel():
+            self.workspace = torch.empty(need, dtype=torch.uint8, device=resid.device)
+        stream = torch.cuda.current_stream(resid.device).cuda_stream
+        st = lib().moe_block_forward(ctypes.byref(desc), _ptr(resid), _ptr(norm_pre), _ptr(norm_post), eps,
+                                     _ptr(self.w["router_w"]), _ptr(self.w["router_b"]), ctypes.byref(self.weights),
+                                     _ptr(self.workspace), self.workspace.numel(),
+                                     ctypes.byref(aux) if aux is not None else None, stream)
+        if st != MOE_OK:
+            raise MoeError(st, "moe_block_forward")
+        return resid
 
 
 def route_outputs(n: int, E: int, k: int, device) -> Dict[str, torch.Tensor]:

@@ -123,13 +123,28 @@ const char *moe_status_string(int status) {
 
 int moe_last_hip_error(void) { return g_last_hip_error; }
 
-int moe_forward(const moe_desc *desc, const void *x, const float *router_w, const float *router_bias,
-                const moe_weights *weights, void *out, void *workspace, size_t workspace_bytes,
-                const moe_aux *aux, void *stream) {
+}  // extern "C"
+
+namespace fgs {
+namespace {
+
+// Sandwich-norm arguments of the block entry point (null for moe_forward).
+struct BlockArgs {
+    void *resid;
+    const float *norm_pre, *norm_post;
+    float eps;
+};
+
+int run_layer(const moe_desc *desc, const void *x, const float *router_w, const float *router_bias,
+              const moe_weights *weights, void *out, void *workspace, size_t workspace_bytes, const moe_aux *aux,
+              void *stream, const BlockArgs *blk) {
     int st = check_desc(desc);
     if (st != MOE_OK) return st;
+    if (blk && (desc->flags & MOE_FLAG_ACCUMULATE)) return MOE_ERR_ARG;
     if (desc->n_tokens == 0) return MOE_OK;
     if (!x || !router_w || !router_bias || !weights || !out || !workspace) return MOE_ERR_ARG;
+    if (blk && (!blk->norm_pre || !blk->norm_post || !(blk->eps >= 0.0f))) return MOE_ERR_ARG;
+    if (blk && desc->d_model > 16384) return MOE_ERR_UNSUPPORTED;  // the fused combine keeps a row in LDS
     const moe_weights &W = *weights;
     if (!W.w_gate || !W.w_up || !W.w_down || !W.ws_gate || !W.ws_up || !W.ws_down) return MOE_ERR_ARG;
     const bool fp8 = desc->w_dtype == MOE_DTYPE_FP8_E4M3;
@@ -140,14 +155,16 @@ int moe_forward(const moe_desc *desc, const void *x, const float *router_w, cons
     const void *ptrs16[] = {x, out, W.w_gate, W.w_up, W.w_down, W.ws_gate, W.ws_up, W.ws_down, router_w};
     for (const void *q : ptrs16)
         if (!aligned(q, 16)) return MOE_ERR_ARG;
+    if (blk && (!aligned(blk->norm_pre, 16) || !aligned(blk->norm_post, 16))) return MOE_ERR_ARG;
     if (!aligned(workspace, 256)) return MOE_ERR_ARG;
 
     const size_t xbytes = (size_t)desc->n_tokens * desc->d_model * (desc->x_dtype == MOE_DTYPE_F32 ? 4 : 2);
-    if (overlaps(x, xbytes, out, xbytes)) {
+    if (!blk && overlaps(x, xbytes, out, xbytes)) {
         if (!(desc->flags & MOE_FLAG_ACCUMULATE) || x != out) return MOE_ERR_ARG;
     }
     const Layout L = layout_for(desc);
-    if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+    const size_t need = L.total + (blk ? ((xbytes + 255) & ~size_t(255)) : 0);
+    if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
     st = check_device();
     if (st != MOE_OK) return st;
     if ((!L.stream || L.rgemm) && g_gemm_init.load(std::memory_order_acquire) != 1) {
@@ -180,12 +197,23 @@ int moe_forward(const moe_desc *desc, const void *x, const float *router_w, cons
     p.w3 = (uint16_t *)(ws + L.w3);
     p.use_stream = L.stream;
     p.stream = (hipStream_t)stream;
+    if (blk) {
+        // the normalised input lives after the layer's own workspace; the
+        // layer reads it as x and the fused combine updates the residual
+        p.x = ws + L.total;
+        p.out = blk->resid;
+        p.norm_post = blk->norm_post;
+        p.eps = blk->eps;
+        hipError_t e = launch_prenorm(p, blk->resid, blk->norm_pre, blk->eps, ws + L.total);
+        if (e != hipSuccess) { g_last_hip_error = (int)e; return MOE_ERR_HIP; }
+    }
 
     void **ev = (aux && aux->stage_events) ? aux->stage_events : nullptr;
     typedef hipError_t (*Stage)(const Plan &);
     const Stage stages[MOE_NUM_STAGES] = {launch_router, launch_topk, launch_dispatch,
                                           p.use_stream ? launch_gate_up : launch_gate_up_gemm,
-                                          p.use_stream ? launch_down : launch_down_gemm, launch_combine};
+                                          p.use_stream ? launch_down : launch_down_gemm,
+                                          blk ? launch_combine_block : launch_combine};
     for (int s = 0; s < MOE_NUM_STAGES; ++s) {
         hipError_t e;
         if (ev && ev[2 * s]) {
@@ -200,6 +228,32 @@ int moe_forward(const moe_desc *desc, const void *x, const float *router_w, cons
         }
     }
     return MOE_OK;
+}
+
+}  // namespace
+}  // namespace fgs
+
+extern "C" {
+
+int moe_forward(const moe_desc *desc, const void *x, const float *router_w, const float *router_bias,
+                const moe_weights *weights, void *out, void *workspace, size_t workspace_bytes,
+                const moe_aux *aux, void *stream) {
+    return run_layer(desc, x, router_w, router_bias, weights, out, workspace, workspace_bytes, aux, stream, nullptr);
+}
+
+size_t moe_block_workspace_size(const moe_desc *desc) {
+    if (check_desc(desc) != MOE_OK) return 0;
+    const size_t xbytes = (size_t)desc->n_tokens * desc->d_model * (desc->x_dtype == MOE_DTYPE_F32 ? 4 : 2);
+    return layout_for(desc).total + ((xbytes + 255) & ~size_t(255));
+}
+
+int moe_block_forward(const moe_desc *desc, void *resid, const float *norm_pre, const float *norm_post, float eps,
+                      const float *router_w, const float *router_bias, const moe_weights *weights, void *workspace,
+                      size_t workspace_bytes, const moe_aux *aux, void *stream) {
+    const BlockArgs blk{resid, norm_pre, norm_post, eps};
+    // x is only checked for presence and alignment; the layer reads the normalised copy
+    return run_layer(desc, resid, router_w, router_bias, weights, resid, workspace, workspace_bytes, aux, stream,
+                     &blk);
 }
 
 }  // extern "C"

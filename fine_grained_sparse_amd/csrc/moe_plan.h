@@ -39,6 +39,8 @@ struct Plan {
     int ldh;
     float *Y;            // [N*k + N][d] expert outputs: float32 (stream path) or bfloat16 (GEMM path)
     uint16_t *w3;        // [E][3d] bf16 split of the router weights (router GEMM only)
+    const float *norm_post;  // block variant: post-norm weights [d] (out = the residual row)
+    float eps;
     bool use_stream;     // decode-shaped expert path; otherwise the grouped GEMMs
     hipStream_t stream;
 };
@@ -53,6 +55,8 @@ hipError_t launch_combine(const Plan &p);
 hipError_t launch_gate_up_gemm(const Plan &p);
 hipError_t launch_down_gemm(const Plan &p);
 hipError_t launch_router_gemm(const Plan &p, uint16_t *w3);
+hipError_t launch_prenorm(const Plan &p, const void *resid, const float *g, float eps, void *xn);
+hipError_t launch_combine_block(const Plan &p);
 hipError_t gemm_kernels_init();  // once per process: raise the kernels' LDS limit
 
 // Decode-shaped expert kernels keep whole weight rows in registers.

@@ -159,6 +159,28 @@ int moe_forward(const moe_desc *desc, const void *x, const float *router_w,
                 void *workspace, size_t workspace_bytes, const moe_aux *aux,
                 void *stream);
 
+/* Workspace bytes moe_block_forward needs (0 on a bad description): the
+ * moe_forward workspace plus room for the normalised input. */
+size_t moe_block_workspace_size(const moe_desc *desc);
+
+/* The MoE sublayer of a sandwich-normalised block, updating the residual
+ * stream in place.  "Inside Kolibri 1" (flozi.net), section "The released
+ * stack": RMSNorm before and after the MoE, residual addition after it.
+ *   x     = RMSNorm(resid; norm_pre), rounded to x_dtype
+ *   y     = the layer of moe_forward applied to x (FP32, before rounding)
+ *   resid = round(resid + RMSNorm(y; norm_post))
+ * with RMSNorm(v; g)_i = v_i / sqrt(mean_j v_j^2 + eps) * g_i (statistics in
+ * FP32).  The post-norm and the residual add are fused into the combine.
+ *   resid      [N][d] x_dtype, read and written (16-byte aligned)
+ *   norm_pre   [d] FP32, norm_post [d] FP32 (16-byte aligned); eps >= 0
+ *   workspace  >= moe_block_workspace_size(desc) bytes, 256-byte aligned
+ * Other arguments and errors as moe_forward; MOE_FLAG_ACCUMULATE is rejected
+ * (the residual add is part of this call). */
+int moe_block_forward(const moe_desc *desc, void *resid, const float *norm_pre, const float *norm_post,
+                      float eps, const float *router_w, const float *router_bias,
+                      const moe_weights *weights, void *workspace, size_t workspace_bytes,
+                      const moe_aux *aux, void *stream);
+
 /* Static text for a status code. */
 const char *moe_status_string(int status);
 

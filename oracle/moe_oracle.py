@@ -55,7 +55,7 @@ __all__ = [
     "decode_bf16", "decode_e4m3fn", "dequant_weight", "router_logits",
     "select_topk", "mixture_weights", "dispatch", "swiglu_expert",
     "combine", "moe_forward", "token_outputs", "brute_force_topk",
-    "expert_param_counts", "round_to_bf16_bits",
+    "expert_param_counts", "round_to_bf16_bits", "rms_norm", "block_forward",
 ]
 
 
@@ -335,6 +335,38 @@ def token_outputs(inp: Dict[str, np.ndarray], tokens: Sequence[int], top_k: int,
             acc = acc + w[t, j] * swiglu_expert(xt, *cache[e])[0]
         outs.append(acc)
     return dict(logits=h32, ids=own_ids, gap=gap, w=w, out64=np.array(outs))
+
+
+# --------------------------------------------------------------------------
+# sandwich normalisation around the MoE sublayer
+# --------------------------------------------------------------------------
+
+def rms_norm(v64: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis: v / sqrt(mean(v^2) + eps) * g, float64."""
+    g64 = np.asarray(g, dtype=np.float32).astype(np.float64)
+    return v64 / np.sqrt(np.mean(v64 * v64, axis=-1, keepdims=True) + eps) * g64
+
+
+def block_forward(inp: Dict[str, np.ndarray], resid: np.ndarray, g_pre: np.ndarray, g_post: np.ndarray,
+                  eps: float, top_k: int, w_dtype: str, x_dtype: str,
+                  renormalize: bool = False) -> Dict[str, np.ndarray]:
+    """The MoE sublayer of a sandwich-normalised block, residual stream updated.
+
+    "Inside Kolibri 1" (flozi.net), section "The released stack": RMSNorm
+    before and after the MoE, residual addition after the sublayer:
+        x   = RMSNorm(r; g_pre), rounded to the activation type (the MoE input)
+        y   = MoE(x)
+        out = r + RMSNorm(y; g_post), rounded once to the activation type.
+    """
+    r64 = _x_to_f64(resid)
+    xn = rms_norm(r64, g_pre, eps)
+    xs = round_to_bf16_bits(xn) if x_dtype == "bf16" else xn.astype(np.float32)
+    res = moe_forward(dict(inp, x=xs), top_k, w_dtype, x_dtype, renormalize=renormalize)
+    z = rms_norm(res["out64"], g_post, eps)
+    out64 = r64 + z
+    out = round_to_bf16_bits(out64) if x_dtype == "bf16" else out64.astype(np.float32)
+    res.update(x_norm=xs, y64=res["out64"], out64=out64, out=out)
+    return res
 
 
 # --------------------------------------------------------------------------

@@ -336,6 +336,55 @@ def pin_renormalized_weights(o):
     assert np.allclose(res["out64"][0], want, rtol=1e-14, atol=1e-15)
 
 
+def pin_rms_norm(o):
+    """RMSNorm equals torch's rms_norm in float64; a constant row has a closed form."""
+    rng = np.random.default_rng(10)
+    v = rng.standard_normal((7, 48)) * 3.0
+    g = rng.standard_normal(48).astype(np.float32)
+    eps = 1e-6
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(v), (48,), torch.from_numpy(g.astype(np.float64)), eps)
+    assert np.allclose(o.rms_norm(v, g, eps), ref.numpy(), rtol=1e-13, atol=1e-15)
+    c = -2.5
+    got = o.rms_norm(np.full((1, 16), c), np.ones(16, np.float32) * 3.0, 0.25)
+    assert np.allclose(got, 3.0 * c / math.sqrt(c * c + 0.25), rtol=1e-15)
+
+
+def pin_block_worked_example(o):
+    """Sandwich-normalised block reduces to the hand-worked instance.
+
+    Residual r = [1, 2] and pre-norm weights sqrt(2.5) make the normalised
+    input exactly x = [1, 2] after rounding to bfloat16; with unit post-norm
+    weights and eps = 0 the block output is r + y / rms(y), y the worked
+    example's layer output.
+    """
+    with open(os.path.join(GOLDEN, "worked_example.json")) as fh:
+        g = json.load(fh)
+    inp = dict(router_w=np.array(g["router_w"], np.float32), router_b=np.array(g["router_b"], np.float32))
+    for key in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+        inp[key] = _bf16_bits(np.array(g[key], np.float32))
+    resid = _bf16_bits(np.array([[1.0, 2.0]], np.float32))
+    g_pre = np.full(2, math.sqrt(2.5), np.float32)
+    res = o.block_forward(inp, resid, g_pre, np.ones(2, np.float32), 0.0, 2, "bf16", "bf16")
+    assert res["x_norm"].tolist() == _bf16_bits(np.array([[1.0, 2.0]], np.float32)).tolist()
+    env = {"sig": _sig}
+    y = np.array([eval(expr, env) for expr in g["expected_out_closed_form"]])
+    want = np.array([1.0, 2.0]) + y / math.sqrt(float(np.mean(y * y)))
+    assert np.allclose(res["out64"][0], want, rtol=1e-14, atol=1e-15)
+
+
+def pin_block_scale_invariance(o):
+    """Scaling the residual by c > 0 leaves the MoE input unchanged (eps ~ 0)."""
+    cfg, inp = _small_layer(n=12, n_exp=8, k=2, x_dtype="f32", seed=4)
+    rng = np.random.default_rng(11)
+    r = rng.standard_normal((12, cfg.d_model)).astype(np.float32)
+    gp = (1 + 0.1 * rng.standard_normal(cfg.d_model)).astype(np.float32)
+    gq = (1 + 0.1 * rng.standard_normal(cfg.d_model)).astype(np.float32)
+    a = o.block_forward(inp, r, gp, gq, 1e-12, 2, "bf16", "f32")
+    b = o.block_forward(inp, (r * 4.0).astype(np.float32), gp, gq, 1e-12, 2, "bf16", "f32")
+    assert np.allclose(a["y64"], b["y64"], rtol=1e-6, atol=1e-9)
+    assert np.allclose(b["out64"] - 4.0 * r, a["out64"] - r, rtol=1e-6, atol=1e-9)
+
+
 def pin_page_arithmetic(o):
     """Expert parameter counts printed on the pages."""
     with open(os.path.join(GOLDEN, "page_arithmetic.json")) as fh:

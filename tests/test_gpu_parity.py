@@ -82,6 +82,18 @@ def test_128_experts(n):
     _run_full(get_config("decode", n_experts=128, n_tokens=n))
 
 
+@pytest.mark.parametrize("cfg_name,over,renorm", [
+    ("toy", {}, False), ("toy", dict(x_dtype="bf16", n_tokens=300), False), ("decode", {}, False),
+    ("decode", dict(n_tokens=100, w_dtype="fp8"), True),
+])
+def test_block_sandwich_norm(cfg_name, over, renorm):
+    """moe_block_forward: pre-RMSNorm, the layer, post-RMSNorm + residual fused in the combine."""
+    cfg = get_config(cfg_name, **over)
+    _say(f"case block {cfg.name} N={cfg.n_tokens} x={cfg.x_dtype} w={cfg.w_dtype} renorm={renorm}")
+    stats = PA.block_run_and_check(cfg, generate(cfg, seed=2), seed=2, renormalize=renorm)
+    _say(f"  -> {stats}")
+
+
 def test_deterministic():
     cfg = get_config("decode", n_tokens=32)
     dev = PA.to_device(generate(cfg, seed=5))

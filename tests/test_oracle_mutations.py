@@ -46,6 +46,10 @@ MUTATIONS = {
     "residual_dropped": ("out64 = out64 + _x_to_f64(residual)", "out64 = out64"),
     "renorm_no_max_shift_sign": ("z = np.exp(h - h.max(axis=1, keepdims=True))",
                                  "z = np.exp(h.max(axis=1, keepdims=True) - h)"),
+    "rms_no_sqrt": ("return v64 / np.sqrt(np.mean(v64 * v64, axis=-1, keepdims=True) + eps) * g64",
+                    "return v64 / (np.mean(v64 * v64, axis=-1, keepdims=True) + eps) * g64"),
+    "block_no_post_norm": ("    z = rms_norm(res[\"out64\"], g_post, eps)", "    z = res[\"out64\"]"),
+    "block_no_residual": ("    out64 = r64 + z", "    out64 = z"),
     "renorm_ignored": ("    w = mixture_weights(h32, ids, renormalize)\n    counts,",
                        "    w = mixture_weights(h32, ids)\n    counts,"),
 }
