@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "fp8", "zipf", "toy"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "fp8", "fp8block", "zipf", "toy"])
     ap.add_argument("--tokens", type=int, default=None, help="override the batch size")
     ap.add_argument("--layers", type=int, default=4, help="independent layer instances cycled by the steps")
     ap.add_argument("--variant", default="plain", choices=["plain", "renorm", "block"],
@@ -221,17 +221,20 @@ def main():
 
     sw = 1 if cfg.w_dtype == "fp8" else 2
     sx = 4 if cfg.x_dtype == "f32" else 2
-    sc = 4 if cfg.w_dtype == "fp8" else 0   # one FP32 scale per output channel
+    def sc_row(n_in):   # FP32 scale bytes per weight row of n_in inputs
+        if cfg.w_dtype != "fp8":
+            return 0
+        return 4 * n_in / (128 * 128) if cfg.scale_block else 4   # per 128x128 block, or per output channel
     stream_path = N <= 64 and d <= 4096 and f <= 512 and fs <= 512
     kind = "stream" if stream_path else "gemm"
 
     # algorithmic bytes and flops per launch of the two expert kernels, for U
     # touched routed experts (+ the shared expert)
     def gu_bytes(U):   # touched experts' gate+up rows (+ shared), x read once
-        return (U * 2 * f * (d * sw + sc) + 2 * fs * (d * sw + sc) + N * d * sx)
+        return (U * 2 * f * (d * sw + sc_row(d)) + 2 * fs * (d * sw + sc_row(d)) + N * d * sx)
 
     def dn_bytes(U):   # touched experts' down rows (+ shared)
-        return (U * d * (f * sw + sc) + d * (fs * sw + sc))
+        return (U * d * (f * sw + sc_row(f)) + d * (fs * sw + sc_row(fs)))
 
     gu_flops = 2.0 * (N * k * 2 * f + N * 2 * fs) * d
     dn_flops = 2.0 * (N * k * f + N * fs) * d
@@ -260,8 +263,9 @@ def main():
     r_dn = roof(f"down_{kind}", dn_b, dn_flops * args.steps, dn_t, len(dn_ms))
     dom = r_gu if gu_t >= dn_t else r_dn
 
-    layer_bytes = [N * d * sx + E * d * 4 + E * 4 + touched[li] * 3 * (d * f * sw) + touched[li] * (2 * f + d) * sc
-                   + 3 * d * fs * sw + (2 * fs + d) * sc + N * d * sx for li in range(L)]
+    layer_bytes = [N * d * sx + E * d * 4 + E * 4 + touched[li] * 3 * (d * f * sw)
+                   + touched[li] * (2 * f * sc_row(d) + d * sc_row(f))
+                   + 3 * d * fs * sw + 2 * fs * sc_row(d) + d * sc_row(fs) + N * d * sx for li in range(L)]
     layer_b = sum(layer_bytes[i % L] for i in range(args.steps))
     layer_flops = (2.0 * N * d * E + gu_flops + dn_flops) * args.steps
 
@@ -288,7 +292,9 @@ def main():
         "vs_baseline": None, "dtype": cfg.w_dtype if cfg.w_dtype == "bf16" else "fp8-weights/bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: N={N} d={d} E={E} top_k={k} f={f} f_shared={fs} "
-                               f"x={cfg.x_dtype} w={cfg.w_dtype} bias={cfg.bias_kind}",
+                               f"x={cfg.x_dtype} w={cfg.w_dtype}"
+                               + (f" scales={cfg.scale_block}x{cfg.scale_block}" if cfg.scale_block else "")
+                               + f" bias={cfg.bias_kind}",
                    "n_tokens": N, "layers_cycled": L, "touched_experts": touched, "expert_path": kind,
                    "variant": args.variant},
         "roofline": roofline,

@@ -20,6 +20,7 @@ MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1
 MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3 = 0, 1, 2
 MOE_FLAG_ACCUMULATE = 1
 MOE_FLAG_RENORMALIZE = 2
+MOE_FLAG_FP8_BLOCK128 = 4
 STAGES = ("router", "topk", "dispatch", "gate_up", "down", "combine")
 MOE_NUM_STAGES = len(STAGES)
 
@@ -132,6 +133,9 @@ class MoeLayer:
         self.fs = inputs["ws_gate"].shape[0]
         self.wdt = MOE_DTYPE_FP8_E4M3 if inputs["w_gate"].dtype == torch.uint8 else MOE_DTYPE_BF16
         self.xdt = _XDT[x_dtype]
+        # FP8 scales of shape [E, f/128, d/128] are 128 x 128 block scales
+        sg = inputs.get("s_gate")
+        self.base_flags = MOE_FLAG_FP8_BLOCK128 if sg is not None and sg.dim() == 3 else 0
         self.weights = weights_struct(inputs)
         ws = workspace_size(self.desc(n_tokens_max))
         if ws == 0:
@@ -140,7 +144,7 @@ class MoeLayer:
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
 
     def desc(self, n: int, flags: int = 0) -> MoeDesc:
-        return make_desc(n, self.d, self.E, self.top_k, self.f, self.fs, self.xdt, self.wdt, flags)
+        return make_desc(n, self.d, self.E, self.top_k, self.f, self.fs, self.xdt, self.wdt, flags | self.base_flags)
 
     def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, accumulate: bool = False,
                 aux: Optional[MoeAux] = None, router_w: Optional[torch.Tensor] = None,
@@ -159,7 +163,6 @@ class MoeLayer:
         if st != MOE_OK:
             raise MoeError(st, "moe_forward")
         return out
-
 
     def block_forward(self, resid: torch.Tensor, norm_pre: torch.Tensor, norm_post: torch.Tensor, eps: float,
                       aux: Optional[MoeAux] = None, renormalize: bool = False) -> torch.Tensor:

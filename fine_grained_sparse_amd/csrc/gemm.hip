@@ -5,8 +5,11 @@
 // MLP (two 2560 -> 512 projections forming SiLU(gate) x up, then 512 -> 2560)
 // and there is no per-expert capacity, so the rows per expert vary from zero
 // to most of the batch.  Section "The FP8 path is explicitly mixed precision":
-// FP8 E4M3 weights with FP32 scales; here the scale is per output channel, so
-// it factors out of the dot product and is applied exactly in the epilogue.
+// FP8 E4M3 weights with FP32 scales.  A per-output-channel scale factors out
+// of the dot product and is applied exactly in the epilogue.  With one scale
+// per 128 x 128 block the scale changes along K: every 128-wide K block (two
+// 64-wide stages) is accumulated on its own and added into the running sum
+// times its block's scale, one FP32 multiply-add per accumulator per block.
 //
 // Work list: the dispatch scan writes one tile per 128 rows of every
 // non-empty group (shared expert first).  The grid is (column blocks, tiles)
@@ -152,11 +155,14 @@ struct Stage {
 // The product covers GEMM columns [k_base, k_base + K).  `a_kmod`: the A
 // column read for GEMM column k is k mod a_kmod (the router repeats x three
 // times along K); pass a value above every k for a plain product.
-template <bool FP8, bool XF32, int WN = kWN>
+// BLK: block-scaled weights (k_base = 0, K a multiple of 128); K block kb of
+// column fragments ni < 2 is scaled by sc_lo[kb], of ni >= 2 by sc_hi[kb].
+template <bool FP8, bool XF32, int WN = kWN, bool BLK = false>
 __device__ __forceinline__ void tile_mma(const void *a_base, const size_t (&a_off)[Geo<WN>::kAPer],
                                          const bool (&a_ok)[Geo<WN>::kAPer], const void *const (&b_base)[Geo<WN>::kBPer],
                                          const size_t (&b_off)[Geo<WN>::kBPer], int k_base, int K, int a_kmod,
-                                         int m, uint16_t *lds, f32x4_t (&acc)[4][4]) {
+                                         int m, uint16_t *lds, f32x4_t (&acc)[4][4],
+                                         const float *sc_lo = nullptr, const float *sc_hi = nullptr) {
     using G = Geo<WN>;
     constexpr int kRowStep = G::kThreads / 8;  // tile rows covered by one pass of the loader
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -186,6 +192,26 @@ __device__ __forceinline__ void tile_mma(const void *a_base, const size_t (&a_of
         for (int j = 0; j < G::kBPer; ++j)
             *reinterpret_cast<uint4 *>(Bs[buf] + (r0 + kRowStep * j) * kLdsStride + chunk) = w8_to_bf16<FP8>(st.b[j]);
     };
+    // BLK: the current K block's products, folded into acc after its second stage
+    f32x4_t accb[4][4];
+    if (BLK) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) accb[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    f32x4_t (&dst)[4][4] = BLK ? accb : acc;
+    auto fold = [&](float slo, float shi) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[mi][ni][q] = fmaf(accb[mi][ni][q], ni < 2 ? slo : shi, acc[mi][ni][q]);
+                    accb[mi][ni][q] = 0.f;
+                }
+    };
     auto compute = [&](int buf) {
 #pragma unroll
         for (int kk = 0; kk < kBK; kk += 32) {
@@ -201,7 +227,7 @@ __device__ __forceinline__ void tile_mma(const void *a_base, const size_t (&a_of
                     // transposed, so a lane holds 4 consecutive output columns
                     // of one row (lane % 16 = row, 4 * (lane / 16) + q = column)
 #pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_bf16(bf[ni], af[mi], acc[mi][ni]);
+                    for (int ni = 0; ni < 4; ++ni) dst[mi][ni] = mfma_bf16(bf[ni], af[mi], dst[mi][ni]);
                 }
             }
         }
@@ -218,8 +244,11 @@ __device__ __forceinline__ void tile_mma(const void *a_base, const size_t (&a_of
     // body lets the compiler's load counters see that only the other slot's
     // loads are outstanding; sched_barrier(0) pins the phase order so the
     // loads are issued first and stay in flight through two multiply phases.
+    // With BLK each trip is exactly one 128-wide K block (kt is even).
     int kt = 0;
     for (; kt + 3 < nk; kt += 2) {
+        float slo = 0.f, shi = 0.f;
+        if (BLK) { slo = sc_lo[kt >> 1]; shi = sc_hi[kt >> 1]; }
         fetch(s0, (kt + 2) * kBK);
         __builtin_amdgcn_sched_barrier(0);
         compute(0);
@@ -229,11 +258,13 @@ __device__ __forceinline__ void tile_mma(const void *a_base, const size_t (&a_of
         fetch(s1, (kt + 3) * kBK);
         __builtin_amdgcn_sched_barrier(0);
         compute(1);
+        if (BLK) fold(slo, shi);
         __builtin_amdgcn_sched_barrier(0);
         stash(s0, 0);
         lds_barrier();
     }
-    // tail: 1, 2 or 3 stages left (stage kt in LDS buffer 0, stage kt+1 in s1)
+    // tail: 1, 2 or 3 stages left (stage kt in LDS buffer 0, stage kt+1 in s1);
+    // with BLK always 2 (K is a multiple of 128)
     const int left = nk - kt;
     if (left == 3) fetch(s0, (kt + 2) * kBK);
     compute(0);
@@ -247,16 +278,21 @@ __device__ __forceinline__ void tile_mma(const void *a_base, const size_t (&a_of
             compute(0);
         }
     }
+    if (BLK) fold(sc_lo[kt >> 1], sc_hi[kt >> 1]);
 }
 
+// weight modes: bfloat16, FP8 with per-channel scales, FP8 with 128x128 block scales
+enum { kWBf16 = 0, kWFp8Row = 1, kWFp8Blk = 2 };
+
 // grid: (ceil(max(f, fs) / 128), tile capacity); block 512; LDS kGemmLds
-template <bool FP8, bool XF32>
+template <int WM, bool XF32>
 __global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
     const void *__restrict__ x, const void *__restrict__ wg, const void *__restrict__ wu,
     const float *__restrict__ sg, const float *__restrict__ su, const void *__restrict__ wsg,
     const void *__restrict__ wsu, const float *__restrict__ ssg, const float *__restrict__ ssu,
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ por, uint16_t *__restrict__ H, int ldh, int d, int E, int k, int f, int fs) {
+    constexpr bool FP8 = WM != kWBf16, BLK = WM == kWFp8Blk;
     extern __shared__ uint16_t lds[];
     const int u = blockIdx.y;
     if (u >= *n_tiles) return;
@@ -296,7 +332,14 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    tile_mma<FP8, XF32>(x, a_off, a_ok, b_base, b_off, 0, d, d, m, lds, acc);
+    // block scales: the tile's 128 gate (and up) rows are output block c0/128
+    const float *sc_lo = nullptr, *sc_hi = nullptr;
+    if (BLK) {
+        const size_t sb = ((shared ? 0 : (size_t)g * (f / 128)) + c0 / 128) * (size_t)(d / 128);
+        sc_lo = (shared ? ssg : sg) + sb;
+        sc_hi = (shared ? ssu : su) + sb;
+    }
+    tile_mma<FP8, XF32, kWN, BLK>(x, a_off, a_ok, b_base, b_off, 0, d, d, m, lds, acc, sc_lo, sc_hi);
 
     // epilogue: acc[mi][ni][q] is row wm*64 + mi*16 + lane%16, GEMM column
     // (B row) b_row_of(wn, ni) + 4*(lane/16) + q; gate tile ni and up tile
@@ -307,7 +350,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
         const int col = c0 + wn * 32 + ni * 16 + (lane >> 4) * 4;
         if (col >= fg) continue;  // f_g is a multiple of 64: all four in range or all out
         float gs[4] = {1.f, 1.f, 1.f, 1.f}, us[4] = {1.f, 1.f, 1.f, 1.f};
-        if (FP8) {
+        if (WM == kWFp8Row) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 gs[q] = shared ? ssg[col + q] : sg[wrow0 + col + q];
@@ -329,12 +372,13 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
 }
 
 // grid: (ceil(d / 256), tile capacity); block 512; LDS kGemmLds
-template <bool FP8>
+template <int WM>
 __global__ __launch_bounds__(kThreads) void down_gemm_kernel(
     const uint16_t *__restrict__ H, int ldh, const void *__restrict__ wd, const float *__restrict__ sd,
     const void *__restrict__ wsd, const float *__restrict__ ssd, const int32_t *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets, uint16_t *__restrict__ Y, int d, int E,
     int f, int fs) {
+    constexpr bool FP8 = WM != kWBf16, BLK = WM == kWFp8Blk;
     extern __shared__ uint16_t lds[];
     const int u = blockIdx.y;
     if (u >= *n_tiles) return;
@@ -368,7 +412,16 @@ __global__ __launch_bounds__(kThreads) void down_gemm_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    tile_mma<FP8, false>(H, a_off, a_ok, b_base, b_off, 0, fg, fg, m, lds, acc);
+    // block scales: B rows [0, 128) are output block o0/128, rows [128, 256)
+    // the next one (clamped at the end of d: those rows are never stored)
+    const float *sc_lo = nullptr, *sc_hi = nullptr;
+    if (BLK) {
+        const int nkb = fg / 128, nob = d / 128, ob = o0 / 128;
+        const float *sp = shared ? ssd : sd + (size_t)g * nob * nkb;
+        sc_lo = sp + (size_t)ob * nkb;
+        sc_hi = sp + (size_t)(ob + 1 < nob ? ob + 1 : ob) * nkb;
+    }
+    tile_mma<FP8, false, kWN, BLK>(H, a_off, a_ok, b_base, b_off, 0, fg, fg, m, lds, acc, sc_lo, sc_hi);
 
     const int lane = tid & 63, wave = tid >> 6, wm = wave >> 2, wn = wave & 3;
 #pragma unroll
@@ -377,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void down_gemm_kernel(
         const int o = o0 + b_row_of(wn, ni) + (lane >> 4) * 4;
         if (o >= d) continue;  // d is a multiple of 64: o..o+3 all in range or all out
         float sc[4] = {1.f, 1.f, 1.f, 1.f};
-        if (FP8) {
+        if (WM == kWFp8Row) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) sc[q] = shared ? ssd[o + q] : sd[obase + o + q];
         }
@@ -492,27 +545,31 @@ static hipError_t allow_lds(K kernel) {
 
 hipError_t gemm_kernels_init() {
     hipError_t e;
-    if ((e = allow_lds(gate_up_gemm_kernel<true, false>)) != hipSuccess) return e;
-    if ((e = allow_lds(gate_up_gemm_kernel<false, false>)) != hipSuccess) return e;
-    if ((e = allow_lds(gate_up_gemm_kernel<true, true>)) != hipSuccess) return e;
-    if ((e = allow_lds(gate_up_gemm_kernel<false, true>)) != hipSuccess) return e;
-    if ((e = allow_lds(down_gemm_kernel<true>)) != hipSuccess) return e;
+    if ((e = allow_lds(gate_up_gemm_kernel<kWBf16, false>)) != hipSuccess) return e;
+    if ((e = allow_lds(gate_up_gemm_kernel<kWBf16, true>)) != hipSuccess) return e;
+    if ((e = allow_lds(gate_up_gemm_kernel<kWFp8Row, false>)) != hipSuccess) return e;
+    if ((e = allow_lds(gate_up_gemm_kernel<kWFp8Row, true>)) != hipSuccess) return e;
+    if ((e = allow_lds(gate_up_gemm_kernel<kWFp8Blk, false>)) != hipSuccess) return e;
+    if ((e = allow_lds(gate_up_gemm_kernel<kWFp8Blk, true>)) != hipSuccess) return e;
+    if ((e = allow_lds(down_gemm_kernel<kWFp8Row>)) != hipSuccess) return e;
+    if ((e = allow_lds(down_gemm_kernel<kWFp8Blk>)) != hipSuccess) return e;
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(router_gemm_kernel),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)Geo<2>::kLds)) != hipSuccess)
         return e;
-    return allow_lds(down_gemm_kernel<false>);
+    return allow_lds(down_gemm_kernel<kWBf16>);
 }
 
 hipError_t launch_gate_up_gemm(const Plan &p) {
     const int fmax = p.f > p.fs ? p.f : p.fs;
     dim3 grid((fmax + kBN / 2 - 1) / (kBN / 2), p.max_tiles), block(kThreads);
-#define FGS_GUG(F8, XF)                                                                                         \
-    hipLaunchKernelGGL((gate_up_gemm_kernel<F8, XF>), grid, block, kGemmLds, p.stream, p.x, p.W.w_gate, p.W.w_up, \
+#define FGS_GUG(WM, XF)                                                                                         \
+    hipLaunchKernelGGL((gate_up_gemm_kernel<WM, XF>), grid, block, kGemmLds, p.stream, p.x, p.W.w_gate, p.W.w_up, \
                        p.W.s_gate, p.W.s_up, p.W.ws_gate, p.W.ws_up, p.W.ss_gate, p.W.ss_up, p.tiles, p.n_tiles,  \
                        p.offsets, p.por, p.H, p.ldh, p.d, p.E, p.k, p.f, p.fs)
-    const bool fp8 = p.wdt == MOE_DTYPE_FP8_E4M3, xf32 = p.xdt == MOE_DTYPE_F32;
-    if (fp8) { if (xf32) FGS_GUG(true, true); else FGS_GUG(true, false); }
-    else { if (xf32) FGS_GUG(false, true); else FGS_GUG(false, false); }
+    const bool xf32 = p.xdt == MOE_DTYPE_F32;
+    if (p.wdt != MOE_DTYPE_FP8_E4M3) { if (xf32) FGS_GUG(kWBf16, true); else FGS_GUG(kWBf16, false); }
+    else if (p.flags & MOE_FLAG_FP8_BLOCK128) { if (xf32) FGS_GUG(kWFp8Blk, true); else FGS_GUG(kWFp8Blk, false); }
+    else { if (xf32) FGS_GUG(kWFp8Row, true); else FGS_GUG(kWFp8Row, false); }
 #undef FGS_GUG
     return hipGetLastError();
 }
@@ -520,14 +577,13 @@ hipError_t launch_gate_up_gemm(const Plan &p) {
 hipError_t launch_down_gemm(const Plan &p) {
     dim3 grid((p.d + kBN - 1) / kBN, p.max_tiles), block(kThreads);
     uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y);
-    if (p.wdt == MOE_DTYPE_FP8_E4M3)
-        hipLaunchKernelGGL((down_gemm_kernel<true>), grid, block, kGemmLds, p.stream, p.H, p.ldh, p.W.w_down,
-                           p.W.s_down, p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, Y, p.d, p.E, p.f,
-                           p.fs);
-    else
-        hipLaunchKernelGGL((down_gemm_kernel<false>), grid, block, kGemmLds, p.stream, p.H, p.ldh, p.W.w_down,
-                           p.W.s_down, p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, Y, p.d, p.E, p.f,
-                           p.fs);
+#define FGS_DNG(WM)                                                                                       \
+    hipLaunchKernelGGL((down_gemm_kernel<WM>), grid, block, kGemmLds, p.stream, p.H, p.ldh, p.W.w_down, p.W.s_down, \
+                       p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs)
+    if (p.wdt != MOE_DTYPE_FP8_E4M3) FGS_DNG(kWBf16);
+    else if (p.flags & MOE_FLAG_FP8_BLOCK128) FGS_DNG(kWFp8Blk);
+    else FGS_DNG(kWFp8Row);
+#undef FGS_DNG
     return hipGetLastError();
 }
 

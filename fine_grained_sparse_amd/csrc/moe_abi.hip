@@ -39,9 +39,12 @@ int check_desc(const moe_desc *d) {
         d->d_ff_shared % 64)
         return MOE_ERR_ARG;
     if ((long)d->n_tokens * d->top_k + d->n_tokens >= (1L << 31)) return MOE_ERR_ARG;
-    if (d->flags & ~(MOE_FLAG_ACCUMULATE | MOE_FLAG_RENORMALIZE)) return MOE_ERR_ARG;
+    if (d->flags & ~(MOE_FLAG_ACCUMULATE | MOE_FLAG_RENORMALIZE | MOE_FLAG_FP8_BLOCK128)) return MOE_ERR_ARG;
     if (d->x_dtype != MOE_DTYPE_F32 && d->x_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
     if (d->w_dtype != MOE_DTYPE_BF16 && d->w_dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+    if ((d->flags & MOE_FLAG_FP8_BLOCK128) &&
+        (d->w_dtype != MOE_DTYPE_FP8_E4M3 || d->d_model % 128 || d->d_ff % 128 || d->d_ff_shared % 128))
+        return MOE_ERR_ARG;
     return MOE_OK;
 }
 

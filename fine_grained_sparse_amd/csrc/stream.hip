@@ -18,6 +18,13 @@
 //
 // Work list: one tile per non-empty group (routed experts, and the shared
 // expert as group E with all N tokens), written by the dispatch scan.
+//
+// FP8 weights are decoded to bf16 once, after their loads land (the E4M3 ->
+// bf16 conversion is exact), so the per-token dot products are the same for
+// both weight types.  Scales ("Inside Kolibri 1", section "The FP8 path is
+// explicitly mixed precision"): a per-output-channel scale is applied to the
+// finished dot product; with 128 x 128 block scales every 8-element partial
+// product is scaled by its own block's scale before the cross-lane sum.
 #include "moe_common.h"
 #include "moe_plan.h"
 
@@ -32,11 +39,23 @@ __device__ __forceinline__ typename WChunk<FP8>::T load_chunk(const void *base, 
     if constexpr (FP8) return ld_stream8((const uint8_t *)base + elem_off);
     else return ld_stream16((const uint16_t *)base + elem_off);
 }
-template <bool FP8>
-__device__ __forceinline__ float dot8(const typename WChunk<FP8>::T &w, const uint4 &x, float c) {
-    if constexpr (FP8) return dot8_e4m3_bf16(w, x, c);
-    else return dot8_bf16(w, x, c);
+// 8 weights as bfloat16: the E4M3 -> bf16 conversion is exact
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1)
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
+template <bool FP8>
+__device__ __forceinline__ uint4 chunk_bf16(const typename WChunk<FP8>::T &w) {
+    if constexpr (FP8)
+        return make_uint4(e4m3x2_bf16x2<false>(w.x), e4m3x2_bf16x2<true>(w.x), e4m3x2_bf16x2<false>(w.y),
+                          e4m3x2_bf16x2<true>(w.y));
+    else
+        return w;
+}
+
+// weight modes: bfloat16, FP8 with per-channel scales, FP8 with 128x128 block scales
+enum { kWBf16 = 0, kWFp8Row = 1, kWFp8Blk = 2 };
 
 // 8 activations -> bfloat16 x 8 (FP32 x is rounded to nearest even)
 __device__ __forceinline__ uint4 load_x8(const void *x, int xdt, size_t elem_off) {
@@ -63,7 +82,7 @@ __device__ __forceinline__ void load_x_row(uint4 (&xv)[CPL], const void *x, int 
 // experts' matrices completely (page and DRAM-row locality).  No LDS and no
 // barrier: each lane reads its slice of a token row straight from L2, with
 // the next token's row in flight while the current one is reduced.
-template <int CPL, bool FP8>
+template <int CPL, int WM>
 __global__ __launch_bounds__(256) void gate_up_stream_kernel(
     const void *__restrict__ x, int xdt, const void *__restrict__ wg, const void *__restrict__ wu,
     const float *__restrict__ sg, const float *__restrict__ su, const void *__restrict__ wsg,
@@ -71,6 +90,7 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ por, uint16_t *__restrict__ H, int ldh, int d, int E, int k, int f, int fs,
     int bm) {
+    constexpr bool FP8 = WM != kWBf16, BLK = WM == kWFp8Blk;
     const int u = blockIdx.y;
     if (u >= *n_tiles) return;
     const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
@@ -88,7 +108,7 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
     // lanes past the row end read chunk 0 again (finite weights) and are
     // multiplied by a zero activation chunk; no select on loaded values, so
     // nothing waits for these loads before the token rows are requested
-    typename WChunk<FP8>::T w[4][CPL];
+    typename WChunk<FP8>::T wr[4][CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int ch = lane + 64 * i;
@@ -96,7 +116,22 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const void *b = r < 2 ? gbase : ubase;
-            w[r][i] = load_chunk<FP8>(b, (rbase + c0 + (r & 1)) * (size_t)d + (size_t)chc * 8);
+            wr[r][i] = load_chunk<FP8>(b, (rbase + c0 + (r & 1)) * (size_t)d + (size_t)chc * 8);
+        }
+    }
+    // block scales: chunk ch covers input columns [8ch, 8ch+8), in K block ch/16;
+    // rows c0 and c0+1 share one output block
+    float bsc[2][CPL];
+    if (BLK) {
+        const int nkb = d / 128;
+        const size_t sb = ((shared ? 0 : (size_t)g * (f / 128)) + c0 / 128) * nkb;
+        const float *gs = (shared ? ssg : sg) + sb, *us = (shared ? ssu : su) + sb;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int ch = lane + 64 * i;
+            const int kb = (ch < nch ? ch : 0) >> 4;
+            bsc[0][i] = gs[kb];
+            bsc[1][i] = us[kb];
         }
     }
 
@@ -108,7 +143,7 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
 
     float gsc = 1.f, usc = 1.f;
     const int r_out = (lane >> 4) & 1;  // after the reduction lanes 0 and 16 own gate columns c0, c0+1
-    if (FP8) {
+    if (WM == kWFp8Row) {
         const float *gs = shared ? ssg : sg + (size_t)g * f;
         const float *us = shared ? ssu : su + (size_t)g * f;
         gsc = gs[c0 + r_out];
@@ -117,13 +152,21 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
 
     uint4 xa[CPL], xb[CPL];
     load_x_row<CPL>(xa, x, xdt, __shfl(tok, 0, kWave), d, lane, nch);
+    uint4 w[4][CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r][i] = chunk_bf16<FP8>(wr[r][i]);
     for (int t = 0; t < m; ++t) {
         if (t + 1 < m) load_x_row<CPL>(xb, x, xdt, __shfl(tok, t + 1, kWave), d, lane, nch);
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < CPL; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = dot8<FP8>(w[r][i], xa[i], acc[r]);
+            for (int r = 0; r < 4; ++r) {
+                if (BLK) acc[r] = fmaf(dot8_bf16(w[r][i], xa[i], 0.f), bsc[r >> 1][i], acc[r]);
+                else acc[r] = dot8_bf16(w[r][i], xa[i], acc[r]);
+            }
         butterfly_reduce<4>(acc);
         // value index = 2*bit5 + bit4 of the lane: gate rows 0,1 then up rows 2,3
         const float upv = __shfl_xor(acc[0], 32, kWave);
@@ -140,12 +183,13 @@ constexpr int kDnRW = 8;   // output rows per wave
 constexpr int kDnRB = 4 * kDnRW;  // output rows per workgroup
 
 // grid: (d / kDnRB, tile list capacity); block 256.  Needs f, fs <= 512.
-template <bool FP8>
+template <int WM>
 __global__ __launch_bounds__(256) void down_stream_kernel(
     const uint16_t *__restrict__ H, int ldh, const void *__restrict__ wd, const float *__restrict__ sd,
     const void *__restrict__ wsd, const float *__restrict__ ssd, const int32_t *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets, float *__restrict__ Y, int d, int E,
     int f, int fs, int bm) {
+    constexpr bool FP8 = WM != kWBf16, BLK = WM == kWFp8Blk;
     const int u = blockIdx.y;
     if (u >= *n_tiles) return;
     const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
@@ -158,23 +202,37 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
     const void *base = shared ? wsd : wd;
     const size_t obase = shared ? 0 : (size_t)g * d;
     const bool ok = lane < nch;  // masked lanes: chunk 0 again, times a zero H chunk
-    typename WChunk<FP8>::T w[kDnRW];
+    typename WChunk<FP8>::T wr[kDnRW];
 #pragma unroll
     for (int r = 0; r < kDnRW; ++r)
-        w[r] = load_chunk<FP8>(base, (obase + o0 + r) * (size_t)fg + (size_t)(ok ? lane : 0) * 8);
+        wr[r] = load_chunk<FP8>(base, (obase + o0 + r) * (size_t)fg + (size_t)(ok ? lane : 0) * 8);
     const int myrow = butterfly_index<kDnRW>(lane);
     float scl = 1.f;
-    if (FP8) scl = shared ? ssd[o0 + myrow] : sd[obase + o0 + myrow];
+    if (WM == kWFp8Row) scl = shared ? ssd[o0 + myrow] : sd[obase + o0 + myrow];
+    // block scales: the wave's 8 rows lie in output block o0/128; lane's chunk
+    // covers inputs [8 lane, 8 lane + 8), in K block lane/16
+    float lsc = 1.f;
+    if (BLK) {
+        const int nkb = fg / 128;
+        const float *sp = shared ? ssd : sd + (size_t)g * (d / 128) * nkb;
+        lsc = sp[(size_t)(o0 / 128) * nkb + ((ok ? lane : 0) >> 4)];
+    }
 
     const int row0 = offsets[g] + m0, m = min(bm, offsets[g + 1] - row0);
     const uint16_t *hp = H + (size_t)row0 * ldh + (size_t)(ok ? lane : 0) * 8;
     uint4 ha = ok ? *reinterpret_cast<const uint4 *>(hp) : make_uint4(0, 0, 0, 0);
+    uint4 w[kDnRW];
+#pragma unroll
+    for (int r = 0; r < kDnRW; ++r) w[r] = chunk_bf16<FP8>(wr[r]);
     for (int t = 0; t < m; ++t) {
         uint4 hb = make_uint4(0, 0, 0, 0);
         if (t + 1 < m && ok) hb = *reinterpret_cast<const uint4 *>(hp + (size_t)(t + 1) * ldh);
         float p[kDnRW];
 #pragma unroll
-        for (int r = 0; r < kDnRW; ++r) p[r] = dot8<FP8>(w[r], ha, 0.f);
+        for (int r = 0; r < kDnRW; ++r) {
+            p[r] = dot8_bf16(w[r], ha, 0.f);
+            if (BLK) p[r] *= lsc;
+        }
         butterfly_reduce<kDnRW>(p);
         if ((lane & (64 / kDnRW - 1)) == 0) Y[(size_t)(row0 + t) * d + o0 + myrow] = p[0] * scl;
         ha = hb;
@@ -186,12 +244,17 @@ hipError_t launch_gate_up(const Plan &p) {
     dim3 grid((fmax + kGuRB - 1) / kGuRB, p.max_tiles), block(256);
     const size_t lds = 0;
     const int cpl = (p.d / 8 + 63) / 64;
-    const bool fp8 = p.wdt == MOE_DTYPE_FP8_E4M3;
-#define FGS_GU(C, F8)                                                                                          \
-    hipLaunchKernelGGL((gate_up_stream_kernel<C, F8>), grid, block, lds, p.stream, p.x, p.xdt, p.W.w_gate,    \
+    const int wm = p.wdt != MOE_DTYPE_FP8_E4M3 ? kWBf16 : (p.flags & MOE_FLAG_FP8_BLOCK128) ? kWFp8Blk : kWFp8Row;
+#define FGS_GU(C, WM)                                                                                          \
+    hipLaunchKernelGGL((gate_up_stream_kernel<C, WM>), grid, block, lds, p.stream, p.x, p.xdt, p.W.w_gate,    \
                        p.W.w_up, p.W.s_gate, p.W.s_up, p.W.ws_gate, p.W.ws_up, p.W.ss_gate, p.W.ss_up, p.tiles, \
                        p.n_tiles, p.offsets, p.por, p.H, p.ldh, p.d, p.E, p.k, p.f, p.fs, p.bm)
-#define FGS_GU_C(C) do { if (fp8) FGS_GU(C, true); else FGS_GU(C, false); } while (0)
+#define FGS_GU_C(C)                                        \
+    do {                                                   \
+        if (wm == kWFp8Blk) FGS_GU(C, kWFp8Blk);           \
+        else if (wm == kWFp8Row) FGS_GU(C, kWFp8Row);      \
+        else FGS_GU(C, kWBf16);                            \
+    } while (0)
     switch (cpl) {
         case 1: FGS_GU_C(1); break;
         case 2: FGS_GU_C(2); break;
@@ -210,12 +273,13 @@ hipError_t launch_gate_up(const Plan &p) {
 
 hipError_t launch_down(const Plan &p) {
     dim3 grid(p.d / kDnRB, p.max_tiles), block(256);
-    if (p.wdt == MOE_DTYPE_FP8_E4M3)
-        hipLaunchKernelGGL((down_stream_kernel<true>), grid, block, 0, p.stream, p.H, p.ldh, p.W.w_down, p.W.s_down,
-                           p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, p.Y, p.d, p.E, p.f, p.fs, p.bm);
-    else
-        hipLaunchKernelGGL((down_stream_kernel<false>), grid, block, 0, p.stream, p.H, p.ldh, p.W.w_down, p.W.s_down,
-                           p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, p.Y, p.d, p.E, p.f, p.fs, p.bm);
+#define FGS_DN(WM)                                                                                           \
+    hipLaunchKernelGGL((down_stream_kernel<WM>), grid, block, 0, p.stream, p.H, p.ldh, p.W.w_down, p.W.s_down, \
+                       p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, p.Y, p.d, p.E, p.f, p.fs, p.bm)
+    if (p.wdt != MOE_DTYPE_FP8_E4M3) FGS_DN(kWBf16);
+    else if (p.flags & MOE_FLAG_FP8_BLOCK128) FGS_DN(kWFp8Blk);
+    else FGS_DN(kWFp8Row);
+#undef FGS_DN
     return hipGetLastError();
 }
 

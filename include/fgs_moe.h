@@ -32,7 +32,8 @@
  *     stored in ascending id order (slot j = j-th smallest id);
  *   - the shared expert has coefficient 1;
  *   - FP8 is OCP E4M3FN (bias 7, max 448, no infinities); a weight is
- *     code * scale with one FP32 scale per output channel (row);
+ *     code * scale with one FP32 scale per output channel (row), or per
+ *     128 x 128 block with MOE_FLAG_FP8_BLOCK128;
  *   - the expert matmuls take bfloat16 activations (an FP32 x is rounded to
  *     bfloat16 for the experts; the router always uses x as given);
  *   - dispatch is a stable counting sort of pairs by (expert, token).
@@ -77,6 +78,13 @@ extern "C" {
                                            Formulation"; default off (sigmoid, not
                                            renormalised) */
 
+#define MOE_FLAG_FP8_BLOCK128 (1u << 2) /* FP8 weights carry one FP32 scale per 128 x 128 block
+                                           instead of one per output channel: the released
+                                           checkpoint's layout, "Inside Kolibri 1" (flozi.net),
+                                           section "The FP8 path is explicitly mixed precision".
+                                           Requires w_dtype FP8_E4M3 and d_model, d_ff,
+                                           d_ff_shared multiples of 128 (else MOE_ERR_ARG). */
+
 /* pipeline stages, for optional timing events */
 #define MOE_STAGE_ROUTER    0   /* router logits */
 #define MOE_STAGE_TOPK      1   /* bias-corrected top-k, sigmoid weights */
@@ -105,8 +113,12 @@ typedef struct moe_desc {
 } moe_desc;
 
 /* Expert weights, row-major [out][in], element type desc->w_dtype.
- * Scales (FP32, one per output channel) are required for FP8 and must be
- * NULL for bfloat16.  All weight pointers 16-byte aligned. */
+ * Scales (FP32) are required for FP8 and must be NULL for bfloat16.  By
+ * default there is one scale per output channel (the shapes below); with
+ * MOE_FLAG_FP8_BLOCK128 one per 128 x 128 block, row-major over blocks:
+ * s_gate, s_up [E][f/128][d/128], s_down [E][d/128][f/128], ss_gate, ss_up
+ * [f_s/128][d/128], ss_down [d/128][f_s/128]; weight (o, i) then uses scale
+ * (o/128, i/128).  All weight pointers 16-byte aligned. */
 typedef struct moe_weights {
     const void  *w_gate;   /* [E][f][d] */
     const void  *w_up;     /* [E][f][d] */

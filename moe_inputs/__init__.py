@@ -17,6 +17,7 @@ Storage conventions (identical for both sides):
   router_w   [E, d]        float32, values rounded to bfloat16-representable
   router_b   [E]           float32
   w_gate     [E, f, d]     bfloat16, or uint8 E4M3 codes + s_gate [E, f] float32
+                           (or [E, f/128, d/128] with 128x128 block scales)
   w_up       [E, f, d]     as w_gate
   w_down     [E, d, f]     bfloat16, or uint8 codes + s_down [E, d] float32
   ws_gate    [f_s, d]      shared expert, same dtype rules (scales [f_s])
@@ -57,6 +58,7 @@ class LayerConfig:
     x_std: float = 1.0
     w_std: float = 0.02
     router_std: float = 0.02
+    scale_block: int = 0  # FP8 scales: 0 = one per output channel, 128 = one per 128x128 block
 
     def replace(self, **kw) -> "LayerConfig":
         return dataclasses.replace(self, **kw)
@@ -78,6 +80,10 @@ CONFIGS: Dict[str, LayerConfig] = {
     # FP8 E4M3 expert weights with one FP32 scale per output channel
     "fp8": LayerConfig("fp8", n_tokens=4096, x_dtype="bf16", w_dtype="fp8",
                        bias_kind="normal", bias_std=0.1, **_FULL),
+    # FP8 E4M3 weights with one FP32 scale per 128x128 block (the released
+    # checkpoint's granularity)
+    "fp8block": LayerConfig("fp8block", n_tokens=4096, x_dtype="bf16", w_dtype="fp8", scale_block=128,
+                            bias_kind="normal", bias_std=0.1, **_FULL),
     # FP8 weights, router bias = log of a Zipf(1.1) popularity over experts
     "zipf": LayerConfig("zipf", n_tokens=16384, x_dtype="bf16", w_dtype="fp8",
                         bias_kind="zipf", zipf_s=1.1, **_FULL),
@@ -129,6 +135,26 @@ def _fp8_per_channel(w: torch.Tensor):
     return q.view(torch.uint8), scale
 
 
+def _fp8_block(w: torch.Tensor, b: int):
+    """Encode float32 [..., out, in] as E4M3 codes + one FP32 scale per b x b block.
+
+    scale = amax(|block|) / 448, codes = round-to-nearest-even(w / scale); the
+    scale tensor has shape [..., out/b, in/b].  Input recipe only.
+    """
+    *lead, o, i = w.shape
+    wb = w.reshape(*lead, o // b, b, i // b, b)
+    amax = wb.abs().amax(dim=(-3, -1))
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).to(torch.float32)
+    q = (wb / scale.unsqueeze(-1).unsqueeze(-3)).to(torch.float8_e4m3fn)
+    return q.reshape(*lead, o, i).view(torch.uint8), scale
+
+
+def _encode(w: torch.Tensor, cfg: "LayerConfig"):
+    if cfg.w_dtype == "fp8":
+        return _fp8_block(w, cfg.scale_block) if cfg.scale_block else _fp8_per_channel(w)
+    return w.to(torch.bfloat16), None
+
+
 def _weight(shape, cfg: LayerConfig, seed: int, device: str, chunk_first_dim: bool):
     """bf16 tensor, or (uint8 codes, fp32 scales) for FP8.
 
@@ -143,19 +169,13 @@ def _weight(shape, cfg: LayerConfig, seed: int, device: str, chunk_first_dim: bo
         for _ in range(shape[0]):
             w = torch.randn(shape[1:], generator=g, dtype=torch.float32, device=device)
             w.mul_(cfg.w_std)
-            if cfg.w_dtype == "fp8":
-                q, s = _fp8_per_channel(w)
-                outs.append(q)
+            q, s = _encode(w, cfg)
+            outs.append(q)
+            if s is not None:
                 scales.append(s)
-            else:
-                outs.append(w.to(torch.bfloat16))
-        if cfg.w_dtype == "fp8":
-            return torch.stack(outs), torch.stack(scales)
-        return torch.stack(outs), None
+        return torch.stack(outs), (torch.stack(scales) if scales else None)
     w = _randn(shape, cfg.w_std, seed, device)
-    if cfg.w_dtype == "fp8":
-        return _fp8_per_channel(w)
-    return w.to(torch.bfloat16), None
+    return _encode(w, cfg)
 
 
 # Expert weights do not depend on the token count; the last few weight sets
@@ -188,7 +208,7 @@ def generate(cfg: LayerConfig, seed: int = 0, device: str = "cpu",
     else:
         out["router_b"] = _randn((E,), cfg.bias_std, seeds["router_b"], device)
 
-    wkey = (d, E, f, fs, cfg.w_dtype, cfg.w_std, seed, str(device))
+    wkey = (d, E, f, fs, cfg.w_dtype, cfg.scale_block, cfg.w_std, seed, str(device))
     if cache and wkey in _WEIGHT_CACHE:
         out.update(_WEIGHT_CACHE[wkey])
         return out

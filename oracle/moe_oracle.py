@@ -109,14 +109,21 @@ def round_to_bf16_bits(v: np.ndarray) -> np.ndarray:
 def dequant_weight(w: np.ndarray, scale: Optional[np.ndarray], w_dtype: str) -> np.ndarray:
     """Stored expert weight -> float64 [out, in].
 
-    bfloat16: exact widening.  FP8: decoded code times its output channel's
-    FP32 scale (the scale is used as stored, never rounded to a power of two).
+    bfloat16: exact widening.  FP8: decoded code times its FP32 scale, used as
+    stored (never rounded to a power of two).  `scale` holds one value per
+    output channel ([..., out]) or one per block of the matrix ([..., out/b,
+    in/b], the released checkpoint's 128 x 128 blocks, "Inside Kolibri 1",
+    section "The FP8 path is explicitly mixed precision").
     """
     if w_dtype == "bf16":
         return decode_bf16(w)
     if w_dtype == "fp8":
         q = decode_e4m3fn(w)
         s = np.asarray(scale, dtype=np.float32).astype(np.float64)
+        if s.ndim == q.ndim:
+            # one scale per (out/b, in/b) block: expand each scale over its block
+            bo, bi = q.shape[-2] // s.shape[-2], q.shape[-1] // s.shape[-1]
+            return q * np.repeat(np.repeat(s, bo, axis=-2), bi, axis=-1)
         return q * s[..., :, None]
     raise ValueError(w_dtype)
 

@@ -69,6 +69,20 @@ def pin_fp8_scale_exact(o):
     assert not np.allclose(got, np.array([[1.0, 2.0, -3.0, 2.0 ** -9]]) * pow2)
 
 
+def pin_fp8_block_scales(o):
+    """128x128 block scales: every element of a block uses that block's scale."""
+    rng = np.random.default_rng(12)
+    q = rng.integers(0, 256, size=(256, 384), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x30  # no NaN codes
+    s = (rng.random((2, 3)) * 0.01 + 1e-3).astype(np.float32)
+    got = o.dequant_weight(q, s, "fp8")
+    dec = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for bo in range(2):
+        for bi in range(3):
+            blk = got[bo * 128:(bo + 1) * 128, bi * 128:(bi + 1) * 128]
+            assert np.array_equal(blk, dec[bo * 128:(bo + 1) * 128, bi * 128:(bi + 1) * 128] * float(s[bo, bi]))
+
+
 def pin_bf16_rounding(o):
     """Output rounding to bfloat16 agrees with torch's float32 -> bfloat16."""
     rng = np.random.default_rng(1)
@@ -228,9 +242,9 @@ def pin_textbook_expert(o):
     assert np.allclose(got, ref, rtol=1e-13, atol=1e-15)
 
 
-def _small_layer(n=48, d=32, n_exp=8, k=2, f=12, w_dtype="bf16", x_dtype="f32", seed=0):
+def _small_layer(n=48, d=32, n_exp=8, k=2, f=12, w_dtype="bf16", x_dtype="f32", seed=0, scale_block=0):
     cfg = get_config("toy").replace(n_tokens=n, d_model=d, n_experts=n_exp, top_k=k, d_ff=f,
-                                    d_ff_shared=f, w_dtype=w_dtype, x_dtype=x_dtype)
+                                    d_ff_shared=f, w_dtype=w_dtype, x_dtype=x_dtype, scale_block=scale_block)
     return cfg, to_numpy(generate(cfg, seed=seed))
 
 
@@ -259,8 +273,10 @@ def _dense_form(o, inp, k, w_dtype):
 
 def pin_dense_formulation(o):
     """Routed output equals the dense compute-every-expert-then-mask form."""
-    for w_dtype, x_dtype, n_exp, k in (("bf16", "f32", 8, 2), ("fp8", "bf16", 8, 6), ("bf16", "bf16", 16, 6)):
-        cfg, inp = _small_layer(n_exp=n_exp, k=k, w_dtype=w_dtype, x_dtype=x_dtype)
+    for w_dtype, x_dtype, n_exp, k, blk in (("bf16", "f32", 8, 2, 0), ("fp8", "bf16", 8, 6, 0),
+                                            ("bf16", "bf16", 16, 6, 0), ("fp8", "bf16", 8, 3, 128)):
+        cfg, inp = _small_layer(n_exp=n_exp, k=k, w_dtype=w_dtype, x_dtype=x_dtype, scale_block=blk,
+                                d=256 if blk else 32, f=128 if blk else 12)
         res = o.moe_forward(inp, k, w_dtype, x_dtype)
         dense, mask = _dense_form(o, inp, k, w_dtype)
         assert np.allclose(res["out64"], dense, rtol=1e-12, atol=1e-14)

@@ -51,8 +51,13 @@ def test_workspace_size_host_only(lib):
     assert B.workspace_size(_desc(n_tokens=64)) > n
     # invalid descriptions give 0
     for bad in (dict(top_k=0), dict(top_k=9), dict(n_experts=4, top_k=6), dict(d_model=100),
-                dict(d_ff=0), dict(n_tokens=-1), dict(flags=4), dict(n_experts=2000)):
+                dict(d_ff=0), dict(n_tokens=-1), dict(flags=8), dict(n_experts=2000),
+                # block scales need FP8 weights and 128-multiples
+                dict(flags=B.MOE_FLAG_FP8_BLOCK128),
+                dict(flags=B.MOE_FLAG_FP8_BLOCK128, w_dtype=B.MOE_DTYPE_FP8_E4M3, d_ff=448),
+                dict(flags=B.MOE_FLAG_FP8_BLOCK128, w_dtype=B.MOE_DTYPE_FP8_E4M3, d_model=2496)):
         assert B.workspace_size(_desc(**bad)) == 0, bad
+    assert B.workspace_size(_desc(flags=B.MOE_FLAG_FP8_BLOCK128, w_dtype=B.MOE_DTYPE_FP8_E4M3)) == n
 
 
 def test_status_strings(lib):

@@ -26,7 +26,8 @@ def _need_gpu():
 
 def _run_full(cfg, seed=0, residual=False, renormalize=False):
     _say(f"case {cfg.name} N={cfg.n_tokens} d={cfg.d_model} E={cfg.n_experts} k={cfg.top_k} "
-         f"f={cfg.d_ff} x={cfg.x_dtype} w={cfg.w_dtype} seed={seed} residual={residual} renorm={renormalize}")
+         f"f={cfg.d_ff} fs={cfg.d_ff_shared} x={cfg.x_dtype} w={cfg.w_dtype} blk={cfg.scale_block} seed={seed} "
+         f"residual={residual} renorm={renormalize}")
     host = generate(cfg, seed=seed)
     dev = PA.to_device(host)
     res_t = res_np = None
@@ -76,6 +77,24 @@ def test_renormalized_gate(cfg_name, over):
     _run_full(get_config(cfg_name, **over), renormalize=True)
 
 
+@pytest.mark.parametrize("over", [
+    dict(n_tokens=16), dict(n_tokens=128), dict(n_tokens=600),
+    dict(n_tokens=9, x_dtype="bf16", d_model=384, d_ff=256, d_ff_shared=128),
+    dict(n_tokens=200, x_dtype="bf16", d_model=384, d_ff=256, d_ff_shared=128),
+])
+def test_fp8_block_scales_toy(over):
+    """FP8 weights with one scale per 128 x 128 block (MOE_FLAG_FP8_BLOCK128): stream and GEMM
+    paths, FP32 and bf16 activations, an odd count of 128-row output blocks, f != f_s."""
+    base = dict(w_dtype="fp8", scale_block=128, d_ff=128, d_ff_shared=128)
+    base.update(over)
+    _run_full(get_config("toy", **base))
+
+
+@pytest.mark.parametrize("n", [4, 48])
+def test_decode_fp8_block_scales(n):
+    _run_full(get_config("fp8block", n_tokens=n))
+
+
 @pytest.mark.parametrize("n", [16, 200])
 def test_128_experts(n):
     """The 128-expert shape of the predecessor model, top-6, full hidden size."""
@@ -114,7 +133,7 @@ def test_zero_tokens_is_noop():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("name", ["prefill", "fp8", "zipf"])
+@pytest.mark.parametrize("name", ["prefill", "fp8", "fp8block", "zipf"])
 def test_full_size_sampled(name):
     """Full-size workloads: routing and layout of every token, output of a sample."""
     cfg = get_config(name)

@@ -46,6 +46,8 @@ MUTATIONS = {
     "residual_dropped": ("out64 = out64 + _x_to_f64(residual)", "out64 = out64"),
     "renorm_no_max_shift_sign": ("z = np.exp(h - h.max(axis=1, keepdims=True))",
                                  "z = np.exp(h.max(axis=1, keepdims=True) - h)"),
+    "block_scale_transposed": ("return q * np.repeat(np.repeat(s, bo, axis=-2), bi, axis=-1)",
+                               "return q * np.repeat(np.repeat(s, bi, axis=-1), bo, axis=-2)[..., ::-1, :]"),
     "rms_no_sqrt": ("return v64 / np.sqrt(np.mean(v64 * v64, axis=-1, keepdims=True) + eps) * g64",
                     "return v64 / (np.mean(v64 * v64, axis=-1, keepdims=True) + eps) * g64"),
     "block_no_post_norm": ("    z = rms_norm(res[\"out64\"], g_post, eps)", "    z = res[\"out64\"]"),
