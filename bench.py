@@ -91,10 +91,16 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": 3}), flush=True)
 
 
-def kernel_sources_hash() -> str:
+# source files that define each expert kernel (with the device helpers it uses)
+KERNEL_SOURCES = {"gate_up_stream": ("stream.hip", "moe_common.h"), "down_stream": ("stream.hip", "moe_common.h"),
+                  "gate_up_gemm": ("gemm.hip", "moe_common.h"), "down_gemm": ("gemm.hip", "moe_common.h")}
+
+
+def kernel_sources_hash(kernel: str) -> str:
+    """Hash of the sources of `kernel`: stored traffic counts are used only while it matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fine_grained_sparse_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(name.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -274,7 +280,7 @@ def main():
     if os.path.exists(tpath):
         with open(tpath) as fh:
             tr = json.load(fh)
-        if tr.get("kernel_sources_hash") == kernel_sources_hash() and tr.get("kernel") == dom["kernel"]:
+        if tr.get("kernel") == dom["kernel"] and tr.get("kernel_sources_hash") == kernel_sources_hash(dom["kernel"]):
             traffic = tr.get("bytes_per_launch")
 
     roofline = {k2: dom[k2] for k2 in ("bound", "achieved", "peak", "unit", "frac")}
