@@ -35,7 +35,11 @@ Readings taken where the pages are silent (each is listed in the design notes):
   * FP8 is OCP E4M3FN (bias 7, max 448, NaN at S.1111.111, no infinities) and
     a dequantised weight is code value x scale;
   * everything after the logits is computed in float64; the output is rounded
-    once to the output dtype (float32 or bfloat16, round to nearest even).
+    once to the output dtype (float32 or bfloat16, round to nearest even);
+  * optional 1 x 128 activation quantisation (the FP8 section's dynamic
+    groups): per group scale = float32(amax / 448), codes = E4M3 nearest-even
+    of float32(v / scale); applied to x and to each expert's hidden
+    activations (rounded to float32 first), never to the router's input.
 
 Parity status: every function below is pinned by the CPU tests (brute-force
 selection, library sorts and decoders, dense compute-every-expert formulation,
@@ -56,6 +60,7 @@ __all__ = [
     "select_topk", "mixture_weights", "dispatch", "swiglu_expert",
     "combine", "moe_forward", "token_outputs", "brute_force_topk",
     "expert_param_counts", "round_to_bf16_bits", "rms_norm", "block_forward",
+    "encode_e4m3fn", "quantize_groups", "dequantize_groups", "fake_quant",
 ]
 
 
@@ -126,6 +131,65 @@ def dequant_weight(w: np.ndarray, scale: Optional[np.ndarray], w_dtype: str) -> 
             return q * np.repeat(np.repeat(s, bo, axis=-2), bi, axis=-1)
         return q * s[..., :, None]
     raise ValueError(w_dtype)
+
+
+E4M3_MAX = 448.0
+
+
+def encode_e4m3fn(r: np.ndarray) -> np.ndarray:
+    """float32 values with |r| <= 448 -> OCP E4M3FN codes, nearest value, ties to even.
+
+    The non-negative finite values are the codes 0x00..0x7E in increasing
+    order; each |r| goes to the closer of its two neighbours in that list, and
+    an exact midpoint to the code whose mantissa (lowest bit) is even.  The
+    sign bit is copied, so -0.0 gives 0x80.
+    """
+    r = np.asarray(r, dtype=np.float32)
+    if np.any(np.abs(r) > E4M3_MAX) or not np.all(np.isfinite(r)):
+        raise ValueError("encode_e4m3fn needs finite |r| <= 448")
+    table = decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))
+    a = np.abs(r.astype(np.float64))
+    hi = np.searchsorted(table, a, side="left")      # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - table[lo], table[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return code | np.where(np.signbit(r), 0x80, 0).astype(np.uint8)
+
+
+def quantize_groups(v32: np.ndarray, group: int = 128):
+    """Dynamic FP8 quantisation of activations in 1 x `group` groups.
+
+    "Inside Kolibri 1", section "The FP8 path is explicitly mixed precision":
+    activations are quantised on the fly in groups of 1 x 128.  Per group of
+    `group` consecutive values of a row: scale = float32(amax / 448) (1 for an
+    all-zero group), code = E4M3 of float32(v / scale) clamped to +-448 (the
+    clamp only catches the amax element when the division rounds above 448).
+    Every step is a float32 operation, as the kernels do it.  Returns codes
+    [rows, cols] uint8 and scales [rows, cols/group] float32.
+    """
+    v = np.asarray(v32, dtype=np.float32)
+    rows, cols = v.shape
+    if cols % group:
+        raise ValueError("cols must be a multiple of the group size")
+    vg = v.reshape(rows, cols // group, group)
+    amax = np.abs(vg).max(axis=2)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    r = (vg / scale[..., None]).astype(np.float32)
+    r = np.clip(r, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    return encode_e4m3fn(r).reshape(rows, cols), scale
+
+
+def dequantize_groups(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """codes [rows, cols] times their group's scale, float64 (exact)."""
+    q = decode_e4m3fn(codes)
+    g = q.shape[1] // scale.shape[1]
+    return q * np.repeat(np.asarray(scale, dtype=np.float32).astype(np.float64), g, axis=1)
+
+
+def fake_quant(v: np.ndarray) -> np.ndarray:
+    """Rows rounded to float32, quantised in 1 x 128 groups and decoded again (float64)."""
+    return dequantize_groups(*quantize_groups(np.asarray(v, dtype=np.float64).astype(np.float32)))
 
 
 def _x_to_f64(x: np.ndarray) -> np.ndarray:
@@ -235,15 +299,20 @@ def _sigmoid(z: np.ndarray) -> np.ndarray:
     return 1.0 / (1.0 + np.exp(-z))
 
 
-def swiglu_expert(x64: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
+def swiglu_expert(x64: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
+                  act_quant: bool = False) -> np.ndarray:
     """One SwiGLU expert on rows of x: W_d (SiLU(W_g x) * (W_u x)).
 
     x64 [m, d]; wg, wu [f, d]; wd [d, f]; all float64; no bias terms.
-    SiLU(z) = z * sigmoid(z).
+    SiLU(z) = z * sigmoid(z).  With `act_quant` the hidden activations, the
+    down projection's input, are rounded to float32 and quantised in 1 x 128
+    groups first (the caller quantises x the same way).
     """
     a = x64 @ wg.T
     u = x64 @ wu.T
     hidden = a * _sigmoid(a) * u
+    if act_quant:
+        hidden = fake_quant(hidden)
     return hidden @ wd.T
 
 
@@ -279,13 +348,17 @@ def _finish(out64: np.ndarray, x_dtype: str, residual: Optional[np.ndarray]):
 
 
 def moe_forward(inp: Dict[str, np.ndarray], top_k: int, w_dtype: str, x_dtype: str,
-                residual: Optional[np.ndarray] = None, renormalize: bool = False) -> Dict[str, np.ndarray]:
+                residual: Optional[np.ndarray] = None, renormalize: bool = False,
+                act_quant: bool = False) -> Dict[str, np.ndarray]:
     """The whole layer for every token.
 
     `inp` holds numpy arrays as produced by moe_inputs.to_numpy.  With
     `residual` the old output is added before the single rounding (the
-    caller's residual add, done in place).  Returns routing, layout, per-row
-    expert outputs and the output (float64 and rounded to the output dtype).
+    caller's residual add, done in place).  With `act_quant` the inputs of
+    every expert matmul (x, and each expert's hidden activations) are
+    quantised dynamically in 1 x 128 groups (quantize_groups); the router
+    still sees x unquantised.  Returns routing, layout, per-row expert
+    outputs and the output (float64 and rounded to the output dtype).
     """
     x64 = _x_to_f64(inp["x"])
     n = x64.shape[0]
@@ -296,6 +369,7 @@ def moe_forward(inp: Dict[str, np.ndarray], top_k: int, w_dtype: str, x_dtype: s
     counts, offsets, pair_of_row, row_of_pair = dispatch(ids, n_exp)
 
     d = x64.shape[1]
+    xe = fake_quant(x64) if act_quant else x64   # the experts' input
     y_rows = np.zeros((n * top_k, d), dtype=np.float64)
     for e in range(n_exp):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
@@ -303,9 +377,9 @@ def moe_forward(inp: Dict[str, np.ndarray], top_k: int, w_dtype: str, x_dtype: s
             continue
         tokens = pair_of_row[lo:hi] // top_k
         wg, wu, wd = _expert_weights(inp, e, w_dtype)
-        y_rows[lo:hi] = swiglu_expert(x64[tokens], wg, wu, wd)
+        y_rows[lo:hi] = swiglu_expert(xe[tokens], wg, wu, wd, act_quant)
 
-    ys = swiglu_expert(x64, *_shared_weights(inp, w_dtype))
+    ys = swiglu_expert(xe, *_shared_weights(inp, w_dtype), act_quant)
     out64 = combine(ys, y_rows, w, row_of_pair)
     out64, out_cast = _finish(out64, x_dtype, residual)
     return dict(logits=h32, scores=s, ids=ids, gap=gap, w=w, counts=counts,
@@ -315,7 +389,7 @@ def moe_forward(inp: Dict[str, np.ndarray], top_k: int, w_dtype: str, x_dtype: s
 
 def token_outputs(inp: Dict[str, np.ndarray], tokens: Sequence[int], top_k: int,
                   w_dtype: str, ids: Optional[np.ndarray] = None,
-                  renormalize: bool = False) -> Dict[str, np.ndarray]:
+                  renormalize: bool = False, act_quant: bool = False) -> Dict[str, np.ndarray]:
     """Routing of every token, and the output of the listed tokens only.
 
     For full-size checks: the layer output of token t depends only on x[t],
@@ -334,12 +408,14 @@ def token_outputs(inp: Dict[str, np.ndarray], tokens: Sequence[int], top_k: int,
     outs = []
     for t in tokens:
         xt = x64[t:t + 1]
-        acc = swiglu_expert(xt, *shared)[0]
+        if act_quant:   # groups lie within one row, so a row quantises on its own
+            xt = fake_quant(xt)
+        acc = swiglu_expert(xt, *shared, act_quant)[0]
         for j in range(top_k):
             e = int(use_ids[t, j])
             if e not in cache:
                 cache[e] = _expert_weights(inp, e, w_dtype)
-            acc = acc + w[t, j] * swiglu_expert(xt, *cache[e])[0]
+            acc = acc + w[t, j] * swiglu_expert(xt, *cache[e], act_quant)[0]
         outs.append(acc)
     return dict(logits=h32, ids=own_ids, gap=gap, w=w, out64=np.array(outs))
 

@@ -83,6 +83,64 @@ def pin_fp8_block_scales(o):
             assert np.array_equal(blk, dec[bo * 128:(bo + 1) * 128, bi * 128:(bi + 1) * 128] * float(s[bo, bi]))
 
 
+def pin_e4m3_encoder(o):
+    """E4M3 encoding: round trip of every code, and torch's float8_e4m3fn cast
+    (nearest, ties to even) on random values, exact midpoints and -0.0."""
+    codes = np.arange(256, dtype=np.uint8)
+    finite = codes[(codes & 0x7F) != 0x7F]
+    assert np.array_equal(o.encode_e4m3fn(o.decode_e4m3fn(finite).astype(np.float32)), finite)
+    rng = np.random.default_rng(13)
+    table = o.decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))
+    mids = ((table[:-1] + table[1:]) / 2).astype(np.float32)   # exact in float32
+    r = np.concatenate([rng.uniform(-448, 448, 20000), rng.standard_normal(20000) * 2.0 ** rng.integers(-12, 6, 20000),
+                        mids, -mids, [0.0, -0.0, 448.0, -448.0]]).astype(np.float32)
+    ref = torch.from_numpy(r).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(o.encode_e4m3fn(r), ref)
+
+
+def pin_group_quantisation(o):
+    """1 x 128 activation groups: closed forms and the error bound."""
+    # a hand-worked group: amax 7 gives scale 7/448 = 2^-6 exactly, so codes are of 64 v
+    v = np.zeros((1, 128), np.float32)
+    v[0, :4] = [1.0, -2.0, 0.5, 7.0]
+    q, sc = o.quantize_groups(v)
+    assert sc[0, 0] == np.float32(2.0 ** -6)
+    assert q[0, :4].tolist() == [0x68, 0xF0, 0x60, 0x7E] and not q[0, 4:].any()
+    # an all-zero group has scale 1 and zero codes
+    q, sc = o.quantize_groups(np.zeros((2, 256), np.float32))
+    assert np.all(sc == 1.0) and not q.any()
+    rng = np.random.default_rng(14)
+    v = (rng.standard_normal((40, 512)) * rng.uniform(1e-3, 1e3, (40, 1))).astype(np.float32)
+    q, sc = o.quantize_groups(v)
+    assert q.shape == v.shape and sc.shape == (40, 4)
+    # each group's largest magnitude maps to +-448
+    g = np.abs(v).reshape(40, 4, 128).argmax(axis=2)
+    top = np.take_along_axis(q.reshape(40, 4, 128), g[..., None], axis=2)[..., 0]
+    assert np.all((top & 0x7F) == 0x7E)
+    # nearest value: error at most half a step (2^-4 relative, or 2^-10 scale in the subnormal range)
+    err = np.abs(o.dequantize_groups(q, sc) - v.astype(np.float64))
+    s_full = np.repeat(sc.astype(np.float64), 128, axis=1)
+    assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(v), 2.0 ** -10 * s_full) * (1 + 1e-6))
+    # scaling a row by a power of two scales its scales and keeps its codes
+    q4, sc4 = o.quantize_groups(v * np.float32(4.0))
+    assert np.array_equal(q4, q) and np.array_equal(sc4, sc * np.float32(4.0))
+
+
+def pin_hidden_quantised(o):
+    """With act_quant, the down projection sees hidden values on the E4M3 grid of their group."""
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((6, 128))
+    wg, wu = rng.standard_normal((128, 128)) * 0.1, rng.standard_normal((128, 128)) * 0.1
+    y = o.swiglu_expert(x, wg, wu, np.eye(128), act_quant=True)   # identity down: y = quantised hidden
+    a = x @ wg.T
+    plain = a / (1 + np.exp(-a)) * (x @ wu.T)
+    s = np.abs(y).max(axis=1, keepdims=True) / 448.0
+    r = y / s
+    grid = o.decode_e4m3fn(o.encode_e4m3fn(np.clip(r, -448, 448).astype(np.float32)))
+    assert np.allclose(r, grid, rtol=1e-6, atol=1e-9)
+    assert not np.allclose(y, plain, rtol=1e-3) and np.allclose(y, plain, rtol=0.07, atol=1e-3 * np.abs(plain).max())
+
+
 def pin_bf16_rounding(o):
     """Output rounding to bfloat16 agrees with torch's float32 -> bfloat16."""
     rng = np.random.default_rng(1)
@@ -248,9 +306,10 @@ def _small_layer(n=48, d=32, n_exp=8, k=2, f=12, w_dtype="bf16", x_dtype="f32", 
     return cfg, to_numpy(generate(cfg, seed=seed))
 
 
-def _dense_form(o, inp, k, w_dtype):
+def _dense_form(o, inp, k, w_dtype, act_quant=False):
     """Compute every expert on every token, mask by the selection, sum by id."""
     x = o.decode_bf16(inp["x"]) if inp["x"].dtype == np.uint16 else inp["x"].astype(np.float64)
+    xe = o.fake_quant(x) if act_quant else x
     n_exp = inp["router_w"].shape[0]
     w32 = inp["router_w"].astype(np.float64)
     h = (x @ w32.T).astype(np.float32)
@@ -261,12 +320,12 @@ def _dense_form(o, inp, k, w_dtype):
         for e in top:
             mask[t, e] = 1.0 / (1.0 + math.exp(-float(h[t, e])))
     sc = lambda key: inp.get(key)
-    out = o.swiglu_expert(x, o.dequant_weight(inp["ws_gate"], sc("ss_gate"), w_dtype),
+    out = o.swiglu_expert(xe, o.dequant_weight(inp["ws_gate"], sc("ss_gate"), w_dtype),
                           o.dequant_weight(inp["ws_up"], sc("ss_up"), w_dtype),
-                          o.dequant_weight(inp["ws_down"], sc("ss_down"), w_dtype))
+                          o.dequant_weight(inp["ws_down"], sc("ss_down"), w_dtype), act_quant)
     for e in range(n_exp):
         g = lambda key, skey: o.dequant_weight(inp[key][e], None if sc(skey) is None else sc(skey)[e], w_dtype)
-        ye = o.swiglu_expert(x, g("w_gate", "s_gate"), g("w_up", "s_up"), g("w_down", "s_down"))
+        ye = o.swiglu_expert(xe, g("w_gate", "s_gate"), g("w_up", "s_up"), g("w_down", "s_down"), act_quant)
         out = out + mask[:, e:e + 1] * ye
     return out, mask
 
@@ -277,12 +336,13 @@ def pin_dense_formulation(o):
                                             ("bf16", "bf16", 16, 6, 0), ("fp8", "bf16", 8, 3, 128)):
         cfg, inp = _small_layer(n_exp=n_exp, k=k, w_dtype=w_dtype, x_dtype=x_dtype, scale_block=blk,
                                 d=256 if blk else 32, f=128 if blk else 12)
-        res = o.moe_forward(inp, k, w_dtype, x_dtype)
-        dense, mask = _dense_form(o, inp, k, w_dtype)
-        assert np.allclose(res["out64"], dense, rtol=1e-12, atol=1e-14)
-        sel = np.zeros_like(mask, dtype=bool)
-        np.put_along_axis(sel, res["ids"].astype(np.int64), True, axis=1)
-        assert np.array_equal(sel, mask > 0)
+        for aq in ((False, True) if blk else (False,)):
+            res = o.moe_forward(inp, k, w_dtype, x_dtype, act_quant=aq)
+            dense, mask = _dense_form(o, inp, k, w_dtype, act_quant=aq)
+            assert np.allclose(res["out64"], dense, rtol=1e-12, atol=1e-14)
+            sel = np.zeros_like(mask, dtype=bool)
+            np.put_along_axis(sel, res["ids"].astype(np.int64), True, axis=1)
+            assert np.array_equal(sel, mask > 0)
 
 
 def pin_all_selected(o):
@@ -320,6 +380,12 @@ def pin_token_outputs_match_full(o):
     part = o.token_outputs(inp, toks, 6, "fp8")
     assert np.array_equal(part["ids"], full["ids"])
     assert np.allclose(part["out64"], full["out64"][toks], rtol=1e-12, atol=1e-14)
+    # with 1 x 128 activation quantisation
+    cfg, inp = _small_layer(n=20, n_exp=8, k=3, w_dtype="fp8", x_dtype="bf16", seed=5, d=256, f=128,
+                            scale_block=128)
+    full = o.moe_forward(inp, 3, "fp8", "bf16", act_quant=True)
+    part = o.token_outputs(inp, toks[:2] + [19], 3, "fp8", act_quant=True)
+    assert np.allclose(part["out64"], full["out64"][toks[:2] + [19]], rtol=1e-12, atol=1e-14)
 
 
 def pin_renormalized_weights(o):

@@ -48,6 +48,12 @@ MUTATIONS = {
                                  "z = np.exp(h.max(axis=1, keepdims=True) - h)"),
     "block_scale_transposed": ("return q * np.repeat(np.repeat(s, bo, axis=-2), bi, axis=-1)",
                                "return q * np.repeat(np.repeat(s, bi, axis=-1), bo, axis=-2)[..., ::-1, :]"),
+    "aq_scale_240": ("amax / np.float32(E4M3_MAX)", "amax / np.float32(240.0)"),
+    "aq_ties_up": ("pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))", "pick_hi = d_hi <= d_lo"),
+    "aq_hidden_plain": ("        hidden = fake_quant(hidden)\n", "        hidden = hidden\n"),
+    "aq_x_plain": ("xe = fake_quant(x64) if act_quant else x64", "xe = x64"),
+    "aq_tokens_plain": ("        if act_quant:   # groups lie within one row, so a row quantises on its own\n            xt = fake_quant(xt)",
+                        "        pass"),
     "rms_no_sqrt": ("return v64 / np.sqrt(np.mean(v64 * v64, axis=-1, keepdims=True) + eps) * g64",
                     "return v64 / (np.mean(v64 * v64, axis=-1, keepdims=True) + eps) * g64"),
     "block_no_post_norm": ("    z = rms_norm(res[\"out64\"], g_post, eps)", "    z = res[\"out64\"]"),
