@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "fp8", "fp8block", "zipf", "toy"])
     ap.add_argument("--tokens", type=int, default=None, help="override the batch size")
     ap.add_argument("--layers", type=int, default=4, help="independent layer instances cycled by the steps")
+    ap.add_argument("--act-quant", action="store_true",
+                    help="FP8 x FP8 expert matmuls on 1 x 128 quantised activations (FP8 weights only)")
     ap.add_argument("--variant", default="plain", choices=["plain", "renorm", "block"],
                     help="plain moe_forward; renormalised gate; or moe_block_forward (sandwich RMSNorms, "
                          "residual updated in place)")
@@ -143,8 +145,12 @@ def main():
     for m in mods[1:]:
         m.workspace = ws  # one workspace, calls are stream-ordered
     outs = [torch.empty_like(inp["x"]) for inp in layers]
-    flags = B.MOE_FLAG_RENORMALIZE if args.variant == "renorm" else 0
+    flags = (B.MOE_FLAG_RENORMALIZE if args.variant == "renorm" else 0) | \
+        (B.MOE_FLAG_FP8_ACT_QUANT if args.act_quant else 0)
     descs = [m.desc(N, flags) for m in mods]
+    need = max(B.workspace_size(dsc) for dsc in descs)
+    if need > ws.numel():
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
     if args.variant == "block":
         need = max(int(B.lib().moe_block_workspace_size(ctypes.byref(dsc))) for dsc in descs)
         if need > ws.numel():
@@ -244,7 +250,9 @@ def main():
 
     gu_flops = 2.0 * (N * k * 2 * f + N * 2 * fs) * d
     dn_flops = 2.0 * (N * k * f + N * fs) * d
-    mfma_peak = MFMA_PEAK_TFLOPS["bf16"]   # the expert matmuls run bf16 (FP8 weights are decoded)
+    # the expert matmuls run bf16 (FP8 weights decoded), or FP8 x FP8 with quantised activations
+    mfma_dtype = "fp8" if args.act_quant else "bf16"
+    mfma_peak = MFMA_PEAK_TFLOPS[mfma_dtype]
 
     def roof(name, bytes_sum, flops_sum, secs, n):
         t_hbm = bytes_sum / (HBM_PEAK_GBS * 1e9)
@@ -259,7 +267,7 @@ def main():
                  "unit": "TFLOP/s", "frac": round(mfma_frac, 4)}
         r.update({"kernel": name, "avg_launch_us": round(secs / n * 1e6, 2),
                   "algorithmic_bytes_per_launch": int(bytes_sum / n), "flops_per_launch": int(flops_sum / n),
-                  "hbm_frac": round(hbm_frac, 4), "mfma_frac_bf16": round(mfma_frac, 4)})
+                  "hbm_frac": round(hbm_frac, 4), f"mfma_frac_{mfma_dtype}": round(mfma_frac, 4)})
         return r
 
     gu_b = sum(gu_bytes(touched[i % L]) for i in range(args.steps))
@@ -288,25 +296,25 @@ def main():
     roofline.update({k2: v for k2, v in dom.items() if k2 not in roofline})
     roofline["other_expert_kernel"] = r_dn if dom is r_gu else r_gu
     roofline["whole_step"] = {"hbm_frac": round(layer_b / elapsed / 1e9 / HBM_PEAK_GBS, 4),
-                              "mfma_frac_bf16": round(layer_flops / elapsed / 1e12 / mfma_peak, 4),
+                              f"mfma_frac_{mfma_dtype}": round(layer_flops / elapsed / 1e12 / mfma_peak, 4),
                               "algorithmic_bytes": int(layer_b / args.steps),
                               "flops": int(layer_flops / args.steps)}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": cfg.w_dtype if cfg.w_dtype == "bf16" else "fp8-weights/bf16",
+        "vs_baseline": None, "dtype": ("bf16" if cfg.w_dtype == "bf16" else "fp8" if args.act_quant else "fp8-weights/bf16"),
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: N={N} d={d} E={E} top_k={k} f={f} f_shared={fs} "
                                f"x={cfg.x_dtype} w={cfg.w_dtype}"
                                + (f" scales={cfg.scale_block}x{cfg.scale_block}" if cfg.scale_block else "")
                                + f" bias={cfg.bias_kind}",
                    "n_tokens": N, "layers_cycled": L, "touched_experts": touched, "expert_path": kind,
-                   "variant": args.variant},
+                   "variant": args.variant, "act_quant": bool(args.act_quant)},
         "roofline": roofline,
     }
 
-    if not args.no_cpu_baseline and args.variant == "plain":
+    if not args.no_cpu_baseline and args.variant == "plain" and not args.act_quant:
         result["cpu_baseline"], result["parity_step0"] = cpu_baseline(cfg, layers[0], outs, mods, descs, ws, stream,
                                                                        args.cpu_seconds)
     print(json.dumps(result), flush=True)

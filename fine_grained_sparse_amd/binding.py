@@ -21,11 +21,12 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3 = 0, 1, 2
 MOE_FLAG_ACCUMULATE = 1
 MOE_FLAG_RENORMALIZE = 2
 MOE_FLAG_FP8_BLOCK128 = 4
+MOE_FLAG_FP8_ACT_QUANT = 8
 STAGES = ("router", "topk", "dispatch", "gate_up", "down", "combine")
 MOE_NUM_STAGES = len(STAGES)
 
 EXPORTED = ("moe_workspace_size", "moe_forward", "moe_status_string", "moe_last_hip_error",
-            "moe_block_workspace_size", "moe_block_forward")
+            "moe_block_workspace_size", "moe_block_forward", "moe_quantize_groups")
 
 
 class MoeDesc(ctypes.Structure):
@@ -73,6 +74,9 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(MoeWeights),
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(MoeAux), ctypes.c_void_p]
         L.moe_block_forward.restype = ctypes.c_int
+        L.moe_quantize_groups.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.moe_quantize_groups.restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_hip_error.argtypes = []
@@ -103,6 +107,20 @@ def workspace_size(desc: MoeDesc) -> int:
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+def quantize_groups(v: torch.Tensor, q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None):
+    """moe_quantize_groups on a [rows, cols] float32/bfloat16 device tensor -> (uint8 codes, float32 scales)."""
+    rows, cols = v.shape
+    if q is None:
+        q = torch.empty(rows, cols, dtype=torch.uint8, device=v.device)
+    if scales is None:
+        scales = torch.empty(rows, max(cols // 128, 1), dtype=torch.float32, device=v.device)
+    st = lib().moe_quantize_groups(_ptr(v), _XDT[v.dtype], rows, cols, _ptr(q), _ptr(scales),
+                                   torch.cuda.current_stream(v.device).cuda_stream)
+    if st != MOE_OK:
+        raise MoeError(st, "moe_quantize_groups")
+    return q, scales
 
 
 def weights_struct(w: Dict[str, torch.Tensor]) -> MoeWeights:
@@ -148,11 +166,13 @@ class MoeLayer:
 
     def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, accumulate: bool = False,
                 aux: Optional[MoeAux] = None, router_w: Optional[torch.Tensor] = None,
-                router_b: Optional[torch.Tensor] = None, renormalize: bool = False) -> torch.Tensor:
+                router_b: Optional[torch.Tensor] = None, renormalize: bool = False,
+                act_quant: bool = False) -> torch.Tensor:
         n = x.shape[0]
         if out is None:
             out = torch.empty_like(x)
-        flags = (MOE_FLAG_ACCUMULATE if accumulate else 0) | (MOE_FLAG_RENORMALIZE if renormalize else 0)
+        flags = ((MOE_FLAG_ACCUMULATE if accumulate else 0) | (MOE_FLAG_RENORMALIZE if renormalize else 0)
+                 | (MOE_FLAG_FP8_ACT_QUANT if act_quant else 0))
         desc = self.desc(n, flags)
         need = workspace_size(desc)
         if need > self.workspace.numel():
@@ -165,10 +185,11 @@ class MoeLayer:
         return out
 
     def block_forward(self, resid: torch.Tensor, norm_pre: torch.Tensor, norm_post: torch.Tensor, eps: float,
-                      aux: Optional[MoeAux] = None, renormalize: bool = False) -> torch.Tensor:
+                      aux: Optional[MoeAux] = None, renormalize: bool = False,
+                      act_quant: bool = False) -> torch.Tensor:
         """Sandwich-normalised MoE sublayer; updates `resid` in place and returns it."""
         n = resid.shape[0]
-        desc = self.desc(n, MOE_FLAG_RENORMALIZE if renormalize else 0)
+        desc = self.desc(n, (MOE_FLAG_RENORMALIZE if renormalize else 0) | (MOE_FLAG_FP8_ACT_QUANT if act_quant else 0))
         need = int(lib().moe_block_workspace_size(ctypes.byref(desc)))
         if need == 0:
             raise MoeError(MOE_ERR_ARG, "moe_block_workspace_size")

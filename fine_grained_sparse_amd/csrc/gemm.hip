@@ -445,6 +445,370 @@ __global__ __launch_bounds__(kThreads) void down_gemm_kernel(
     }
 }
 
+// ---------------------------------------------------------------- FP8 x FP8
+// 1 x 128 activation quantisation ("Inside Kolibri 1", section "The FP8 path
+// is explicitly mixed precision"): A holds E4M3 codes of activations with one
+// FP32 scale per row and 128 columns, B the E4M3 weights.  A stage is one
+// 128-wide K block, i.e. 128 bytes per tile row, the same bytes as a bf16
+// stage, so the loader and the LDS layout (rows of 128 bytes padded to 160)
+// are those of the bf16 tile.  Each 16 x 16 sub-tile takes one
+// v_mfma_f32_16x16x128_f8f6f4 per stage (a lane supplies 32 consecutive K
+// bytes of its row: half the LDS bytes per flop of bf16), and the stage's
+// products are added into the running sum times (activation scale of the row)
+// x (weight scale of the column block).
+
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4_t mfma_f8(const uint4 &a0, const uint4 &a1, const uint4 &b0, const uint4 &b1) {
+    const i32x8_t a = {(int32_t)a0.x, (int32_t)a0.y, (int32_t)a0.z, (int32_t)a0.w,
+                       (int32_t)a1.x, (int32_t)a1.y, (int32_t)a1.z, (int32_t)a1.w};
+    const i32x8_t b = {(int32_t)b0.x, (int32_t)b0.y, (int32_t)b0.z, (int32_t)b0.w,
+                       (int32_t)b1.x, (int32_t)b1.y, (int32_t)b1.z, (int32_t)b1.w};
+    // formats 0/0: both operands E4M3; scale operands 0 select the unscaled form
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+}
+
+constexpr int kLdsRowB = 2 * kLdsStride;   // 160-byte LDS rows
+
+struct StageF8 {
+    uint4 a[kAPer];
+    uint4 b[kBPer];
+};
+
+// sa[mi]: this lane's activation-scale row for sub-tile mi (row wm*64 + mi*16
+// + lane%16), indexed by K block.  BLKW: column fragments ni < 2 use weight
+// scale sw_lo[kb], ni >= 2 sw_hi[kb]; otherwise the weight scale is applied by
+// the caller (per output channel).
+// b_base[j] is the same for every lane (one expert's matrix); b_off[j] < 2^32.
+template <bool BLKW>
+__device__ __forceinline__ void tile_mma_f8(const uint8_t *a_base, const size_t (&a_off)[kAPer],
+                                            const bool (&a_ok)[kAPer], const uint8_t *const (&b_base)[kBPer],
+                                            const uint32_t (&b_off)[kBPer], int K, const float *sa_base,
+                                            const uint32_t (&sa_off)[4], const float *sw_lo, const float *sw_hi,
+                                            int m, uint8_t *lds, f32x4_t (&acc)[4][4]) {
+    constexpr int kRowStep = kThreads / 8;
+    constexpr int kAB = kBM * kLdsRowB, kStageB = (kBM + kBN) * kLdsRowB;
+    // the wave index is uniform: in a scalar register, the live-row tests are scalar branches
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / kWN, wn = wave % kWN;
+    const int chunk = (tid & 7) * 16;
+    const int r0 = tid >> 3;
+    uint8_t *const As[2] = {lds, lds + kStageB};
+    uint8_t *const Bs[2] = {lds + kAB, lds + kStageB + kAB};
+    const int fr = lane & 15, fk = (lane >> 4) * 32;
+    const int live = min(4, max(0, (m - wm * 64 + 15) / 16));
+
+    auto fetch = [&](StageF8 &st, int k0) {
+#pragma unroll
+        for (int j = 0; j < kAPer; ++j) st.a[j] = *reinterpret_cast<const uint4 *>(a_base + a_off[j] + k0 + chunk);
+#pragma unroll
+        for (int j = 0; j < kBPer; ++j) st.b[j] = *reinterpret_cast<const uint4 *>(b_base[j] + b_off[j] + k0 + chunk);
+    };
+    auto stash = [&](const StageF8 &st, int buf) {
+#pragma unroll
+        for (int j = 0; j < kAPer; ++j)
+            *reinterpret_cast<uint4 *>(As[buf] + (r0 + kRowStep * j) * kLdsRowB + chunk) =
+                a_ok[j] ? st.a[j] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < kBPer; ++j)
+            *reinterpret_cast<uint4 *>(Bs[buf] + (r0 + kRowStep * j) * kLdsRowB + chunk) = st.b[j];
+    };
+    // scales of K block kb: the activation scale of each sub-tile row of this
+    // lane, and the weight scales of the two column halves (wave-uniform)
+    struct Sc { float a[4], wlo, whi; };
+    auto scales = [&](int kb, Sc &sc) {
+        sc.wlo = 1.f;
+        sc.whi = 1.f;
+        if (BLKW) { sc.wlo = sw_lo[kb]; sc.whi = sw_hi[kb]; }
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) sc.a[mi] = sa_base[sa_off[mi] + kb];
+    };
+    // The products of sub-tile row mi are folded while those of mi+1 are in
+    // the matrix core, so at most two rows of products (32 registers) live.
+    auto compute = [&](int buf, const Sc &sc) {
+        uint4 bf[4][2];
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const uint8_t *bp = Bs[buf] + (b_row_of(wn, ni) + fr) * kLdsRowB + fk;
+            bf[ni][0] = *reinterpret_cast<const uint4 *>(bp);
+            bf[ni][1] = *reinterpret_cast<const uint4 *>(bp + 16);
+        }
+        auto products = [&](int mi, f32x4_t (&pr)[4]) {
+            const uint8_t *ap = As[buf] + (wm * 64 + mi * 16 + fr) * kLdsRowB + fk;
+            const uint4 a0 = *reinterpret_cast<const uint4 *>(ap), a1 = *reinterpret_cast<const uint4 *>(ap + 16);
+            // B fragment first: transposed result, a lane holds 4 consecutive columns of one row
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) pr[ni] = mfma_f8(bf[ni][0], bf[ni][1], a0, a1);
+        };
+        auto fold = [&](int mi, const f32x4_t (&pr)[4]) {
+            const float clo = sc.a[mi] * sc.wlo, chi = sc.a[mi] * sc.whi;
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                const float c = ni < 2 ? clo : chi;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[mi][ni][q] = fmaf(pr[ni][q], c, acc[mi][ni][q]);
+            }
+        };
+        f32x4_t p0[4], p1[4];
+        if (live > 0) products(0, p0);
+        if (live > 1) products(1, p1);
+        if (live > 0) fold(0, p0);
+        if (live > 2) products(2, p0);
+        if (live > 1) fold(1, p1);
+        if (live > 3) products(3, p1);
+        if (live > 2) fold(2, p0);
+        if (live > 3) fold(3, p1);
+    };
+
+    const int nk = K / 128;
+    StageF8 s0, s1;
+    Sc c0, c1;
+    fetch(s0, 0);
+    if (nk > 1) fetch(s1, 128);
+    stash(s0, 0);
+    lds_barrier();
+    int kt = 0;
+    for (; kt + 3 < nk; kt += 2) {
+        scales(kt, c0);
+        fetch(s0, (kt + 2) * 128);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(0, c0);
+        __builtin_amdgcn_sched_barrier(0);
+        stash(s1, 1);
+        lds_barrier();
+        scales(kt + 1, c1);
+        fetch(s1, (kt + 3) * 128);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1, c1);
+        __builtin_amdgcn_sched_barrier(0);
+        stash(s0, 0);
+        lds_barrier();
+    }
+    // tail: 1, 2 or 3 stages left (stage kt in LDS buffer 0, stage kt+1 in s1)
+    const int left = nk - kt;
+    if (left == 3) fetch(s0, (kt + 2) * 128);
+    scales(kt, c0);
+    compute(0, c0);
+    if (left >= 2) {
+        stash(s1, 1);
+        lds_barrier();
+        scales(kt + 1, c1);
+        compute(1, c1);
+        if (left == 3) {
+            stash(s0, 0);
+            lds_barrier();
+            scales(kt + 2, c0);
+            compute(0, c0);
+        }
+    }
+}
+
+// grid: (ceil(max(f, fs) / 128), tile capacity); block 512; LDS kGemmLds.
+// A = E4M3 codes of x rows gathered through pair_of_row, scales xs [N][d/128].
+// The epilogue quantises each row's 128 H columns of the tile (one 1 x 128
+// group) to hq / hs.
+template <bool BLKW>
+__global__ __launch_bounds__(kThreads) void gate_up_gemm_f8_kernel(
+    const uint8_t *__restrict__ xq, const float *__restrict__ xs, const void *__restrict__ wg,
+    const void *__restrict__ wu, const float *__restrict__ sg, const float *__restrict__ su,
+    const void *__restrict__ wsg, const void *__restrict__ wsu, const float *__restrict__ ssg,
+    const float *__restrict__ ssu, const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ por, uint8_t *__restrict__ hq,
+    float *__restrict__ hs, int ldh, int d, int E, int k, int f, int fs) {
+    extern __shared__ uint8_t ldsb[];
+    const int u = blockIdx.y;
+    if (u >= *n_tiles) return;
+    const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
+    const bool shared = g == E;
+    const int fg = shared ? fs : f;
+    constexpr int kHalf = kBN / 2;
+    const int c0 = blockIdx.x * kHalf;
+    if (c0 >= fg) return;
+    const int gstart = offsets[g];
+    const int row0 = gstart + m0, m = min(kBM, offsets[g + 1] - row0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 2, wn = wave & 3;
+    const int nkb = d / 128;
+
+    auto token_of = [&](int r) { return shared ? (row0 + r - gstart) : por[row0 + r] / k; };
+    size_t a_off[kAPer];
+    uint32_t b_off[kBPer];
+    bool a_ok[kAPer];
+    const uint8_t *b_base[kBPer];
+    const size_t wrow0 = shared ? 0 : (size_t)g * f;
+#pragma unroll
+    for (int j = 0; j < kAPer; ++j) {
+        const int r = (tid >> 3) + 64 * j;
+        a_ok[j] = r < m;
+        a_off[j] = (size_t)token_of(a_ok[j] ? r : 0) * d;
+    }
+    // loader rows tid/8 + 64 j: j < 2 are gate rows c0.., j >= 2 the matching up rows
+    const uint8_t *gbase = (const uint8_t *)(shared ? wsg : wg) + (wrow0 + c0) * (size_t)d;
+    const uint8_t *ubase = (const uint8_t *)(shared ? wsu : wu) + (wrow0 + c0) * (size_t)d;
+#pragma unroll
+    for (int j = 0; j < kBPer; ++j) {
+        const int r = (tid >> 3) + 64 * j;
+        b_base[j] = j * 64 >= kHalf ? ubase : gbase;
+        b_off[j] = (uint32_t)((r & (kHalf - 1)) * d);   // f_g is a multiple of 128
+    }
+    uint32_t sa_off[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int r = wm * 64 + mi * 16 + (lane & 15);
+        sa_off[mi] = (uint32_t)(token_of(r < m ? r : 0) * nkb);
+    }
+    const float *sw_lo = nullptr, *sw_hi = nullptr;
+    if (BLKW) {
+        const size_t sb = ((shared ? 0 : (size_t)g * (f / 128)) + c0 / 128) * (size_t)nkb;
+        sw_lo = (shared ? ssg : sg) + sb;
+        sw_hi = (shared ? ssu : su) + sb;
+    }
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    tile_mma_f8<BLKW>(xq, a_off, a_ok, b_base, b_off, d, xs, sa_off, sw_lo, sw_hi, m, ldsb, acc);
+
+    // SwiGLU: hv[mi][ni][q] is row wm*64 + mi*16 + lane%16, H column
+    // c0 + wn*32 + ni*16 + 4*(lane/16) + q
+    float hv[4][2][4];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+        const int col = c0 + wn * 32 + ni * 16 + (lane >> 4) * 4;
+        float gs[4] = {1.f, 1.f, 1.f, 1.f}, us[4] = {1.f, 1.f, 1.f, 1.f};
+        if (!BLKW) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                gs[q] = shared ? ssg[col + q] : sg[wrow0 + col + q];
+                us[q] = shared ? ssu[col + q] : su[wrow0 + col + q];
+            }
+        }
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hv[mi][ni][q] = silu(acc[mi][ni][q] * gs[q]) * (acc[mi][ni + 2][q] * us[q]);
+    }
+    // row maxima over the tile's 128 columns: this wave's 32, then across the 4 column waves in LDS
+    float *red = reinterpret_cast<float *>(ldsb);   // [128 rows][4 column waves]
+    float amax[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        float mx = 0.f;
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) mx = fmaxf(mx, fabsf(hv[mi][ni][q]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        amax[mi] = mx;
+    }
+    lds_barrier();   // every wave is done reading the operand tiles
+    if (lane < 16) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) red[(wm * 64 + mi * 16 + lane) * 4 + wn] = amax[mi];
+    }
+    lds_barrier();
+    const int nhb = ldh / 128;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int r = wm * 64 + mi * 16 + (lane & 15);
+        const float4 rm = *reinterpret_cast<const float4 *>(red + r * 4);
+        const float mx = fmaxf(fmaxf(rm.x, rm.y), fmaxf(rm.z, rm.w));
+        const float sc = mx > 0.f ? mx / 448.0f : 1.0f;
+        if (r < m) {
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+                const int col = c0 + wn * 32 + ni * 16 + (lane >> 4) * 4;
+                float v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = fminf(fmaxf(hv[mi][ni][q] / sc, -448.f), 448.f);
+                uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
+                *reinterpret_cast<uint32_t *>(hq + (size_t)(row0 + r) * ldh + col) = w;
+            }
+            if (wn == 0 && lane < 16) hs[(size_t)(row0 + r) * nhb + c0 / 128] = sc;
+        }
+    }
+}
+
+// grid: (ceil(d / 256), tile capacity); block 512; LDS kGemmLds.
+// A = E4M3 codes of the group's hidden rows (contiguous), scales hs.
+template <bool BLKW>
+__global__ __launch_bounds__(kThreads) void down_gemm_f8_kernel(
+    const uint8_t *__restrict__ hq, const float *__restrict__ hs, int ldh, const void *__restrict__ wd,
+    const float *__restrict__ sd, const void *__restrict__ wsd, const float *__restrict__ ssd,
+    const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets,
+    uint16_t *__restrict__ Y, int d, int E, int f, int fs) {
+    extern __shared__ uint8_t ldsb[];
+    const int u = blockIdx.y;
+    if (u >= *n_tiles) return;
+    const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
+    const bool shared = g == E;
+    const int fg = shared ? fs : f;
+    const int o0 = blockIdx.x * kBN;
+    const int row0 = offsets[g] + m0, m = min(kBM, offsets[g + 1] - row0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 2, wn = wave & 3;
+    const uint8_t *base = (const uint8_t *)(shared ? wsd : wd);
+    const size_t obase = shared ? 0 : (size_t)g * d;
+    const int nhb = ldh / 128;
+
+    size_t a_off[kAPer];
+    uint32_t b_off[kBPer];
+    bool a_ok[kAPer];
+    const uint8_t *b_base[kBPer];
+#pragma unroll
+    for (int j = 0; j < kAPer; ++j) {
+        const int r = (tid >> 3) + 64 * j;
+        a_ok[j] = r < m;
+        a_off[j] = (size_t)(row0 + (a_ok[j] ? r : 0)) * ldh;
+    }
+    const uint8_t *ebase = base + obase * (size_t)fg;   // this expert's [d][f_g] matrix
+#pragma unroll
+    for (int j = 0; j < kBPer; ++j) {
+        const int r = (tid >> 3) + 64 * j;
+        b_base[j] = ebase;
+        b_off[j] = (uint32_t)((o0 + r < d ? o0 + r : 0) * fg);   // rows past d: never stored
+    }
+    uint32_t sa_off[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int r = wm * 64 + mi * 16 + (lane & 15);
+        sa_off[mi] = (uint32_t)((row0 + (r < m ? r : 0)) * nhb);
+    }
+    const float *sw_lo = nullptr, *sw_hi = nullptr;
+    if (BLKW) {
+        const int nkb = fg / 128, nob = d / 128, ob = o0 / 128;
+        const float *sp = shared ? ssd : sd + (size_t)g * nob * nkb;
+        sw_lo = sp + (size_t)ob * nkb;
+        sw_hi = sp + (size_t)(ob + 1 < nob ? ob + 1 : ob) * nkb;
+    }
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    tile_mma_f8<BLKW>(hq, a_off, a_ok, b_base, b_off, fg, hs, sa_off, sw_lo, sw_hi, m, ldsb, acc);
+
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+        const int o = o0 + b_row_of(wn, ni) + (lane >> 4) * 4;
+        if (o >= d) continue;
+        float sc[4] = {1.f, 1.f, 1.f, 1.f};
+        if (!BLKW) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sc[q] = shared ? ssd[o + q] : sd[obase + o + q];
+        }
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int r = wm * 64 + mi * 16 + (lane & 15);
+            if (r < m)
+                *reinterpret_cast<uint2 *>(Y + (size_t)(row0 + r) * d + o) =
+                    make_uint2(pack_bf16x2(acc[mi][ni][0] * sc[0], acc[mi][ni][1] * sc[1]),
+                               pack_bf16x2(acc[mi][ni][2] * sc[2], acc[mi][ni][3] * sc[3]));
+        }
+    }
+}
+
 // ---------------------------------------------------------------- router
 // "Inside Kolibri 1" (flozi.net), section "Routing: selection bias and
 // mixture weights are separate": FP32 logits [N, 384] from the flattened
@@ -553,6 +917,10 @@ hipError_t gemm_kernels_init() {
     if ((e = allow_lds(gate_up_gemm_kernel<kWFp8Blk, true>)) != hipSuccess) return e;
     if ((e = allow_lds(down_gemm_kernel<kWFp8Row>)) != hipSuccess) return e;
     if ((e = allow_lds(down_gemm_kernel<kWFp8Blk>)) != hipSuccess) return e;
+    if ((e = allow_lds(gate_up_gemm_f8_kernel<true>)) != hipSuccess) return e;
+    if ((e = allow_lds(gate_up_gemm_f8_kernel<false>)) != hipSuccess) return e;
+    if ((e = allow_lds(down_gemm_f8_kernel<true>)) != hipSuccess) return e;
+    if ((e = allow_lds(down_gemm_f8_kernel<false>)) != hipSuccess) return e;
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(router_gemm_kernel),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)Geo<2>::kLds)) != hipSuccess)
         return e;
@@ -562,6 +930,18 @@ hipError_t gemm_kernels_init() {
 hipError_t launch_gate_up_gemm(const Plan &p) {
     const int fmax = p.f > p.fs ? p.f : p.fs;
     dim3 grid((fmax + kBN / 2 - 1) / (kBN / 2), p.max_tiles), block(kThreads);
+    if (p.aq) {
+        hipError_t e = launch_quant_groups(p.x, 1, p.d, p.N, p.d, p.xq, p.d, p.xs, p.d / 128, p.stream);
+        if (e != hipSuccess) return e;
+#define FGS_GUF(B)                                                                                            \
+    hipLaunchKernelGGL((gate_up_gemm_f8_kernel<B>), grid, block, kGemmLds, p.stream, p.xq, p.xs, p.W.w_gate,   \
+                       p.W.w_up, p.W.s_gate, p.W.s_up, p.W.ws_gate, p.W.ws_up, p.W.ss_gate, p.W.ss_up, p.tiles, \
+                       p.n_tiles, p.offsets, p.por, p.hq, p.hs, p.ldh, p.d, p.E, p.k, p.f, p.fs)
+        if (p.flags & MOE_FLAG_FP8_BLOCK128) FGS_GUF(true);
+        else FGS_GUF(false);
+#undef FGS_GUF
+        return hipGetLastError();
+    }
 #define FGS_GUG(WM, XF)                                                                                         \
     hipLaunchKernelGGL((gate_up_gemm_kernel<WM, XF>), grid, block, kGemmLds, p.stream, p.x, p.W.w_gate, p.W.w_up, \
                        p.W.s_gate, p.W.s_up, p.W.ws_gate, p.W.ws_up, p.W.ss_gate, p.W.ss_up, p.tiles, p.n_tiles,  \
@@ -577,6 +957,15 @@ hipError_t launch_gate_up_gemm(const Plan &p) {
 hipError_t launch_down_gemm(const Plan &p) {
     dim3 grid((p.d + kBN - 1) / kBN, p.max_tiles), block(kThreads);
     uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y);
+    if (p.aq) {
+#define FGS_DNF(B)                                                                                             \
+    hipLaunchKernelGGL((down_gemm_f8_kernel<B>), grid, block, kGemmLds, p.stream, p.hq, p.hs, p.ldh, p.W.w_down, \
+                       p.W.s_down, p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs)
+        if (p.flags & MOE_FLAG_FP8_BLOCK128) FGS_DNF(true);
+        else FGS_DNF(false);
+#undef FGS_DNF
+        return hipGetLastError();
+    }
 #define FGS_DNG(WM)                                                                                       \
     hipLaunchKernelGGL((down_gemm_kernel<WM>), grid, block, kGemmLds, p.stream, p.H, p.ldh, p.W.w_down, p.W.s_down, \
                        p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs)

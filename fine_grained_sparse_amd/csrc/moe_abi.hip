@@ -39,19 +39,24 @@ int check_desc(const moe_desc *d) {
         d->d_ff_shared % 64)
         return MOE_ERR_ARG;
     if ((long)d->n_tokens * d->top_k + d->n_tokens >= (1L << 31)) return MOE_ERR_ARG;
-    if (d->flags & ~(MOE_FLAG_ACCUMULATE | MOE_FLAG_RENORMALIZE | MOE_FLAG_FP8_BLOCK128)) return MOE_ERR_ARG;
+    if (d->flags & ~(MOE_FLAG_ACCUMULATE | MOE_FLAG_RENORMALIZE | MOE_FLAG_FP8_BLOCK128 | MOE_FLAG_FP8_ACT_QUANT))
+        return MOE_ERR_ARG;
     if (d->x_dtype != MOE_DTYPE_F32 && d->x_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
     if (d->w_dtype != MOE_DTYPE_BF16 && d->w_dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
     if ((d->flags & MOE_FLAG_FP8_BLOCK128) &&
         (d->w_dtype != MOE_DTYPE_FP8_E4M3 || d->d_model % 128 || d->d_ff % 128 || d->d_ff_shared % 128))
         return MOE_ERR_ARG;
+    if ((d->flags & MOE_FLAG_FP8_ACT_QUANT) &&
+        (d->w_dtype != MOE_DTYPE_FP8_E4M3 || d->x_dtype != MOE_DTYPE_BF16 || d->d_model % 128 || d->d_ff % 128 ||
+         d->d_ff_shared % 128))
+        return MOE_ERR_ARG;
     return MOE_OK;
 }
 
 struct Layout {
-    size_t partial, ids, tw, blk, offsets, tiles, n_tiles, por, rop, H, Y, w3, total;
+    size_t partial, ids, tw, blk, offsets, tiles, n_tiles, por, rop, H, Y, w3, xq, xs, hq, hs, hf, total;
     int ks, kslice, nblk, max_tiles, bm, ldh;
-    bool stream, rgemm;
+    bool stream, rgemm, aq;
 };
 
 size_t take(size_t &cur, size_t bytes) {
@@ -92,6 +97,13 @@ Layout layout_for(const moe_desc *d) {
     L.H = take(cur, rows * L.ldh * 2);
     L.Y = take(cur, rows * (size_t)d->d_model * 4);
     L.w3 = take(cur, L.rgemm ? E * 3 * (size_t)d->d_model * 2 : 0);
+    L.aq = (d->flags & MOE_FLAG_FP8_ACT_QUANT) != 0;
+    const size_t dm = d->d_model;
+    L.xq = take(cur, L.aq ? N * dm : 0);
+    L.xs = take(cur, L.aq ? N * (dm / 128) * 4 : 0);
+    L.hq = take(cur, L.aq ? rows * L.ldh : 0);
+    L.hs = take(cur, L.aq ? rows * (L.ldh / 128) * 4 : 0);
+    L.hf = take(cur, L.aq && L.stream ? rows * L.ldh * 4 : 0);
     L.total = cur;
     return L;
 }
@@ -200,6 +212,14 @@ int run_layer(const moe_desc *desc, const void *x, const float *router_w, const 
     p.w3 = (uint16_t *)(ws + L.w3);
     p.use_stream = L.stream;
     p.stream = (hipStream_t)stream;
+    p.aq = L.aq;
+    if (L.aq) {
+        p.xq = (uint8_t *)(ws + L.xq);
+        p.xs = (float *)(ws + L.xs);
+        p.hq = (uint8_t *)(ws + L.hq);
+        p.hs = (float *)(ws + L.hs);
+        p.hf = L.stream ? (float *)(ws + L.hf) : nullptr;
+    }
     if (blk) {
         // the normalised input lives after the layer's own workspace; the
         // layer reads it as x and the fused combine updates the residual
@@ -248,6 +268,20 @@ size_t moe_block_workspace_size(const moe_desc *desc) {
     if (check_desc(desc) != MOE_OK) return 0;
     const size_t xbytes = (size_t)desc->n_tokens * desc->d_model * (desc->x_dtype == MOE_DTYPE_F32 ? 4 : 2);
     return layout_for(desc).total + ((xbytes + 255) & ~size_t(255));
+}
+
+int moe_quantize_groups(const void *v, int v_dtype, int64_t rows, int32_t cols, uint8_t *q, float *scales,
+                        void *stream) {
+    if (rows < 0 || cols <= 0 || cols % 128 || rows * (int64_t)cols >= (int64_t(1) << 40)) return MOE_ERR_ARG;
+    if (v_dtype != MOE_DTYPE_F32 && v_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (rows == 0) return MOE_OK;
+    if (!v || !q || !scales || !aligned(v, 16) || !aligned(q, 8) || !aligned(scales, 4)) return MOE_ERR_ARG;
+    int st = check_device();
+    if (st != MOE_OK) return st;
+    hipError_t e = launch_quant_groups(v, v_dtype == MOE_DTYPE_BF16, cols, rows, cols, q, cols, scales, cols / 128,
+                                       (hipStream_t)stream);
+    if (e != hipSuccess) { g_last_hip_error = (int)e; return MOE_ERR_HIP; }
+    return MOE_OK;
 }
 
 int moe_block_forward(const moe_desc *desc, void *resid, const float *norm_pre, const float *norm_post, float eps,

@@ -41,6 +41,13 @@ struct Plan {
     uint16_t *w3;        // [E][3d] bf16 split of the router weights (router GEMM only)
     const float *norm_post;  // block variant: post-norm weights [d] (out = the residual row)
     float eps;
+    // 1 x 128 activation quantisation (FP8 x FP8 expert matmuls)
+    bool aq;
+    uint8_t *xq;         // [N][d] E4M3 codes of the experts' input
+    float *xs;           // [N][d/128] its group scales
+    uint8_t *hq;         // [N*k + N][ldh] E4M3 codes of the hidden activations
+    float *hs;           // [N*k + N][ldh/128] their group scales
+    float *hf;           // [N*k + N][ldh] FP32 hidden activations (stream path, before quantisation)
     bool use_stream;     // decode-shaped expert path; otherwise the grouped GEMMs
     hipStream_t stream;
 };
@@ -58,6 +65,8 @@ hipError_t launch_router_gemm(const Plan &p, uint16_t *w3);
 hipError_t launch_prenorm(const Plan &p, const void *resid, const float *g, float eps, void *xn);
 hipError_t launch_combine_block(const Plan &p);
 hipError_t gemm_kernels_init();  // once per process: raise the kernels' LDS limit
+hipError_t launch_quant_groups(const void *v, int v_bf16, int ldv, long rows, int cols, uint8_t *q, int ldq,
+                               float *s, int lds, hipStream_t stream);
 
 // Decode-shaped expert kernels keep whole weight rows in registers.
 constexpr int kStreamMaxN = 64;

@@ -25,6 +25,12 @@
 // explicitly mixed precision"): a per-output-channel scale is applied to the
 // finished dot product; with 128 x 128 block scales every 8-element partial
 // product is scaled by its own block's scale before the cross-lane sum.
+// With 1 x 128 activation quantisation (AQ) the token rows arrive as E4M3
+// codes plus one FP32 scale per 128 values; codes are exact in bf16, so the
+// same dot products run on them and each 8-element partial is multiplied by
+// its group's activation scale (times the weight block scale).  The gate/up
+// kernel then writes FP32 hidden values, which are quantised in 1 x 128
+// groups before the down kernel reads them.
 #include "moe_common.h"
 #include "moe_plan.h"
 
@@ -77,19 +83,35 @@ __device__ __forceinline__ void load_x_row(uint4 (&xv)[CPL], const void *x, int 
     }
 }
 
+// AQ token row: 8 E4M3 codes per chunk and the scale of the chunk's 128-group
+// (lanes past the row end get zero codes and a valid scale)
+template <int CPL>
+__device__ __forceinline__ void load_xq_row(uint2 (&xv)[CPL], float (&sv)[CPL], const uint8_t *xq, const float *xs,
+                                            int t, int d, int lane, int nch) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int ch = lane + 64 * i;
+        const bool ok = ch < nch;
+        xv[i] = ok ? *reinterpret_cast<const uint2 *>(xq + (size_t)t * d + (size_t)ch * 8) : make_uint2(0, 0);
+        sv[i] = xs[(size_t)t * (d / 128) + ((ok ? ch : 0) >> 4)];
+    }
+}
+
 // grid: (ceil(max(f, fs) / 8) column blocks, tile list capacity); block 256.
 // Column blocks run fastest, so the workgroups in flight together cover a few
 // experts' matrices completely (page and DRAM-row locality).  No LDS and no
 // barrier: each lane reads its slice of a token row straight from L2, with
 // the next token's row in flight while the current one is reduced.
-template <int CPL, int WM>
+// AQ: x is the E4M3 codes [N][d] with scales xs [N][d/128]; the output goes to
+// the FP32 buffer Hf instead of H.
+template <int CPL, int WM, bool AQ>
 __global__ __launch_bounds__(256) void gate_up_stream_kernel(
-    const void *__restrict__ x, int xdt, const void *__restrict__ wg, const void *__restrict__ wu,
-    const float *__restrict__ sg, const float *__restrict__ su, const void *__restrict__ wsg,
-    const void *__restrict__ wsu, const float *__restrict__ ssg, const float *__restrict__ ssu,
-    const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ por, uint16_t *__restrict__ H, int ldh, int d, int E, int k, int f, int fs,
-    int bm) {
+    const void *__restrict__ x, int xdt, const float *__restrict__ xs, const void *__restrict__ wg,
+    const void *__restrict__ wu, const float *__restrict__ sg, const float *__restrict__ su,
+    const void *__restrict__ wsg, const void *__restrict__ wsu, const float *__restrict__ ssg,
+    const float *__restrict__ ssu, const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ por, uint16_t *__restrict__ H,
+    float *__restrict__ Hf, int ldh, int d, int E, int k, int f, int fs, int bm) {
     constexpr bool FP8 = WM != kWBf16, BLK = WM == kWFp8Blk;
     const int u = blockIdx.y;
     if (u >= *n_tiles) return;
@@ -151,31 +173,44 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
     }
 
     uint4 xa[CPL], xb[CPL];
-    load_x_row<CPL>(xa, x, xdt, __shfl(tok, 0, kWave), d, lane, nch);
+    uint2 qa[CPL], qb[CPL];
+    float sa[CPL], sb[CPL];
+    if (AQ) load_xq_row<CPL>(qa, sa, (const uint8_t *)x, xs, __shfl(tok, 0, kWave), d, lane, nch);
+    else load_x_row<CPL>(xa, x, xdt, __shfl(tok, 0, kWave), d, lane, nch);
     uint4 w[4][CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) w[r][i] = chunk_bf16<FP8>(wr[r][i]);
     for (int t = 0; t < m; ++t) {
-        if (t + 1 < m) load_x_row<CPL>(xb, x, xdt, __shfl(tok, t + 1, kWave), d, lane, nch);
+        if (t + 1 < m) {
+            if (AQ) load_xq_row<CPL>(qb, sb, (const uint8_t *)x, xs, __shfl(tok, t + 1, kWave), d, lane, nch);
+            else load_x_row<CPL>(xb, x, xdt, __shfl(tok, t + 1, kWave), d, lane, nch);
+        }
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < CPL; ++i)
+        for (int i = 0; i < CPL; ++i) {
+            const uint4 xc = AQ ? chunk_bf16<true>(qa[i]) : xa[i];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                if (BLK) acc[r] = fmaf(dot8_bf16(w[r][i], xa[i], 0.f), bsc[r >> 1][i], acc[r]);
-                else acc[r] = dot8_bf16(w[r][i], xa[i], acc[r]);
+                if (AQ) acc[r] = fmaf(dot8_bf16(w[r][i], xc, 0.f), BLK ? sa[i] * bsc[r >> 1][i] : sa[i], acc[r]);
+                else if (BLK) acc[r] = fmaf(dot8_bf16(w[r][i], xc, 0.f), bsc[r >> 1][i], acc[r]);
+                else acc[r] = dot8_bf16(w[r][i], xc, acc[r]);
             }
+        }
         butterfly_reduce<4>(acc);
         // value index = 2*bit5 + bit4 of the lane: gate rows 0,1 then up rows 2,3
         const float upv = __shfl_xor(acc[0], 32, kWave);
         if ((lane & 47) == 0) {  // lanes 0 and 16
             const float hv = silu(acc[0] * gsc) * (upv * usc);
-            H[(size_t)(row0 + t) * ldh + c0 + r_out] = (uint16_t)f32_to_bf16_rne(hv);
+            if (AQ) Hf[(size_t)(row0 + t) * ldh + c0 + r_out] = hv;
+            else H[(size_t)(row0 + t) * ldh + c0 + r_out] = (uint16_t)f32_to_bf16_rne(hv);
         }
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) xa[i] = xb[i];
+        for (int i = 0; i < CPL; ++i) {
+            if (AQ) { qa[i] = qb[i]; sa[i] = sb[i]; }
+            else xa[i] = xb[i];
+        }
     }
 }
 
@@ -183,9 +218,11 @@ constexpr int kDnRW = 8;   // output rows per wave
 constexpr int kDnRB = 4 * kDnRW;  // output rows per workgroup
 
 // grid: (d / kDnRB, tile list capacity); block 256.  Needs f, fs <= 512.
-template <int WM>
+// AQ: H is the E4M3 codes [rows][ldh] (as bytes) with scales hs [rows][ldh/128].
+template <int WM, bool AQ>
 __global__ __launch_bounds__(256) void down_stream_kernel(
-    const uint16_t *__restrict__ H, int ldh, const void *__restrict__ wd, const float *__restrict__ sd,
+    const uint16_t *__restrict__ H, const float *__restrict__ hs, int ldh, const void *__restrict__ wd,
+    const float *__restrict__ sd,
     const void *__restrict__ wsd, const float *__restrict__ ssd, const int32_t *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets, float *__restrict__ Y, int d, int E,
     int f, int fs, int bm) {
@@ -220,22 +257,42 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
 
     const int row0 = offsets[g] + m0, m = min(bm, offsets[g + 1] - row0);
     const uint16_t *hp = H + (size_t)row0 * ldh + (size_t)(ok ? lane : 0) * 8;
-    uint4 ha = ok ? *reinterpret_cast<const uint4 *>(hp) : make_uint4(0, 0, 0, 0);
+    const uint8_t *qp = (const uint8_t *)H + (size_t)row0 * ldh + (size_t)(ok ? lane : 0) * 8;
+    const float *sp = AQ ? hs + (size_t)row0 * (ldh / 128) + ((ok ? lane : 0) >> 4) : nullptr;
+    uint4 ha = make_uint4(0, 0, 0, 0);
+    float hsa = 0.f;
+    if (AQ) {
+        if (ok) ha = chunk_bf16<true>(*reinterpret_cast<const uint2 *>(qp));
+        hsa = sp[0];
+    } else if (ok) {
+        ha = *reinterpret_cast<const uint4 *>(hp);
+    }
     uint4 w[kDnRW];
 #pragma unroll
     for (int r = 0; r < kDnRW; ++r) w[r] = chunk_bf16<FP8>(wr[r]);
     for (int t = 0; t < m; ++t) {
         uint4 hb = make_uint4(0, 0, 0, 0);
-        if (t + 1 < m && ok) hb = *reinterpret_cast<const uint4 *>(hp + (size_t)(t + 1) * ldh);
+        uint2 hqb = make_uint2(0, 0);
+        float hsb = 0.f;
+        if (t + 1 < m) {
+            if (AQ) {
+                if (ok) hqb = *reinterpret_cast<const uint2 *>(qp + (size_t)(t + 1) * ldh);
+                hsb = sp[(size_t)(t + 1) * (ldh / 128)];
+            } else if (ok) {
+                hb = *reinterpret_cast<const uint4 *>(hp + (size_t)(t + 1) * ldh);
+            }
+        }
+        const float psc = AQ ? (BLK ? hsa * lsc : hsa) : lsc;
         float p[kDnRW];
 #pragma unroll
         for (int r = 0; r < kDnRW; ++r) {
             p[r] = dot8_bf16(w[r], ha, 0.f);
-            if (BLK) p[r] *= lsc;
+            if (AQ || BLK) p[r] *= psc;
         }
         butterfly_reduce<kDnRW>(p);
         if ((lane & (64 / kDnRW - 1)) == 0) Y[(size_t)(row0 + t) * d + o0 + myrow] = p[0] * scl;
-        ha = hb;
+        if (AQ) { ha = chunk_bf16<true>(hqb); hsa = hsb; }
+        else ha = hb;
     }
 }
 
@@ -245,15 +302,20 @@ hipError_t launch_gate_up(const Plan &p) {
     const size_t lds = 0;
     const int cpl = (p.d / 8 + 63) / 64;
     const int wm = p.wdt != MOE_DTYPE_FP8_E4M3 ? kWBf16 : (p.flags & MOE_FLAG_FP8_BLOCK128) ? kWFp8Blk : kWFp8Row;
-#define FGS_GU(C, WM)                                                                                          \
-    hipLaunchKernelGGL((gate_up_stream_kernel<C, WM>), grid, block, lds, p.stream, p.x, p.xdt, p.W.w_gate,    \
-                       p.W.w_up, p.W.s_gate, p.W.s_up, p.W.ws_gate, p.W.ws_up, p.W.ss_gate, p.W.ss_up, p.tiles, \
-                       p.n_tiles, p.offsets, p.por, p.H, p.ldh, p.d, p.E, p.k, p.f, p.fs, p.bm)
-#define FGS_GU_C(C)                                        \
-    do {                                                   \
-        if (wm == kWFp8Blk) FGS_GU(C, kWFp8Blk);           \
-        else if (wm == kWFp8Row) FGS_GU(C, kWFp8Row);      \
-        else FGS_GU(C, kWBf16);                            \
+    if (p.aq) {  // the experts' input in 1 x 128 groups
+        hipError_t e = launch_quant_groups(p.x, 1, p.d, p.N, p.d, p.xq, p.d, p.xs, p.d / 128, p.stream);
+        if (e != hipSuccess) return e;
+    }
+    const void *xin = p.aq ? (const void *)p.xq : p.x;
+#define FGS_GU(C, WM, AQ)                                                                                        \
+    hipLaunchKernelGGL((gate_up_stream_kernel<C, WM, AQ>), grid, block, lds, p.stream, xin, p.xdt, p.xs,        \
+                       p.W.w_gate, p.W.w_up, p.W.s_gate, p.W.s_up, p.W.ws_gate, p.W.ws_up, p.W.ss_gate, p.W.ss_up, \
+                       p.tiles, p.n_tiles, p.offsets, p.por, p.H, p.hf, p.ldh, p.d, p.E, p.k, p.f, p.fs, p.bm)
+#define FGS_GU_C(C)                                                                  \
+    do {                                                                             \
+        if (wm == kWFp8Blk) { if (p.aq) FGS_GU(C, kWFp8Blk, true); else FGS_GU(C, kWFp8Blk, false); } \
+        else if (wm == kWFp8Row) { if (p.aq) FGS_GU(C, kWFp8Row, true); else FGS_GU(C, kWFp8Row, false); } \
+        else FGS_GU(C, kWBf16, false);                                               \
     } while (0)
     switch (cpl) {
         case 1: FGS_GU_C(1); break;
@@ -273,12 +335,19 @@ hipError_t launch_gate_up(const Plan &p) {
 
 hipError_t launch_down(const Plan &p) {
     dim3 grid(p.d / kDnRB, p.max_tiles), block(256);
-#define FGS_DN(WM)                                                                                           \
-    hipLaunchKernelGGL((down_stream_kernel<WM>), grid, block, 0, p.stream, p.H, p.ldh, p.W.w_down, p.W.s_down, \
-                       p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, p.Y, p.d, p.E, p.f, p.fs, p.bm)
-    if (p.wdt != MOE_DTYPE_FP8_E4M3) FGS_DN(kWBf16);
-    else if (p.flags & MOE_FLAG_FP8_BLOCK128) FGS_DN(kWFp8Blk);
-    else FGS_DN(kWFp8Row);
+    const long rows = (long)p.N * p.k + p.N;
+    if (p.aq) {  // hidden activations in 1 x 128 groups (every row of H, routed and shared)
+        hipError_t e = launch_quant_groups(p.hf, 0, p.ldh, rows, p.ldh, p.hq, p.ldh, p.hs, p.ldh / 128, p.stream);
+        if (e != hipSuccess) return e;
+    }
+    const uint16_t *hin = p.aq ? (const uint16_t *)p.hq : p.H;
+#define FGS_DN(WM, AQ)                                                                                         \
+    hipLaunchKernelGGL((down_stream_kernel<WM, AQ>), grid, block, 0, p.stream, hin, p.hs, p.ldh, p.W.w_down,    \
+                       p.W.s_down, p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, p.Y, p.d, p.E, p.f, \
+                       p.fs, p.bm)
+    if (p.wdt != MOE_DTYPE_FP8_E4M3) FGS_DN(kWBf16, false);
+    else if (p.flags & MOE_FLAG_FP8_BLOCK128) { if (p.aq) FGS_DN(kWFp8Blk, true); else FGS_DN(kWFp8Blk, false); }
+    else { if (p.aq) FGS_DN(kWFp8Row, true); else FGS_DN(kWFp8Row, false); }
 #undef FGS_DN
     return hipGetLastError();
 }

@@ -85,6 +85,14 @@ extern "C" {
                                            Requires w_dtype FP8_E4M3 and d_model, d_ff,
                                            d_ff_shared multiples of 128 (else MOE_ERR_ARG). */
 
+#define MOE_FLAG_FP8_ACT_QUANT (1u << 3) /* FP8 x FP8 expert matmuls: the experts' input x and each
+                                           expert's hidden activations are quantised on the fly in
+                                           1 x 128 groups (moe_quantize_groups) and multiplied on the
+                                           FP8 matrix cores; same page and section.  The router
+                                           still reads x unquantised.  Requires w_dtype FP8_E4M3,
+                                           x_dtype BF16 and d_model, d_ff, d_ff_shared multiples
+                                           of 128 (else MOE_ERR_ARG). */
+
 /* pipeline stages, for optional timing events */
 #define MOE_STAGE_ROUTER    0   /* router logits */
 #define MOE_STAGE_TOPK      1   /* bias-corrected top-k, sigmoid weights */
@@ -192,6 +200,22 @@ int moe_block_forward(const moe_desc *desc, void *resid, const float *norm_pre, 
                       float eps, const float *router_w, const float *router_bias,
                       const moe_weights *weights, void *workspace, size_t workspace_bytes,
                       const moe_aux *aux, void *stream);
+
+/* Dynamic FP8 quantisation in 1 x 128 groups, the activation format of
+ * MOE_FLAG_FP8_ACT_QUANT ("Inside Kolibri 1", section "The FP8 path is
+ * explicitly mixed precision": activations quantised dynamically in groups
+ * of 1 x 128).  For each row r and group g of 128 consecutive columns:
+ *   scale[r][g] = amax / 448 in FP32 (1 if the group is all zero),
+ *   q[r][c]     = E4M3FN(v[r][c] / scale) with IEEE FP32 division, clamped to
+ *                 +-448, rounded to nearest even.
+ *   v       [rows][cols] v_dtype (MOE_DTYPE_F32 or MOE_DTYPE_BF16), row-major,
+ *           16-byte aligned; cols a positive multiple of 128
+ *   q       [rows][cols] uint8 codes, 8-byte aligned
+ *   scales  [rows][cols/128] FP32, 4-byte aligned
+ * rows == 0 is a no-op.  Device pointers owned by the caller; enqueued on
+ * `stream`.  Returns MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED or MOE_ERR_HIP. */
+int moe_quantize_groups(const void *v, int v_dtype, int64_t rows, int32_t cols, uint8_t *q, float *scales,
+                        void *stream);
 
 /* Static text for a status code. */
 const char *moe_status_string(int status);

@@ -432,7 +432,7 @@ def rms_norm(v64: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
 
 def block_forward(inp: Dict[str, np.ndarray], resid: np.ndarray, g_pre: np.ndarray, g_post: np.ndarray,
                   eps: float, top_k: int, w_dtype: str, x_dtype: str,
-                  renormalize: bool = False) -> Dict[str, np.ndarray]:
+                  renormalize: bool = False, act_quant: bool = False) -> Dict[str, np.ndarray]:
     """The MoE sublayer of a sandwich-normalised block, residual stream updated.
 
     "Inside Kolibri 1" (flozi.net), section "The released stack": RMSNorm
@@ -444,7 +444,7 @@ def block_forward(inp: Dict[str, np.ndarray], resid: np.ndarray, g_pre: np.ndarr
     r64 = _x_to_f64(resid)
     xn = rms_norm(r64, g_pre, eps)
     xs = round_to_bf16_bits(xn) if x_dtype == "bf16" else xn.astype(np.float32)
-    res = moe_forward(dict(inp, x=xs), top_k, w_dtype, x_dtype, renormalize=renormalize)
+    res = moe_forward(dict(inp, x=xs), top_k, w_dtype, x_dtype, renormalize=renormalize, act_quant=act_quant)
     z = rms_norm(res["out64"], g_post, eps)
     out64 = r64 + z
     out = round_to_bf16_bits(out64) if x_dtype == "bf16" else out64.astype(np.float32)

@@ -33,7 +33,7 @@ def to_device(inputs: Dict[str, torch.Tensor], device="cuda") -> Dict[str, torch
 
 
 def run_gpu(cfg: LayerConfig, dev_inputs: Dict[str, torch.Tensor], residual: Optional[torch.Tensor] = None,
-            n_tokens: Optional[int] = None, renormalize: bool = False) -> Dict[str, np.ndarray]:
+            n_tokens: Optional[int] = None, renormalize: bool = False, act_quant: bool = False) -> Dict[str, np.ndarray]:
     """One moe_forward call with every optional output requested."""
     x = dev_inputs["x"]
     n = x.shape[0] if n_tokens is None else n_tokens
@@ -42,10 +42,10 @@ def run_gpu(cfg: LayerConfig, dev_inputs: Dict[str, torch.Tensor], residual: Opt
     aux = B.aux_struct(bufs)
     if residual is not None:
         out = residual.clone()
-        layer.forward(x, out=out, accumulate=True, aux=aux, renormalize=renormalize)
+        layer.forward(x, out=out, accumulate=True, aux=aux, renormalize=renormalize, act_quant=act_quant)
     else:
         out = torch.full_like(x, float("nan"))
-        layer.forward(x, out=out, aux=aux, renormalize=renormalize)
+        layer.forward(x, out=out, aux=aux, renormalize=renormalize, act_quant=act_quant)
     torch.cuda.synchronize()
     res = {k: v.cpu().numpy() for k, v in bufs.items()}
     res["out"] = out.float().cpu().numpy().astype(np.float64)
@@ -108,15 +108,18 @@ def check_output(cfg: LayerConfig, gpu_out: np.ndarray, ref_out: np.ndarray, tok
 
 
 def full_check(cfg: LayerConfig, host_inputs: Dict[str, torch.Tensor], g: Dict[str, np.ndarray],
-               residual: Optional[np.ndarray] = None, renormalize: bool = False) -> Dict[str, float]:
+               residual: Optional[np.ndarray] = None, renormalize: bool = False,
+               act_quant: bool = False) -> Dict[str, float]:
     """Whole-layer oracle on every token (small and decode-sized cases)."""
     npi = to_numpy(host_inputs)
-    ref = O.moe_forward(npi, cfg.top_k, cfg.w_dtype, cfg.x_dtype, residual=residual, renormalize=renormalize)
+    ref = O.moe_forward(npi, cfg.top_k, cfg.w_dtype, cfg.x_dtype, residual=residual, renormalize=renormalize,
+                        act_quant=act_quant)
     stats = check_routing(cfg, g, ref, renormalize)
     ref_out = ref["out64"].copy()
     diff = np.nonzero(np.any(g["topk_ids"] != ref["ids"], axis=1))[0]
     if diff.size:
-        alt = O.token_outputs(npi, diff, cfg.top_k, cfg.w_dtype, ids=g["topk_ids"], renormalize=renormalize)["out64"]
+        alt = O.token_outputs(npi, diff, cfg.top_k, cfg.w_dtype, ids=g["topk_ids"], renormalize=renormalize,
+                              act_quant=act_quant)["out64"]
         if residual is not None:
             alt = alt + (O.decode_bf16(residual[diff]) if residual.dtype == np.uint16 else residual[diff])
         ref_out[diff] = alt
@@ -125,13 +128,13 @@ def full_check(cfg: LayerConfig, host_inputs: Dict[str, torch.Tensor], g: Dict[s
 
 
 def sampled_check(cfg: LayerConfig, host_inputs: Dict[str, torch.Tensor], g: Dict[str, np.ndarray],
-                  n_sample: int = 24, seed: int = 0) -> Dict[str, float]:
+                  n_sample: int = 24, seed: int = 0, act_quant: bool = False) -> Dict[str, float]:
     """Full-size cases: routing of every token, output of sampled tokens."""
     npi = to_numpy(host_inputs)
     n = g["topk_ids"].shape[0]
     rng = np.random.default_rng(seed)
     toks = np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=min(n, n_sample), replace=False)]))
-    part = O.token_outputs(npi, toks, cfg.top_k, cfg.w_dtype, ids=g["topk_ids"])
+    part = O.token_outputs(npi, toks, cfg.top_k, cfg.w_dtype, ids=g["topk_ids"], act_quant=act_quant)
     x64 = O.decode_bf16(npi["x"]) if npi["x"].dtype == np.uint16 else npi["x"].astype(np.float64)
     h32 = part["logits"]
     _, gap, s = O.select_topk(h32, npi["router_b"], cfg.top_k)
@@ -144,7 +147,7 @@ def sampled_check(cfg: LayerConfig, host_inputs: Dict[str, torch.Tensor], g: Dic
 
 
 def block_run_and_check(cfg: LayerConfig, host_inputs: Dict[str, torch.Tensor], seed: int = 0,
-                        renormalize: bool = False, eps: float = 1e-6) -> Dict[str, float]:
+                        renormalize: bool = False, eps: float = 1e-6, act_quant: bool = False) -> Dict[str, float]:
     """moe_block_forward (sandwich norms, residual in place) against oracle.block_forward."""
     g = torch.Generator().manual_seed(seed + 7)
     n, d = host_inputs["x"].shape
@@ -156,17 +159,18 @@ def block_run_and_check(cfg: LayerConfig, host_inputs: Dict[str, torch.Tensor], 
     layer = B.MoeLayer(cfg.top_k, dev, max(n, 1), xdt)
     bufs = B.route_outputs(n, cfg.n_experts, cfg.top_k, "cuda")
     r_dev = resid.cuda()
-    layer.block_forward(r_dev, g_pre.cuda(), g_post.cuda(), eps, aux=B.aux_struct(bufs), renormalize=renormalize)
+    layer.block_forward(r_dev, g_pre.cuda(), g_post.cuda(), eps, aux=B.aux_struct(bufs), renormalize=renormalize,
+                        act_quant=act_quant)
     torch.cuda.synchronize()
     gout = {k: v.cpu().numpy() for k, v in bufs.items()}
     # the normalised input the layer read: stored after the layer's own workspace
-    off = B.workspace_size(layer.desc(n))
+    off = B.workspace_size(layer.desc(n, B.MOE_FLAG_FP8_ACT_QUANT if act_quant else 0))
     nbytes = n * d * (2 if xdt == torch.bfloat16 else 4)
     xn_gpu = layer.workspace[off:off + nbytes].cpu().view(xdt).reshape(n, d).float().numpy().astype(np.float64)
     npi = to_numpy(host_inputs)
     r_np = resid.view(torch.int16).numpy().view(np.uint16) if xdt == torch.bfloat16 else resid.numpy()
     ref = O.block_forward(npi, r_np, g_pre.numpy(), g_post.numpy(), eps, cfg.top_k, cfg.w_dtype, cfg.x_dtype,
-                          renormalize=renormalize)
+                          renormalize=renormalize, act_quant=act_quant)
     xn_ref = O.decode_bf16(ref["x_norm"]) if xdt == torch.bfloat16 else ref["x_norm"].astype(np.float64)
     # The normalised input is rounded to the activation type; where the FP32
     # value lies next to a rounding boundary, FP32 summation order can flip the

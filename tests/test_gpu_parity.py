@@ -24,10 +24,10 @@ def _need_gpu():
     binding.lib()  # raises if the library is missing
 
 
-def _run_full(cfg, seed=0, residual=False, renormalize=False):
+def _run_full(cfg, seed=0, residual=False, renormalize=False, act_quant=False):
     _say(f"case {cfg.name} N={cfg.n_tokens} d={cfg.d_model} E={cfg.n_experts} k={cfg.top_k} "
          f"f={cfg.d_ff} fs={cfg.d_ff_shared} x={cfg.x_dtype} w={cfg.w_dtype} blk={cfg.scale_block} seed={seed} "
-         f"residual={residual} renorm={renormalize}")
+         f"residual={residual} renorm={renormalize} act_quant={act_quant}")
     host = generate(cfg, seed=seed)
     dev = PA.to_device(host)
     res_t = res_np = None
@@ -36,8 +36,8 @@ def _run_full(cfg, seed=0, residual=False, renormalize=False):
         r = torch.randn(host["x"].shape, generator=g).to(host["x"].dtype)
         res_t = r.cuda()
         res_np = r.view(torch.int16).numpy().view(np.uint16) if r.dtype == torch.bfloat16 else r.numpy()
-    g = PA.run_gpu(cfg, dev, residual=res_t, renormalize=renormalize)
-    stats = PA.full_check(cfg, host, g, residual=res_np, renormalize=renormalize)
+    g = PA.run_gpu(cfg, dev, residual=res_t, renormalize=renormalize, act_quant=act_quant)
+    stats = PA.full_check(cfg, host, g, residual=res_np, renormalize=renormalize, act_quant=act_quant)
     _say(f"  -> {stats}")
     return stats
 
@@ -95,6 +95,60 @@ def test_decode_fp8_block_scales(n):
     _run_full(get_config("fp8block", n_tokens=n))
 
 
+@pytest.mark.parametrize("dtype,rows,cols", [("bf16", 1, 128), ("bf16", 37, 2560), ("f32", 300, 512),
+                                             ("f32", 5, 384), ("bf16", 4096, 2560)])
+def test_quantize_groups_bit_exact(dtype, rows, cols):
+    """moe_quantize_groups: codes and scales bit-identical to the oracle's 1 x 128 quantiser."""
+    from fine_grained_sparse_amd import binding as B
+    from oracle import moe_oracle as O
+    _say(f"case quantize {dtype} rows={rows} cols={cols}")
+    g = torch.Generator().manual_seed(rows * 7 + cols)
+    v = torch.randn(rows, cols, generator=g) * torch.exp2(torch.randint(-30, 30, (rows, 1), generator=g).float())
+    v[0, :128] = 0.0                          # an all-zero group
+    if rows > 2:
+        v[1, 3] = -0.0                        # negative zero inside a non-zero group
+        table = O.decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))
+        mids = (table[:-1] + table[1:]) / 2   # exact ties once the scale is 1
+        v[2, :128] = 0.0
+        v[2, 0] = 448.0
+        v[2, 1:127] = torch.from_numpy(np.concatenate([mids[:63], -mids[63:126]]))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    v = v.to(tdt)
+    q, sc = B.quantize_groups(v.cuda())
+    torch.cuda.synchronize()
+    rq, rs = O.quantize_groups(v.float().numpy())
+    assert np.array_equal(sc.cpu().numpy(), rs), "scales differ"
+    qg = q.cpu().numpy()
+    bad = np.argwhere(qg != rq)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:5].tolist()}: {qg[tuple(bad[0])]} vs {rq[tuple(bad[0])]}"
+
+
+@pytest.mark.parametrize("over", [
+    dict(n_tokens=16), dict(n_tokens=128), dict(n_tokens=600), dict(n_tokens=16, scale_block=0),
+    dict(n_tokens=200, scale_block=0), dict(n_tokens=9, d_model=384, d_ff=256, d_ff_shared=128),
+    dict(n_tokens=200, d_model=384, d_ff=256, d_ff_shared=128),
+])
+def test_fp8_act_quant_toy(over):
+    """1 x 128 activation quantisation with FP8 x FP8 matmuls (MOE_FLAG_FP8_ACT_QUANT): stream and
+    GEMM paths, block and per-channel weight scales, odd block counts, f != f_s."""
+    base = dict(x_dtype="bf16", w_dtype="fp8", scale_block=128, d_ff=128, d_ff_shared=128)
+    base.update(over)
+    _run_full(get_config("toy", **base), act_quant=True)
+
+
+@pytest.mark.parametrize("name,n", [("fp8block", 32), ("fp8", 48)])
+def test_decode_act_quant(name, n):
+    _run_full(get_config(name, n_tokens=n), act_quant=True)
+
+
+def test_block_act_quant():
+    """Sandwich-norm block with 1 x 128 activation quantisation."""
+    cfg = get_config("fp8block", n_tokens=150)
+    _say(f"case block act_quant {cfg.name} N={cfg.n_tokens}")
+    stats = PA.block_run_and_check(cfg, generate(cfg, seed=3), seed=3, act_quant=True)
+    _say(f"  -> {stats}")
+
+
 @pytest.mark.parametrize("n", [16, 200])
 def test_128_experts(n):
     """The 128-expert shape of the predecessor model, top-6, full hidden size."""
@@ -133,14 +187,15 @@ def test_zero_tokens_is_noop():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("name", ["prefill", "fp8", "fp8block", "zipf"])
-def test_full_size_sampled(name):
+@pytest.mark.parametrize("name,aq", [("prefill", False), ("fp8", False), ("fp8block", False), ("zipf", False),
+                                     ("fp8block", True), ("zipf", True)])
+def test_full_size_sampled(name, aq):
     """Full-size workloads: routing and layout of every token, output of a sample."""
     cfg = get_config(name)
-    _say(f"case {name} N={cfg.n_tokens} w={cfg.w_dtype} bias={cfg.bias_kind} (sampled outputs)")
+    _say(f"case {name} N={cfg.n_tokens} w={cfg.w_dtype} bias={cfg.bias_kind} act_quant={aq} (sampled outputs)")
     host = generate(cfg, seed=0)
-    g = PA.run_gpu(cfg, PA.to_device(host))
-    stats = PA.sampled_check(cfg, host, g, n_sample=24)
+    g = PA.run_gpu(cfg, PA.to_device(host), act_quant=aq)
+    stats = PA.sampled_check(cfg, host, g, n_sample=24, act_quant=aq)
     counts = np.diff(g["expert_offsets"])
     stats["empty_experts"] = int((counts == 0).sum())
     stats["max_expert_rows"] = int(counts.max())
