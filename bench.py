@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "fp8", "fp8block", "zipf", "toy"])
     ap.add_argument("--tokens", type=int, default=None, help="override the batch size")
     ap.add_argument("--layers", type=int, default=4, help="independent layer instances cycled by the steps")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the same steps replayed from a captured HIP graph")
     ap.add_argument("--act-quant", action="store_true",
                     help="FP8 x FP8 expert matmuls on 1 x 128 quantised activations (FP8 weights only)")
     ap.add_argument("--variant", default="plain", choices=["plain", "renorm", "block"],
@@ -190,23 +192,24 @@ def main():
     aux_timed = [B.MoeAux(None, None, None, None, None, None, None, ctypes.cast(a, ctypes.c_void_p))
                  for a in ev_arrays]
 
-    def step(i, aux=None):
+    def step(i, aux=None, strm=None):
         li = i % L
         m = mods[li]
+        strm = stream if strm is None else strm
         if args.variant == "block":
             # the layer instance's token batch is its residual stream, updated in place
             st = B.lib().moe_block_forward(ctypes.byref(descs[li]), layers[li]["x"].data_ptr(),
                                            norms[li][0].data_ptr(), norms[li][1].data_ptr(), 1e-6,
                                            layers[li]["router_w"].data_ptr(), layers[li]["router_b"].data_ptr(),
                                            ctypes.byref(m.weights), ws.data_ptr(), ws.numel(),
-                                           ctypes.byref(aux) if aux is not None else None, stream)
+                                           ctypes.byref(aux) if aux is not None else None, strm)
             if st != B.MOE_OK:
                 raise B.MoeError(st, "moe_block_forward")
             return
         st = B.lib().moe_forward(ctypes.byref(descs[li]), layers[li]["x"].data_ptr(),
                                  layers[li]["router_w"].data_ptr(), layers[li]["router_b"].data_ptr(),
                                  ctypes.byref(m.weights), outs[li].data_ptr(), ws.data_ptr(), ws.numel(),
-                                 ctypes.byref(aux) if aux is not None else None, stream)
+                                 ctypes.byref(aux) if aux is not None else None, strm)
         if st != B.MOE_OK:
             raise B.MoeError(st, "moe_forward")
 
@@ -215,6 +218,7 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
 
+    cur = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -223,6 +227,44 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     value = N * args.steps / elapsed
+
+    # distribution of single steps: a second pass with an event pair around every step
+    # (kept out of the timed loop above, where the extra events would cost time)
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step_ev[i][0].record(cur)
+        step(i)
+        step_ev[i][1].record(cur)
+    torch.cuda.synchronize()
+    step_us = np.array([a.elapsed_time(b) * 1e3 for a, b in step_ev])
+    step_stats = {"p10": round(float(np.percentile(step_us, 10)), 2), "median": round(float(np.median(step_us)), 2),
+                  "p90": round(float(np.percentile(step_us, 90)), 2), "pass": "separate, one event pair per step"}
+
+    # the same steps replayed from a HIP graph (one graph holds one step of every layer instance)
+    graph = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            for i in range(L):   # warm the capture stream
+                step(i, None, side.cuda_stream)
+        cur.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream(dev).cuda_stream
+            for i in range(L):
+                step(i, None, cs)
+        reps = max(1, args.steps // L)
+        g.replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        gms = (time.perf_counter() - tg) * 1e3 / (reps * L)
+        graph = {"ms_per_step": round(gms, 5), "tokens_per_s": round(N / gms * 1e3, 1), "replays": reps,
+                 "steps_per_replay": L}
 
     # per-launch durations of the expert kernels from the library's events
     gu_ms = [hip.elapsed_ms(ev_handles[i][2 * STAGE_GU], ev_handles[i][2 * STAGE_GU + 1]) for i in range(args.steps)]
@@ -312,7 +354,10 @@ def main():
                    "n_tokens": N, "layers_cycled": L, "touched_experts": touched, "expert_path": kind,
                    "variant": args.variant, "act_quant": bool(args.act_quant)},
         "roofline": roofline,
+        "step_us": step_stats,
     }
+    if graph is not None:
+        result["graph_replay"] = graph
 
     if not args.no_cpu_baseline and args.variant == "plain" and not args.act_quant:
         result["cpu_baseline"], result["parity_step0"] = cpu_baseline(cfg, layers[0], outs, mods, descs, ws, stream,

@@ -176,6 +176,38 @@ def test_deterministic():
         assert np.array_equal(a[key], b[key], equal_nan=True), key
 
 
+@pytest.mark.parametrize("cfg_name,over,aq", [("decode", dict(n_tokens=32), False), ("toy", dict(n_tokens=300), False),
+                                             ("fp8block", dict(n_tokens=200), True)])
+def test_graph_replay_matches_eager(cfg_name, over, aq):
+    """moe_forward captured in a HIP graph: every replay equals the eager result bit for bit,
+    with eager work on the same buffers between replays."""
+    from fine_grained_sparse_amd import binding as B
+    cfg = get_config(cfg_name, **over)
+    _say(f"case graph {cfg.name} N={cfg.n_tokens} act_quant={aq}")
+    dev = PA.to_device(generate(cfg, seed=6))
+    x = dev["x"]
+    layer = B.MoeLayer(cfg.top_k, dev, x.shape[0], x.dtype)
+    ref = torch.empty_like(x)
+    layer.forward(x, out=ref, act_quant=aq)
+    out = torch.empty_like(x)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.forward(x, out=out, act_quant=aq)   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x, out=out, act_quant=aq)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        layer.forward(x[: max(1, x.shape[0] // 2)], act_quant=aq)   # eager work that reuses the workspace
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out.view(torch.int32),
+                           ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref.view(torch.int32)), rep
+
+
 def test_zero_tokens_is_noop():
     from fine_grained_sparse_amd import binding as B
     cfg = get_config("toy")
