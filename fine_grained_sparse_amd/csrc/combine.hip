@@ -27,23 +27,30 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const void *__restrict__ Y, const float *__restrict__ tw, const int32_t *__restrict__ rop, void *out,
     int N, int d, int k, bool accumulate) {
     const int t = blockIdx.x;
-    __shared__ float ws[8];
-    __shared__ int rs[8];
-    if (threadIdx.x < k) {
-        ws[threadIdx.x] = tw[(size_t)t * k + threadIdx.x];
-        rs[threadIdx.x] = rop[(size_t)t * k + threadIdx.x];
+    // the token's k <= 8 rows and weights: uniform addresses, so scalar loads
+    // (slots past k repeat slot k-1 and are not added)
+    int rs[8];
+    float ws[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int jj = j < k ? j : k - 1;
+        rs[j] = rop[(size_t)t * k + jj];
+        ws[j] = tw[(size_t)t * k + jj];
     }
-    __syncthreads();
     const size_t shared_row = (size_t)N * k + t;
     for (int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4; c < d; c += gridDim.y * blockDim.x * 4) {
+        // all rows are requested at once, then added in slot order
         float4 a = load_y4<YBF16>(Y, shared_row * d + c);
-        for (int j = 0; j < k; ++j) {
-            const float wj = ws[j];
-            const float4 y = load_y4<YBF16>(Y, (size_t)rs[j] * d + c);
-            a.x = fmaf(wj, y.x, a.x);
-            a.y = fmaf(wj, y.y, a.y);
-            a.z = fmaf(wj, y.z, a.z);
-            a.w = fmaf(wj, y.w, a.w);
+        float4 y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = load_y4<YBF16>(Y, (size_t)rs[j] * d + c);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {   // per-value selects, not branches: the loads stay ahead of every use
+            const bool on = j < k;
+            a.x = on ? fmaf(ws[j], y[j].x, a.x) : a.x;
+            a.y = on ? fmaf(ws[j], y[j].y, a.y) : a.y;
+            a.z = on ? fmaf(ws[j], y[j].z, a.z) : a.z;
+            a.w = on ? fmaf(ws[j], y[j].w, a.w) : a.w;
         }
         if (BF16OUT) {
             uint2 *o = reinterpret_cast<uint2 *>((uint16_t *)out + (size_t)t * d + c);

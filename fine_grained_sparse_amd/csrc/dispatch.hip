@@ -101,27 +101,37 @@ __device__ void offsets_and_tiles(const int *cnt, int *off, int *ntile, int *wsu
     if (tid == 0) *n_tiles = nt;
 }
 
+// The k <= 8 expert ids of token t in registers: all loads issued at once
+// (slots past k repeat slot k-1; a thread without a token reads token 0).
+__device__ __forceinline__ void load_token_ids(const int32_t *ids, int t, int k, bool live, int (&e)[8]) {
+    const int32_t *p = ids + (size_t)(live ? t : 0) * k;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = p[j < k ? j : k - 1];
+}
+
 // Rank of every pair of one block inside its expert, then the scatter.
-__device__ void block_scatter(const int32_t *ids, uint32_t *bits, const int *base, int b, int N, int k, int E,
+// `e` holds the ids of this thread's token (block b, token b*kBT + tid).
+__device__ void block_scatter(const int (&e)[8], uint32_t *bits, const int *base, int b, int N, int k, int E,
                               int32_t *por, int32_t *rop) {
     const int tid = threadIdx.x;
     for (int i = tid; i < E * kBTW; i += blockDim.x) bits[i] = 0;
     __syncthreads();
     const int t = b * kBT + tid;
     const bool live = tid < kBT && t < N;
-    if (live)
-        for (int j = 0; j < k; ++j) {
-            int e = ids[(size_t)t * k + j];
-            atomicOr(&bits[e * kBTW + (tid >> 5)], 1u << (tid & 31));
-        }
+    if (live) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < k) atomicOr(&bits[e[j] * kBTW + (tid >> 5)], 1u << (tid & 31));
+    }
     __syncthreads();
     if (live)
-        for (int j = 0; j < k; ++j) {
-            int e = ids[(size_t)t * k + j];
-            const uint32_t *row = bits + e * kBTW;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j >= k) break;
+            const uint32_t *row = bits + e[j] * kBTW;
             int rank = __popc(row[tid >> 5] & ((1u << (tid & 31)) - 1u));
             for (int w = 0; w < (tid >> 5); ++w) rank += __popc(row[w]);
-            int pos = base[e] + rank;
+            int pos = base[e[j]] + rank;
             por[pos] = t * k + j;
             rop[(size_t)t * k + j] = pos;
         }
@@ -138,13 +148,20 @@ __global__ __launch_bounds__(1024) void dispatch_fused_kernel(
     __shared__ int wsum[17];
     __shared__ uint32_t bits[1024 * kBTW];
     const int tid = threadIdx.x;
+    const bool live = tid < N;   // N <= kBT
+    int my[8];
+    load_token_ids(ids, tid, k, live, my);
     for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
     __syncthreads();
-    for (int i = tid; i < N * k; i += blockDim.x) atomicAdd(&cnt[ids[i]], 1);
+    if (live) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < k) atomicAdd(&cnt[my[j]], 1);
+    }
     __syncthreads();
     offsets_and_tiles(cnt, off, ntile, wsum, N, k, E, bm, g_offsets, g_exp_off, tiles, n_tiles);
     __syncthreads();
-    block_scatter(ids, bits, off, 0, N, k, E, por, rop);
+    block_scatter(my, bits, off, 0, N, k, E, por, rop);
 }
 
 // ---- multi-block path
@@ -153,11 +170,16 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t *__res
                                                             int32_t *__restrict__ blk) {
     __shared__ int cnt[1024];
     const int tid = threadIdx.x, b = blockIdx.x;
+    const int t = b * kBT + tid;
+    int my[8];
+    load_token_ids(ids, t, k, t < N, my);
     for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
     __syncthreads();
-    const int t = b * kBT + tid;
-    if (t < N)
-        for (int j = 0; j < k; ++j) atomicAdd(&cnt[ids[(size_t)t * k + j]], 1);
+    if (t < N) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < k) atomicAdd(&cnt[my[j]], 1);
+    }
     __syncthreads();
     for (int e = tid; e < E; e += blockDim.x) blk[(size_t)b * E + e] = cnt[e];
 }
@@ -190,7 +212,10 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t *blk, int n
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t *__restrict__ ids, const int32_t *blk,
                                                                int N, int k, int E, int32_t *por, int32_t *rop) {
     __shared__ uint32_t bits[1024 * kBTW];
-    block_scatter(ids, bits, blk + (size_t)blockIdx.x * E, blockIdx.x, N, k, E, por, rop);
+    const int t = blockIdx.x * kBT + threadIdx.x;
+    int my[8];
+    load_token_ids(ids, t, k, t < N, my);
+    block_scatter(my, bits, blk + (size_t)blockIdx.x * E, blockIdx.x, N, k, E, por, rop);
 }
 
 hipError_t launch_dispatch(const Plan &p) {

@@ -77,26 +77,33 @@ __global__ __launch_bounds__(256) void combine_block_kernel(const void *__restri
                                                             const float *__restrict__ g, float eps, void *resid,
                                                             int N, int d, int k) {
     extern __shared__ float yrow[];
-    __shared__ float ws[8];
-    __shared__ int rs[8];
     __shared__ float red[4];
     const int t = blockIdx.x;
-    if (threadIdx.x < k) {
-        ws[threadIdx.x] = tw[(size_t)t * k + threadIdx.x];
-        rs[threadIdx.x] = rop[(size_t)t * k + threadIdx.x];
+    // the token's k <= 8 rows and weights: uniform addresses, so scalar loads
+    // (slots past k repeat slot k-1 and are not added)
+    int rs[8];
+    float ws[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int jj = j < k ? j : k - 1;
+        rs[j] = rop[(size_t)t * k + jj];
+        ws[j] = tw[(size_t)t * k + jj];
     }
-    __syncthreads();
     const size_t shared_row = (size_t)N * k + t;
     float ss = 0.f;
     for (int c = threadIdx.x * 4; c < d; c += 1024) {
+        // every slot's row requested at once, added in slot order
         float4 a = load_y4n<YBF16>(Y, shared_row * d + c);
-        for (int j = 0; j < k; ++j) {
-            const float wj = ws[j];
-            const float4 y = load_y4n<YBF16>(Y, (size_t)rs[j] * d + c);
-            a.x = fmaf(wj, y.x, a.x);
-            a.y = fmaf(wj, y.y, a.y);
-            a.z = fmaf(wj, y.z, a.z);
-            a.w = fmaf(wj, y.w, a.w);
+        float4 y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = load_y4n<YBF16>(Y, (size_t)rs[j] * d + c);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {   // per-value selects, not branches: the loads stay ahead of every use
+            const bool on = j < k;
+            a.x = on ? fmaf(ws[j], y[j].x, a.x) : a.x;
+            a.y = on ? fmaf(ws[j], y[j].y, a.y) : a.y;
+            a.z = on ? fmaf(ws[j], y[j].z, a.z) : a.z;
+            a.w = on ? fmaf(ws[j], y[j].w, a.w) : a.w;
         }
         *reinterpret_cast<float4 *>(yrow + c) = a;
         ss = fmaf(a.x, a.x, fmaf(a.y, a.y, fmaf(a.z, a.z, fmaf(a.w, a.w, ss))));

@@ -47,6 +47,13 @@ __global__ __launch_bounds__(256) void topk_kernel(
     const float *row = partial + (size_t)t * E;
     constexpr int kMaxSlices = 10;
     constexpr bool kAllAtOnce = VPL * kMaxSlices <= 60;
+    // the biases go out first, from clamped indices, so no load waits behind another
+    float bv[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        const int e = lane + 64 * v;
+        bv[v] = bias[e < E ? e : 0];
+    }
     float part[kAllAtOnce ? VPL : 1][kMaxSlices];
     if constexpr (kAllAtOnce) {
 #pragma unroll
@@ -67,13 +74,12 @@ __global__ __launch_bounds__(256) void topk_kernel(
 #pragma unroll
         for (int s = 1; s < kMaxSlices; ++s) acc += s < ks ? p[s] : 0.0f;
         h[v] = acc;
-        if (e < E) {
-            if (logits_out) logits_out[(size_t)t * E + e] = acc;
-            const float sc = acc + bias[e];
-            key[v] = ((uint64_t)orderable(sc) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
-        } else {
-            key[v] = 0;  // below every real key
-        }
+        // the key is formed unconditionally (a select, no branch), so the bias
+        // load cannot be sunk behind the partial sums
+        const float sc = acc + bv[v];
+        const uint64_t kv = ((uint64_t)orderable(sc) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+        key[v] = e < E ? kv : 0;  // 0 is below every real key
+        if (e < E && logits_out) logits_out[(size_t)t * E + e] = acc;
     }
 
     // k <= 8: fully unrolled rounds keep every array in registers
