@@ -165,7 +165,8 @@ __device__ __forceinline__ void tile_mma(const void *a_base, const size_t (&a_of
                                          const float *sc_lo = nullptr, const float *sc_hi = nullptr) {
     using G = Geo<WN>;
     constexpr int kRowStep = G::kThreads / 8;  // tile rows covered by one pass of the loader
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform: in a scalar register, the live-row tests are scalar branches
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int chunk = (tid & 7) * 8;
     const int r0 = tid >> 3;
@@ -212,24 +213,42 @@ __device__ __forceinline__ void tile_mma(const void *a_base, const size_t (&a_of
                     accb[mi][ni][q] = 0.f;
                 }
     };
+    // All 16 fragment reads of a stage (both 32-wide K halves) are issued
+    // before the first MFMA, so the second half's reads land while the first
+    // half multiplies.  Rows past the group end are zero in LDS; their reads
+    // are harmless and their MFMAs are skipped.  With block scales the second
+    // accumulator set leaves no room for both halves' fragments, so each half
+    // is read just before it is used.
     auto compute = [&](int buf) {
+        constexpr int kHalves = BLK ? 1 : 2;   // halves whose fragments are in registers at once
 #pragma unroll
-        for (int kk = 0; kk < kBK; kk += 32) {
-            uint4 af[4], bf[4];
+        for (int h0 = 0; h0 < 2; h0 += kHalves) {
+            uint4 af[kHalves][4], bf[kHalves][4];
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                bf[ni] = *reinterpret_cast<const uint4 *>(Bs[buf] + (b_row_of<WN>(wn, ni) + fr) * kLdsStride + kk + fk);
+            for (int h = 0; h < kHalves; ++h) {
+                const int kk = 32 * (h0 + h);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                if (mi < live) {  // wave-uniform
-                    af[mi] = *reinterpret_cast<const uint4 *>(As[buf] + (wm * 64 + mi * 16 + fr) * kLdsStride + kk + fk);
-                    // B fragment as the MFMA's first operand: the result is
-                    // transposed, so a lane holds 4 consecutive output columns
-                    // of one row (lane % 16 = row, 4 * (lane / 16) + q = column)
+                for (int ni = 0; ni < 4; ++ni)
+                    bf[h][ni] =
+                        *reinterpret_cast<const uint4 *>(Bs[buf] + (b_row_of<WN>(wn, ni) + fr) * kLdsStride + kk + fk);
 #pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) dst[mi][ni] = mfma_bf16(bf[ni], af[mi], dst[mi][ni]);
-                }
+                for (int mi = 0; mi < 4; ++mi)
+                    af[h][mi] =
+                        *reinterpret_cast<const uint4 *>(As[buf] + (wm * 64 + mi * 16 + fr) * kLdsStride + kk + fk);
+                __builtin_amdgcn_sched_barrier(0);   // keep the first half's reads ahead of the second's
             }
+#pragma unroll
+            for (int h = 0; h < kHalves; ++h)
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    if (mi < live) {  // wave-uniform
+                        // B fragment as the MFMA's first operand: the result is
+                        // transposed, so a lane holds 4 consecutive output columns
+                        // of one row (lane % 16 = row, 4 * (lane / 16) + q = column)
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni) dst[mi][ni] = mfma_bf16(bf[h][ni], af[h][mi], dst[mi][ni]);
+                    }
+                }
         }
     };
 
