@@ -62,6 +62,27 @@ constexpr int kAPer = Geo<kWN>::kAPer;
 constexpr int kBPer = Geo<kWN>::kBPer;
 constexpr size_t kGemmLds = Geo<kWN>::kLds;   // 108 KiB
 
+// XCD-aware work order.  Workgroups are handed to the 8 XCDs round-robin by
+// launch index, and each XCD has its own L2.  Work items (column block
+// fastest, then the tile list, whose tiles of one expert are adjacent) are
+// grouped in blocks of kXcdTiles tile rows; XCD c takes blocks c, c+8, c+16,
+// ... in order.  The workgroups that share an expert's weight slices and
+// token rows thus run on one XCD and hit in its L2, while heavy stretches of
+// the list (the shared expert's tiles come first) spread over all XCDs.
+// Launch slot L = 8 s + c runs item ((s / B) * 8 + c) * B + s % B, with
+// B = kXcdTiles * gridDim.x; every item below n has a slot below n + 8 B, so
+// the grid must hold that many workgroups.  Returns false for a workgroup
+// without an item.
+constexpr int kXcds = 8;
+constexpr int kXcdTiles = 4;
+__device__ __forceinline__ bool xcd_item(int n_items, int &item) {
+    const int L = blockIdx.y * gridDim.x + blockIdx.x;
+    const int B = kXcdTiles * gridDim.x;
+    const int c = L % kXcds, slot = L / kXcds;
+    item = ((slot / B) * kXcds + c) * B + slot % B;
+    return item < n_items;
+}
+
 __device__ __forceinline__ f32x4_t mfma_bf16(const uint4 &a, const uint4 &b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -313,13 +334,14 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
     const int32_t *__restrict__ por, uint16_t *__restrict__ H, int ldh, int d, int E, int k, int f, int fs) {
     constexpr bool FP8 = WM != kWBf16, BLK = WM == kWFp8Blk;
     extern __shared__ uint16_t lds[];
-    const int u = blockIdx.y;
-    if (u >= *n_tiles) return;
+    int item;
+    if (!xcd_item(*n_tiles * (int)gridDim.x, item)) return;
+    const int u = item / gridDim.x;
     const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
     const bool shared = g == E;
     const int fg = shared ? fs : f;
     constexpr int kHalf = kBN / 2;  // H columns per tile
-    const int c0 = blockIdx.x * kHalf;
+    const int c0 = (item % gridDim.x) * kHalf;
     if (c0 >= fg) return;
     const int gstart = offsets[g];
     const int row0 = gstart + m0, m = min(kBM, offsets[g + 1] - row0);
@@ -399,12 +421,13 @@ __global__ __launch_bounds__(kThreads) void down_gemm_kernel(
     int f, int fs) {
     constexpr bool FP8 = WM != kWBf16, BLK = WM == kWFp8Blk;
     extern __shared__ uint16_t lds[];
-    const int u = blockIdx.y;
-    if (u >= *n_tiles) return;
+    int item;
+    if (!xcd_item(*n_tiles * (int)gridDim.x, item)) return;
+    const int u = item / gridDim.x;
     const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
     const bool shared = g == E;
     const int fg = shared ? fs : f;
-    const int o0 = blockIdx.x * kBN;
+    const int o0 = (item % gridDim.x) * kBN;
     const int row0 = offsets[g] + m0, m = min(kBM, offsets[g + 1] - row0);
     const int tid = threadIdx.x;
     const void *base = shared ? wsd : wd;
@@ -635,13 +658,14 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemm_f8_kernel(
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ por, uint8_t *__restrict__ hq,
     float *__restrict__ hs, int ldh, int d, int E, int k, int f, int fs) {
     extern __shared__ uint8_t ldsb[];
-    const int u = blockIdx.y;
-    if (u >= *n_tiles) return;
+    int item;
+    if (!xcd_item(*n_tiles * (int)gridDim.x, item)) return;
+    const int u = item / gridDim.x;
     const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
     const bool shared = g == E;
     const int fg = shared ? fs : f;
     constexpr int kHalf = kBN / 2;
-    const int c0 = blockIdx.x * kHalf;
+    const int c0 = (item % gridDim.x) * kHalf;
     if (c0 >= fg) return;
     const int gstart = offsets[g];
     const int row0 = gstart + m0, m = min(kBM, offsets[g + 1] - row0);
@@ -759,12 +783,13 @@ __global__ __launch_bounds__(kThreads) void down_gemm_f8_kernel(
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets,
     uint16_t *__restrict__ Y, int d, int E, int f, int fs) {
     extern __shared__ uint8_t ldsb[];
-    const int u = blockIdx.y;
-    if (u >= *n_tiles) return;
+    int item;
+    if (!xcd_item(*n_tiles * (int)gridDim.x, item)) return;
+    const int u = item / gridDim.x;
     const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
     const bool shared = g == E;
     const int fg = shared ? fs : f;
-    const int o0 = blockIdx.x * kBN;
+    const int o0 = (item % gridDim.x) * kBN;
     const int row0 = offsets[g] + m0, m = min(kBM, offsets[g + 1] - row0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 2, wn = wave & 3;
     const uint8_t *base = (const uint8_t *)(shared ? wsd : wd);
@@ -948,7 +973,9 @@ hipError_t gemm_kernels_init() {
 
 hipError_t launch_gate_up_gemm(const Plan &p) {
     const int fmax = p.f > p.fs ? p.f : p.fs;
-    dim3 grid((fmax + kBN / 2 - 1) / (kBN / 2), p.max_tiles), block(kThreads);
+    // spare tile rows: the XCD-aware order needs n + 8 * kXcdTiles * gx launch slots
+    const int gx = (fmax + kBN / 2 - 1) / (kBN / 2);
+    dim3 grid(gx, p.max_tiles + kXcds * kXcdTiles), block(kThreads);
     if (p.aq) {
         hipError_t e = launch_quant_groups(p.x, 1, p.d, p.N, p.d, p.xq, p.d, p.xs, p.d / 128, p.stream);
         if (e != hipSuccess) return e;
@@ -974,7 +1001,8 @@ hipError_t launch_gate_up_gemm(const Plan &p) {
 }
 
 hipError_t launch_down_gemm(const Plan &p) {
-    dim3 grid((p.d + kBN - 1) / kBN, p.max_tiles), block(kThreads);
+    const int gx = (p.d + kBN - 1) / kBN;
+    dim3 grid(gx, p.max_tiles + kXcds * kXcdTiles), block(kThreads);
     uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y);
     if (p.aq) {
 #define FGS_DNF(B)                                                                                             \
