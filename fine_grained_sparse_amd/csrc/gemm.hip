@@ -60,7 +60,12 @@ constexpr int kThreads = Geo<kWN>::kThreads;  // 512
 constexpr int kBN = Geo<kWN>::kBN;            // 256
 constexpr int kAPer = Geo<kWN>::kAPer;
 constexpr int kBPer = Geo<kWN>::kBPer;
-constexpr size_t kGemmLds = Geo<kWN>::kLds;   // 108 KiB
+constexpr size_t kGemmLds = Geo<kWN>::kLds;   // 120 KiB
+// direct-to-LDS variant: three stages of unpadded 128-byte rows
+constexpr int kDmaStages = 3;
+constexpr int kDmaRowB = 128;
+constexpr int kDmaStageB = (kBM + kBN) * kDmaRowB;                 // 48 KiB
+constexpr size_t kGemmLdsDma = (size_t)kDmaStages * kDmaStageB;    // 144 KiB, static
 
 // XCD-aware work order.  Workgroups are handed to the 8 XCDs round-robin by
 // launch index, and each XCD has its own L2.  Work items (column block
@@ -324,7 +329,126 @@ __device__ __forceinline__ void tile_mma(const void *a_base, const size_t (&a_of
 // weight modes: bfloat16, FP8 with per-channel scales, FP8 with 128x128 block scales
 enum { kWBf16 = 0, kWFp8Row = 1, kWFp8Blk = 2 };
 
+// ---------------------------------------------------------------- direct-to-LDS tile
+// bf16 x bf16 tile product with the operand tiles fetched straight into LDS
+// (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS
+// destination + 16 * lane), three stages deep, one barrier per stage, no
+// register staging.  LDS rows are 128 bytes, unpadded; 16-byte chunk c of
+// tile row r sits at chunk position c ^ (r & 7), which keeps the fragment
+// reads free of bank conflicts.  Each lane therefore fetches, for its LDS
+// slot, the chunk that the swizzle puts there: the callers pass per-lane
+// source pointers for K = 0 that already include it.
+//
+// DMA j of wave w covers tile rows 8 * (w * n + j) .. + 7 (n = 2 for A, 4 for
+// B): lane i fills row 8 * (w * n + j) + i / 8, position i % 8.
+//
+// Synchronisation: at the top of stage kt a wave waits until its own DMAs of
+// stage kt have landed (vmcnt counts only these loads in the loop: the later
+// stage's 6 may stay in flight), then the LDS barrier makes every wave's
+// stage-kt data visible.  Stage kt's fragment reads are issued next, then
+// stage kt + 2 is fetched into the buffer of stage kt - 1: every wave passed
+// the barrier, so every wave has consumed (waited for) all its fragment reads
+// of that buffer.  Rows past the group end hold some valid row's data; their
+// MFMAs are skipped or their outputs never stored.
+//
+// The DMA is issued from inline assembly: the compiler's wait insertion
+// cannot tell the three buffers apart across the loop and would wait for
+// every DMA in flight before each stage's reads, which removes the prefetch.
+// The instruction has no register result (its data goes to LDS), its address
+// registers are read at issue, it saves and restores M0, and the explicit
+// vmcnt waits above order it; the compiler's own waits only count its own
+// loads, which vmcnt completes in order, so they can only wait longer.
+
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left at their no-wait maxima
+#define FGS_VMCNT(N) (((N) & 0xF) | (((N) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from `src` into LDS at `lds_addr` (wave-uniform) + 16 * lane
+__device__ __forceinline__ void dma16(const void *src, const void *lds_dst) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds_dst);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(dst)
+        : "memory");
+}
+
+// The three stage buffers are distinct LDS objects and the stage loop is
+// unrolled by three, so every buffer reference is static: the compiler then
+// knows that a stage's fragment reads never alias the DMAs just issued into
+// another buffer and does not wait for them.
+__device__ __forceinline__ void tile_mma_dma(const uint16_t *const (&a_src)[kAPer],
+                                             const uint16_t *const (&b_src)[kBPer], int K, int m,
+                                             f32x4_t (&acc)[4][4]) {
+    static_assert(kAPer == 2 && kBPer == 4, "six DMAs per wave and stage");
+    __shared__ __attribute__((aligned(16))) uint8_t L0[kDmaStageB];
+    __shared__ __attribute__((aligned(16))) uint8_t L1[kDmaStageB];
+    __shared__ __attribute__((aligned(16))) uint8_t L2[kDmaStageB];
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / kWN, wn = wave % kWN;
+    const int fr = lane & 15, fg = lane >> 4;
+    const int live = min(4, max(0, (m - wm * 64 + 15) / 16));
+    auto fetch = [&](int kt, uint8_t *buf) {
+        const int k0 = kt * kBK;
+#pragma unroll
+        for (int j = 0; j < kAPer; ++j) dma16(a_src[j] + k0, buf + (wave * kAPer + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < kBPer; ++j) dma16(b_src[j] + k0, buf + kBM * kDmaRowB + (wave * kBPer + j) * 1024);
+    };
+    // 16-byte fragment of tile row r, logical chunk c (8 bf16 along K)
+    auto frag = [&](const uint8_t *base, int r, int c) {
+        return *reinterpret_cast<const uint4 *>(base + r * kDmaRowB + ((c ^ (r & 7)) << 4));
+    };
+    // stage kt: wait for own stage-kt DMAs, barrier, read stage kt's
+    // fragments, fetch stage kt + 2 into the buffer of stage kt - 1, multiply
+    const int nk = K / kBK;
+    auto step = [&](int kt, const uint8_t *cur, uint8_t *next2) {
+        if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(kAPer + kBPer));
+        else __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        uint4 af[2][4], bf[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int c = 4 * h + fg;   // K elements 32 h + 8 (lane / 16) ..
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) bf[h][ni] = frag(cur + kBM * kDmaRowB, b_row_of(wn, ni) + fr, c);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) af[h][mi] = frag(cur, wm * 64 + mi * 16 + fr, c);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kt + 2 < nk) fetch(kt + 2, next2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                if (mi < live) {
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_bf16(bf[h][ni], af[h][mi], acc[mi][ni]);
+                }
+            }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    fetch(0, L0);
+    if (nk > 1) fetch(1, L1);
+    int kt = 0;
+    for (; kt + 3 <= nk; kt += 3) {   // stage s uses buffer s % 3
+        step(kt, L0, L2);
+        step(kt + 1, L1, L0);
+        step(kt + 2, L2, L1);
+    }
+    if (kt < nk) step(kt, L0, L2);
+    if (kt + 1 < nk) step(kt + 1, L1, L0);
+}
+
 // grid: (ceil(max(f, fs) / 128), tile capacity); block 512; LDS kGemmLds
+// (kGemmLdsDma for bf16 x and weights: direct-to-LDS tile)
 template <int WM, bool XF32>
 __global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
     const void *__restrict__ x, const void *__restrict__ wg, const void *__restrict__ wu,
@@ -351,13 +475,13 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
     bool a_ok[kAPer];
     const void *b_base[kBPer];
     const size_t wrow0 = shared ? 0 : (size_t)g * f;
+    auto token_row = [&](int r) { return shared ? (row0 + r - gstart) : por[row0 + r] / k; };
 #pragma unroll
     for (int j = 0; j < kAPer; ++j) {
         const int r = (tid >> 3) + 64 * j;
         a_ok[j] = r < m;
         const int rr = a_ok[j] ? r : 0;  // rows past the group end read row 0 (masked when stored)
-        const int t = shared ? (row0 + rr - gstart) : por[row0 + rr] / k;
-        a_off[j] = (size_t)t * d;
+        a_off[j] = (size_t)token_row(rr) * d;
     }
 #pragma unroll
     for (int j = 0; j < kBPer; ++j) {
@@ -373,14 +497,36 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // block scales: the tile's 128 gate (and up) rows are output block c0/128
-    const float *sc_lo = nullptr, *sc_hi = nullptr;
-    if (BLK) {
-        const size_t sb = ((shared ? 0 : (size_t)g * (f / 128)) + c0 / 128) * (size_t)(d / 128);
-        sc_lo = (shared ? ssg : sg) + sb;
-        sc_hi = (shared ? ssu : su) + sb;
+    if constexpr (WM == kWBf16 && !XF32) {
+        // direct-to-LDS tile: lane i of DMA j of wave w fills tile row
+        // 8 (w n + j) + i / 8 at swizzled chunk position i % 8
+        const int lane = tid & 63, w = tid >> 6, pos = lane & 7;
+        const uint16_t *a_src[kAPer], *b_src[kBPer];
+#pragma unroll
+        for (int j = 0; j < kAPer; ++j) {
+            const int r = 8 * (w * kAPer + j) + (lane >> 3);
+            const int t = token_row(r < m ? r : 0);
+            a_src[j] = (const uint16_t *)x + (size_t)t * d + ((pos ^ (r & 7)) << 3);
+        }
+#pragma unroll
+        for (int j = 0; j < kBPer; ++j) {
+            const int r = 8 * (w * kBPer + j) + (lane >> 3);
+            const bool up = r >= kHalf;
+            const int c = c0 + (r & (kHalf - 1));
+            const uint16_t *wb = (const uint16_t *)(up ? (shared ? wsu : wu) : (shared ? wsg : wg));
+            b_src[j] = wb + (wrow0 + (c < fg ? c : c0)) * (size_t)d + ((pos ^ (r & 7)) << 3);
+        }
+        tile_mma_dma(a_src, b_src, d, m, acc);
+    } else {
+        // block scales: the tile's 128 gate (and up) rows are output block c0/128
+        const float *sc_lo = nullptr, *sc_hi = nullptr;
+        if (BLK) {
+            const size_t sb = ((shared ? 0 : (size_t)g * (f / 128)) + c0 / 128) * (size_t)(d / 128);
+            sc_lo = (shared ? ssg : sg) + sb;
+            sc_hi = (shared ? ssu : su) + sb;
+        }
+        tile_mma<FP8, XF32, kWN, BLK>(x, a_off, a_ok, b_base, b_off, 0, d, d, m, lds, acc, sc_lo, sc_hi);
     }
-    tile_mma<FP8, XF32, kWN, BLK>(x, a_off, a_ok, b_base, b_off, 0, d, d, m, lds, acc, sc_lo, sc_hi);
 
     // epilogue: acc[mi][ni][q] is row wm*64 + mi*16 + lane%16, GEMM column
     // (B row) b_row_of(wn, ni) + 4*(lane/16) + q; gate tile ni and up tile
@@ -454,16 +600,33 @@ __global__ __launch_bounds__(kThreads) void down_gemm_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // block scales: B rows [0, 128) are output block o0/128, rows [128, 256)
-    // the next one (clamped at the end of d: those rows are never stored)
-    const float *sc_lo = nullptr, *sc_hi = nullptr;
-    if (BLK) {
-        const int nkb = fg / 128, nob = d / 128, ob = o0 / 128;
-        const float *sp = shared ? ssd : sd + (size_t)g * nob * nkb;
-        sc_lo = sp + (size_t)ob * nkb;
-        sc_hi = sp + (size_t)(ob + 1 < nob ? ob + 1 : ob) * nkb;
+    if constexpr (WM == kWBf16) {
+        // direct-to-LDS tile (see the gate/up kernel for the lane -> row map)
+        const int lane = tid & 63, w = tid >> 6, pos = lane & 7;
+        const uint16_t *a_src[kAPer], *b_src[kBPer];
+#pragma unroll
+        for (int j = 0; j < kAPer; ++j) {
+            const int r = 8 * (w * kAPer + j) + (lane >> 3);
+            a_src[j] = H + (size_t)(row0 + (r < m ? r : 0)) * ldh + ((pos ^ (r & 7)) << 3);
+        }
+#pragma unroll
+        for (int j = 0; j < kBPer; ++j) {
+            const int r = 8 * (w * kBPer + j) + (lane >> 3);
+            b_src[j] = (const uint16_t *)base + (obase + (o0 + r < d ? o0 + r : 0)) * (size_t)fg + ((pos ^ (r & 7)) << 3);
+        }
+        tile_mma_dma(a_src, b_src, fg, m, acc);
+    } else {
+        // block scales: B rows [0, 128) are output block o0/128, rows [128, 256)
+        // the next one (clamped at the end of d: those rows are never stored)
+        const float *sc_lo = nullptr, *sc_hi = nullptr;
+        if (BLK) {
+            const int nkb = fg / 128, nob = d / 128, ob = o0 / 128;
+            const float *sp = shared ? ssd : sd + (size_t)g * nob * nkb;
+            sc_lo = sp + (size_t)ob * nkb;
+            sc_hi = sp + (size_t)(ob + 1 < nob ? ob + 1 : ob) * nkb;
+        }
+        tile_mma<FP8, false, kWN, BLK>(H, a_off, a_ok, b_base, b_off, 0, fg, fg, m, lds, acc, sc_lo, sc_hi);
     }
-    tile_mma<FP8, false, kWN, BLK>(H, a_off, a_ok, b_base, b_off, 0, fg, fg, m, lds, acc, sc_lo, sc_hi);
 
     const int lane = tid & 63, wave = tid >> 6, wm = wave >> 2, wn = wave & 3;
 #pragma unroll
@@ -946,14 +1109,13 @@ hipError_t launch_router_gemm(const Plan &p, uint16_t *w3) {
 }
 
 template <typename K>
-static hipError_t allow_lds(K kernel) {
+static hipError_t allow_lds(K kernel, size_t bytes = kGemmLds) {
     return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)kGemmLds);
+                               (int)bytes);
 }
 
 hipError_t gemm_kernels_init() {
     hipError_t e;
-    if ((e = allow_lds(gate_up_gemm_kernel<kWBf16, false>)) != hipSuccess) return e;
     if ((e = allow_lds(gate_up_gemm_kernel<kWBf16, true>)) != hipSuccess) return e;
     if ((e = allow_lds(gate_up_gemm_kernel<kWFp8Row, false>)) != hipSuccess) return e;
     if ((e = allow_lds(gate_up_gemm_kernel<kWFp8Row, true>)) != hipSuccess) return e;
@@ -968,7 +1130,7 @@ hipError_t gemm_kernels_init() {
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(router_gemm_kernel),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)Geo<2>::kLds)) != hipSuccess)
         return e;
-    return allow_lds(down_gemm_kernel<kWBf16>);
+    return hipSuccess;   // the bf16 kernels' tile buffers are static LDS
 }
 
 hipError_t launch_gate_up_gemm(const Plan &p) {
@@ -989,7 +1151,8 @@ hipError_t launch_gate_up_gemm(const Plan &p) {
         return hipGetLastError();
     }
 #define FGS_GUG(WM, XF)                                                                                         \
-    hipLaunchKernelGGL((gate_up_gemm_kernel<WM, XF>), grid, block, kGemmLds, p.stream, p.x, p.W.w_gate, p.W.w_up, \
+    hipLaunchKernelGGL((gate_up_gemm_kernel<WM, XF>), grid, block,                                               \
+                       (WM == kWBf16 && !XF) ? 0 : kGemmLds, p.stream, p.x, p.W.w_gate, p.W.w_up,               \
                        p.W.s_gate, p.W.s_up, p.W.ws_gate, p.W.ws_up, p.W.ss_gate, p.W.ss_up, p.tiles, p.n_tiles,  \
                        p.offsets, p.por, p.H, p.ldh, p.d, p.E, p.k, p.f, p.fs)
     const bool xf32 = p.xdt == MOE_DTYPE_F32;
@@ -1014,7 +1177,8 @@ hipError_t launch_down_gemm(const Plan &p) {
         return hipGetLastError();
     }
 #define FGS_DNG(WM)                                                                                       \
-    hipLaunchKernelGGL((down_gemm_kernel<WM>), grid, block, kGemmLds, p.stream, p.H, p.ldh, p.W.w_down, p.W.s_down, \
+    hipLaunchKernelGGL((down_gemm_kernel<WM>), grid, block, WM == kWBf16 ? 0 : kGemmLds, p.stream, p.H,            \
+                       p.ldh, p.W.w_down, p.W.s_down,                                                                \
                        p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs)
     if (p.wdt != MOE_DTYPE_FP8_E4M3) FGS_DNG(kWBf16);
     else if (p.flags & MOE_FLAG_FP8_BLOCK128) FGS_DNG(kWFp8Blk);
