@@ -19,9 +19,9 @@
 // Work list: one tile per non-empty group (routed experts, and the shared
 // expert as group E with all N tokens), written by the dispatch scan.
 //
-// FP8 weights are decoded to bf16 once, after their loads land (the E4M3 ->
-// bf16 conversion is exact), so the per-token dot products are the same for
-// both weight types.  Scales ("Inside Kolibri 1", section "The FP8 path is
+// FP8 weights are decoded to bf16 (exact) before the dot products: in the
+// gate/up kernel per token (a wave holds twice as many FP8 rows, too many to
+// keep converted), in the down kernel once after the loads land.  Scales ("Inside Kolibri 1", section "The FP8 path is
 // explicitly mixed precision"): a per-output-channel scale is applied to the
 // finished dot product; with 128 x 128 block scales every 8-element partial
 // product is scaled by its own block's scale before the cross-lane sum.
@@ -71,7 +71,11 @@ __device__ __forceinline__ uint4 load_x8(const void *x, int xdt, size_t elem_off
     return make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
 }
 
-constexpr int kGuRB = 8;   // H columns per workgroup (2 per wave)
+// H columns per wave: 2 with bf16 weights, 4 with FP8 weights (rows of
+// E4M3 codes are half the bytes, so a wave holds twice as many to keep as many
+// bytes in flight)
+template <bool FP8> constexpr int gu_cols_per_wave() { return FP8 ? 4 : 2; }
+template <bool FP8> constexpr int gu_cols_per_block() { return 4 * gu_cols_per_wave<FP8>(); }
 
 template <int CPL>
 __device__ __forceinline__ void load_x_row(uint4 (&xv)[CPL], const void *x, int xdt, int t, int d, int lane,
@@ -97,7 +101,7 @@ __device__ __forceinline__ void load_xq_row(uint2 (&xv)[CPL], float (&sv)[CPL], 
     }
 }
 
-// grid: (ceil(max(f, fs) / 8) column blocks, tile list capacity); block 256.
+// grid: (ceil(max(f, fs) / gu_cols_per_block) column blocks, tile list capacity); block 256.
 // Column blocks run fastest, so the workgroups in flight together cover a few
 // experts' matrices completely (page and DRAM-row locality).  No LDS and no
 // barrier: each lane reads its slice of a token row straight from L2, with
@@ -113,36 +117,37 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ por, uint16_t *__restrict__ H,
     float *__restrict__ Hf, int ldh, int d, int E, int k, int f, int fs, int bm) {
     constexpr bool FP8 = WM != kWBf16, BLK = WM == kWFp8Blk;
+    constexpr int RP = gu_cols_per_wave<FP8>(), NR = 2 * RP;   // H columns, weight rows per wave
     const int u = blockIdx.y;
     if (u >= *n_tiles) return;
     const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
     const bool shared = g == E;
     const int fg = shared ? fs : f;
-    if ((int)blockIdx.x * kGuRB >= fg) return;
+    if ((int)blockIdx.x * gu_cols_per_block<FP8>() >= fg) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int c0 = blockIdx.x * kGuRB + wave * 2;
+    const int c0 = blockIdx.x * gu_cols_per_block<FP8>() + wave * RP;
     const int nch = d / 8;
 
-    // this wave's 4 weight rows: gate c0, c0+1, up c0, c0+1 (issued first)
+    // this wave's NR weight rows: gate c0 .. c0+RP-1, then up c0 .. c0+RP-1 (issued first)
     const void *gbase = shared ? wsg : wg;
     const void *ubase = shared ? wsu : wu;
     const size_t rbase = shared ? 0 : (size_t)g * f;
     // lanes past the row end read chunk 0 again (finite weights) and are
     // multiplied by a zero activation chunk; no select on loaded values, so
     // nothing waits for these loads before the token rows are requested
-    typename WChunk<FP8>::T wr[4][CPL];
+    typename WChunk<FP8>::T wr[NR][CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int ch = lane + 64 * i;
         const int chc = ch < nch ? ch : 0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const void *b = r < 2 ? gbase : ubase;
-            wr[r][i] = load_chunk<FP8>(b, (rbase + c0 + (r & 1)) * (size_t)d + (size_t)chc * 8);
+        for (int r = 0; r < NR; ++r) {
+            const void *b = r < RP ? gbase : ubase;
+            wr[r][i] = load_chunk<FP8>(b, (rbase + c0 + (r % RP)) * (size_t)d + (size_t)chc * 8);
         }
     }
     // block scales: chunk ch covers input columns [8ch, 8ch+8), in K block ch/16;
-    // rows c0 and c0+1 share one output block
+    // rows c0 .. c0+RP-1 share one output block
     float bsc[2][CPL];
     if (BLK) {
         const int nkb = d / 128;
@@ -163,8 +168,12 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
     int tok = 0;
     if (lane < m) tok = shared ? (m0 + lane) : por[row0 + lane] / k;
 
+    // after the reduction the value index of a lane is its top log2(NR) bits:
+    // gate column c0 + j sits on the lanes with bit 5 clear and value j, the
+    // matching up column on the same lanes with bit 5 set
+    constexpr int kLb = 6 - (NR == 8 ? 3 : 2);   // lowest value bit
+    const int r_out = (lane >> kLb) & (RP - 1);
     float gsc = 1.f, usc = 1.f;
-    const int r_out = (lane >> 4) & 1;  // after the reduction lanes 0 and 16 own gate columns c0, c0+1
     if (WM == kWFp8Row) {
         const float *gs = shared ? ssg : sg + (size_t)g * f;
         const float *us = shared ? ssu : su + (size_t)g * f;
@@ -177,31 +186,38 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
     float sa[CPL], sb[CPL];
     if (AQ) load_xq_row<CPL>(qa, sa, (const uint8_t *)x, xs, __shfl(tok, 0, kWave), d, lane, nch);
     else load_x_row<CPL>(xa, x, xdt, __shfl(tok, 0, kWave), d, lane, nch);
-    uint4 w[4][CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) w[r][i] = chunk_bf16<FP8>(wr[r][i]);
+    // bf16 rows are used as loaded; E4M3 rows are converted per token (held
+    // converted they would need twice the registers)
     for (int t = 0; t < m; ++t) {
         if (t + 1 < m) {
             if (AQ) load_xq_row<CPL>(qb, sb, (const uint8_t *)x, xs, __shfl(tok, t + 1, kWave), d, lane, nch);
             else load_x_row<CPL>(xb, x, xdt, __shfl(tok, t + 1, kWave), d, lane, nch);
         }
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        float acc[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[r] = 0.f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const uint4 xc = AQ ? chunk_bf16<true>(qa[i]) : xa[i];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (AQ) acc[r] = fmaf(dot8_bf16(w[r][i], xc, 0.f), BLK ? sa[i] * bsc[r >> 1][i] : sa[i], acc[r]);
-                else if (BLK) acc[r] = fmaf(dot8_bf16(w[r][i], xc, 0.f), bsc[r >> 1][i], acc[r]);
-                else acc[r] = dot8_bf16(w[r][i], xc, acc[r]);
+            for (int r = 0; r < NR; ++r) {
+                const int gu = r / RP;   // 0 gate, 1 up
+                typename WChunk<FP8>::T raw = wr[r][i];
+                if constexpr (FP8) {
+                    // an empty asm makes the codes opaque per token, so the
+                    // conversion is not hoisted out of the token loop (which
+                    // would hold every row converted: twice the registers)
+                    asm volatile("" : "+v"(raw.x), "+v"(raw.y));
+                }
+                const uint4 wv = chunk_bf16<FP8>(raw);
+                if (AQ) acc[r] = fmaf(dot8_bf16(wv, xc, 0.f), BLK ? sa[i] * bsc[gu][i] : sa[i], acc[r]);
+                else if (BLK) acc[r] = fmaf(dot8_bf16(wv, xc, 0.f), bsc[gu][i], acc[r]);
+                else acc[r] = dot8_bf16(wv, xc, acc[r]);
             }
         }
-        butterfly_reduce<4>(acc);
-        // value index = 2*bit5 + bit4 of the lane: gate rows 0,1 then up rows 2,3
+        butterfly_reduce<NR>(acc);
         const float upv = __shfl_xor(acc[0], 32, kWave);
-        if ((lane & 47) == 0) {  // lanes 0 and 16
+        if ((lane & (32 | ((1 << kLb) - 1))) == 0) {  // one lane per gate column
             const float hv = silu(acc[0] * gsc) * (upv * usc);
             if (AQ) Hf[(size_t)(row0 + t) * ldh + c0 + r_out] = hv;
             else H[(size_t)(row0 + t) * ldh + c0 + r_out] = (uint16_t)f32_to_bf16_rne(hv);
@@ -214,10 +230,12 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
     }
 }
 
-constexpr int kDnRW = 8;   // output rows per wave
-constexpr int kDnRB = 4 * kDnRW;  // output rows per workgroup
+// output rows per wave (16 for FP8 weights, i.e. the same bytes in flight as
+// bf16, measured slower: fewer workgroups and a longer reduction per token)
+template <bool FP8> constexpr int dn_rows_per_wave() { return 8; }
+template <bool FP8> constexpr int dn_rows_per_block() { return 4 * dn_rows_per_wave<FP8>(); }
 
-// grid: (d / kDnRB, tile list capacity); block 256.  Needs f, fs <= 512.
+// grid: (d / dn_rows_per_block, tile list capacity); block 256.  Needs f, fs <= 512.
 // AQ: H is the E4M3 codes [rows][ldh] (as bytes) with scales hs [rows][ldh/128].
 template <int WM, bool AQ>
 __global__ __launch_bounds__(256) void down_stream_kernel(
@@ -227,6 +245,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
     const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets, float *__restrict__ Y, int d, int E,
     int f, int fs, int bm) {
     constexpr bool FP8 = WM != kWBf16, BLK = WM == kWFp8Blk;
+    constexpr int kDnRW = dn_rows_per_wave<FP8>();
     const int u = blockIdx.y;
     if (u >= *n_tiles) return;
     const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
@@ -234,7 +253,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
     const int fg = shared ? fs : f;
     const int nch = fg / 8;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int o0 = blockIdx.x * kDnRB + wave * kDnRW;
+    const int o0 = blockIdx.x * dn_rows_per_block<FP8>() + wave * kDnRW;
 
     const void *base = shared ? wsd : wd;
     const size_t obase = shared ? 0 : (size_t)g * d;
@@ -298,7 +317,8 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
 
 hipError_t launch_gate_up(const Plan &p) {
     const int fmax = p.f > p.fs ? p.f : p.fs;
-    dim3 grid((fmax + kGuRB - 1) / kGuRB, p.max_tiles), block(256);
+    const int cb = p.wdt == MOE_DTYPE_FP8_E4M3 ? gu_cols_per_block<true>() : gu_cols_per_block<false>();
+    dim3 grid((fmax + cb - 1) / cb, p.max_tiles), block(256);
     const size_t lds = 0;
     const int cpl = (p.d / 8 + 63) / 64;
     const int wm = p.wdt != MOE_DTYPE_FP8_E4M3 ? kWBf16 : (p.flags & MOE_FLAG_FP8_BLOCK128) ? kWFp8Blk : kWFp8Row;
@@ -334,7 +354,8 @@ hipError_t launch_gate_up(const Plan &p) {
 }
 
 hipError_t launch_down(const Plan &p) {
-    dim3 grid(p.d / kDnRB, p.max_tiles), block(256);
+    const int rb = p.wdt == MOE_DTYPE_FP8_E4M3 ? dn_rows_per_block<true>() : dn_rows_per_block<false>();
+    dim3 grid(p.d / rb, p.max_tiles), block(256);
     const long rows = (long)p.N * p.k + p.N;
     if (p.aq) {  // hidden activations in 1 x 128 groups (every row of H, routed and shared)
         hipError_t e = launch_quant_groups(p.hf, 0, p.ldh, rows, p.ldh, p.hq, p.ldh, p.hs, p.ldh / 128, p.stream);
