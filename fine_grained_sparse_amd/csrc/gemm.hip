@@ -1026,30 +1026,47 @@ __global__ __launch_bounds__(kThreads) void down_gemm_f8_kernel(
 // three times along K.  Products of bf16 values are exact in FP32 and all 3d
 // terms of a logit accumulate in one FP32 accumulator.
 
+// grid: E (one workgroup per router row); block 256.  Also writes flags[e] =
+// whether any mid or lo term of row e is nonzero (bf16-representable router
+// weights, as in the pages' checkpoint, have none).
 __global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ rw, uint16_t *__restrict__ w3,
-                                                           int E, int d) {
-    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (long)E * d) return;
-    const int e = (int)(i / d), kx = (int)(i % d);
-    const float v = rw[i];
-    const uint32_t uh = __float_as_uint(v) & 0xFFFF0000u;
-    const float r1 = v - __uint_as_float(uh);
-    const uint32_t um = __float_as_uint(r1) & 0xFFFF0000u;
-    const float r2 = r1 - __uint_as_float(um);
+                                                           int32_t *__restrict__ flags, int E, int d) {
+    const int e = blockIdx.x;
     uint16_t *row = w3 + (size_t)e * 3 * d;
-    row[kx] = (uint16_t)(uh >> 16);
-    row[d + kx] = (uint16_t)(um >> 16);
-    row[2 * d + kx] = (uint16_t)f32_to_bf16_rne(r2);
+    int any = 0;
+    for (int kx = threadIdx.x; kx < d; kx += blockDim.x) {
+        const float v = rw[(size_t)e * d + kx];
+        const uint32_t uh = __float_as_uint(v) & 0xFFFF0000u;
+        const float r1 = v - __uint_as_float(uh);
+        const uint32_t um = __float_as_uint(r1) & 0xFFFF0000u;
+        const float r2 = r1 - __uint_as_float(um);
+        const uint16_t m = (uint16_t)(um >> 16), l = (uint16_t)f32_to_bf16_rne(r2);
+        row[kx] = (uint16_t)(uh >> 16);
+        row[d + kx] = m;
+        row[2 * d + kx] = l;
+        any |= ((m | l) & 0x7FFF) != 0;   // a -0 term contributes nothing either
+    }
+    any = __syncthreads_or(any);
+    if (threadIdx.x == 0) flags[e] = any;
 }
 
 // grid: (ceil(E / 128), ceil(N / 128), ks); block 256; LDS Geo<2>::kLds.
 // Slice z covers GEMM columns [z*3d/ks, (z+1)*3d/ks) and writes partial[z].
 __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__restrict__ x,
-                                                          const uint16_t *__restrict__ w3, float *__restrict__ partial,
+                                                          const uint16_t *__restrict__ w3,
+                                                          const int32_t *__restrict__ flags, float *__restrict__ partial,
                                                           int N, int d, int E) {
     using G = Geo<2>;
     extern __shared__ uint16_t lds[];
     const int t0 = blockIdx.y * kBM, e0 = blockIdx.x * G::kBN;
+    // slices 0 .. ks/3-1 cover the hi term, then mid, then lo; a mid or lo
+    // slice whose experts all have zero terms there is skipped (its partial
+    // sums would be exactly zero; the top-k does not read them)
+    if ((int)blockIdx.z >= (int)gridDim.z / 3) {
+        const int e = e0 + (int)threadIdx.x;
+        const int any = __syncthreads_or(threadIdx.x < G::kBN && e < E ? flags[e] : 0);
+        if (!any) return;
+    }
     const int m = min(kBM, N - t0);
     const int tid = threadIdx.x;
     size_t a_off[G::kAPer], b_off[G::kBPer];
@@ -1097,14 +1114,12 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__rest
 }
 
 hipError_t launch_router_gemm(const Plan &p, uint16_t *w3) {
-    const long total = (long)p.E * p.d;
-    hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, p.stream, p.rw, w3,
-                       p.E, p.d);
+    hipLaunchKernelGGL(router_split_kernel, dim3(p.E), dim3(256), 0, p.stream, p.rw, w3, p.rflags, p.E, p.d);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 grid((p.E + Geo<2>::kBN - 1) / Geo<2>::kBN, (p.N + kBM - 1) / kBM, p.ks);
     hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(Geo<2>::kThreads), Geo<2>::kLds, p.stream,
-                       (const uint16_t *)p.x, w3, p.partial, p.N, p.d, p.E);
+                       (const uint16_t *)p.x, w3, p.rflags, p.partial, p.N, p.d, p.E);
     return hipGetLastError();
 }
 

@@ -54,7 +54,7 @@ int check_desc(const moe_desc *d) {
 }
 
 struct Layout {
-    size_t partial, ids, tw, blk, offsets, tiles, n_tiles, por, rop, H, Y, w3, xq, xs, hq, hs, hf, total;
+    size_t partial, ids, tw, blk, offsets, tiles, n_tiles, por, rop, H, Y, w3, rflags, xq, xs, hq, hs, hf, total;
     int ks, kslice, nblk, max_tiles, bm, ldh;
     bool stream, rgemm, aq;
 };
@@ -97,6 +97,7 @@ Layout layout_for(const moe_desc *d) {
     L.H = take(cur, rows * L.ldh * 2);
     L.Y = take(cur, rows * (size_t)d->d_model * 4);
     L.w3 = take(cur, L.rgemm ? E * 3 * (size_t)d->d_model * 2 : 0);
+    L.rflags = take(cur, L.rgemm ? E * 4 : 0);
     L.aq = (d->flags & MOE_FLAG_FP8_ACT_QUANT) != 0;
     const size_t dm = d->d_model;
     L.xq = take(cur, L.aq ? N * dm : 0);
@@ -210,6 +211,7 @@ int run_layer(const moe_desc *desc, const void *x, const float *router_w, const 
     p.H = (uint16_t *)(ws + L.H); p.ldh = L.ldh;
     p.Y = (float *)(ws + L.Y);
     p.w3 = (uint16_t *)(ws + L.w3);
+    p.rflags = L.rgemm ? (int32_t *)(ws + L.rflags) : nullptr;
     p.use_stream = L.stream;
     p.stream = (hipStream_t)stream;
     p.aq = L.aq;

@@ -39,6 +39,7 @@ struct Plan {
     int ldh;
     float *Y;            // [N*k + N][d] expert outputs: float32 (stream path) or bfloat16 (GEMM path)
     uint16_t *w3;        // [E][3d] bf16 split of the router weights (router GEMM only)
+    int32_t *rflags;     // [E] router GEMM only: nonzero if expert e's mid or lo split term is nonzero
     const float *norm_post;  // block variant: post-norm weights [d] (out = the residual row)
     float eps;
     // 1 x 128 activation quantisation (FP8 x FP8 expert matmuls)
@@ -82,16 +83,17 @@ struct RouterTiling { int mt, nt, ks; };
 // (one k-slice, W_r split into three bf16 terms along K).
 constexpr int kRouterGemmN = 64;
 inline bool router_gemm(int N, int xdt) { return xdt == MOE_DTYPE_BF16 && N > kRouterGemmN; }
-// k-slices of the router GEMM: enough workgroups to cover the chip; the slice
-// count divides the 3d/64 K stages
+// k-slices of the router GEMM: 3 c slices, c per split term (hi, mid, lo),
+// so that a slice never straddles two terms and the slices of all-zero terms
+// can be skipped; c divides the d/64 K stages of a term and is raised until
+// the hi term alone gives about 512 workgroups (ks <= 9).
 inline int router_gemm_ks(int N, int d, int E) {
     const long wgs = (long)((N + 127) / 128) * ((E + 127) / 128);
-    const int stages = 3 * d / 64;
-    const int cands[] = {1, 2, 3, 4, 5, 6, 8, 10};
-    int ks = 1;
-    for (int c : cands)
-        if (stages % c == 0 && ks < c && wgs * ks < 512) ks = c;
-    return ks;
+    const int stages = d / 64;
+    int c = 1;
+    for (int cand : {2, 3})
+        if (stages % cand == 0 && wgs * c < 512) c = cand;
+    return 3 * c;
 }
 inline RouterTiling router_tiling(int N, int d, int E) {
     RouterTiling r;

@@ -28,9 +28,10 @@ __device__ __forceinline__ float from_orderable(uint32_t o) {
     return __uint_as_float(u);
 }
 
-template <int VPL>
+// FLAGS: partial sums from the router GEMM, whose mid/lo slices are skipped per rflags
+template <int VPL, bool FLAGS>
 __global__ __launch_bounds__(256) void topk_kernel(
-    const float *__restrict__ partial, int ks, const float *__restrict__ bias,
+    const float *__restrict__ partial, int ks, const int32_t *__restrict__ rflags, const float *__restrict__ bias,
     float *__restrict__ logits_out, int32_t *__restrict__ ids, float *__restrict__ tw,
     float *__restrict__ gap, int N, int E, int k, bool renorm) {
     const int lane = threadIdx.x & 63;
@@ -48,12 +49,17 @@ __global__ __launch_bounds__(256) void topk_kernel(
     constexpr int kMaxSlices = 10;
     constexpr bool kAllAtOnce = VPL * kMaxSlices <= 60;
     // the biases go out first, from clamped indices, so no load waits behind another
+    // (with the router GEMM's split, rflags[e] == 0 says the slices of the mid
+    // and lo terms, the last two thirds, are all zero for expert e: not added)
     float bv[VPL];
+    int fl[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
         const int e = lane + 64 * v;
         bv[v] = bias[e < E ? e : 0];
+        fl[v] = FLAGS ? rflags[e < E ? e : 0] : 1;
     }
+    const int hi_slices = FLAGS ? ks / 3 : ks;
     float part[kAllAtOnce ? VPL : 1][kMaxSlices];
     if constexpr (kAllAtOnce) {
 #pragma unroll
@@ -72,7 +78,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
             p[s] = kAllAtOnce ? part[kAllAtOnce ? v : 0][s] : row[(size_t)min(s, ks - 1) * slice + ec];
         float acc = p[0];
 #pragma unroll
-        for (int s = 1; s < kMaxSlices; ++s) acc += s < ks ? p[s] : 0.0f;
+        for (int s = 1; s < kMaxSlices; ++s) acc += (s < hi_slices || (FLAGS && s < ks && fl[v])) ? p[s] : 0.0f;
         h[v] = acc;
         // the key is formed unconditionally (a select, no branch), so the bias
         // load cannot be sunk behind the partial sums
@@ -152,9 +158,10 @@ __global__ __launch_bounds__(256) void topk_kernel(
 hipError_t launch_topk(const Plan &p) {
     dim3 grid((p.N + 3) / 4), block(256);
     int vpl = (p.E + 63) / 64;
-#define FGS_TOPK(V)                                                                              \
-    hipLaunchKernelGGL((topk_kernel<V>), grid, block, 0, p.stream, p.partial, p.ks, p.rb,       \
+#define FGS_TOPK2(V, F)                                                                             \
+    hipLaunchKernelGGL((topk_kernel<V, F>), grid, block, 0, p.stream, p.partial, p.ks, p.rflags, p.rb, \
                        p.logits, p.ids, p.tw, p.gap, p.N, p.E, p.k, (p.flags & MOE_FLAG_RENORMALIZE) != 0)
+#define FGS_TOPK(V) do { if (p.rflags) FGS_TOPK2(V, true); else FGS_TOPK2(V, false); } while (0)
     if (vpl <= 1) FGS_TOPK(1);
     else if (vpl <= 2) FGS_TOPK(2);
     else if (vpl <= 4) FGS_TOPK(4);
@@ -162,6 +169,7 @@ hipError_t launch_topk(const Plan &p) {
     else if (vpl <= 8) FGS_TOPK(8);
     else FGS_TOPK(16);
 #undef FGS_TOPK
+#undef FGS_TOPK2
     return hipGetLastError();
 }
 

@@ -149,6 +149,26 @@ def test_block_act_quant():
     _say(f"  -> {stats}")
 
 
+@pytest.mark.parametrize("n", [300, 40])
+def test_router_full_fp32_weights(n):
+    """FP32 router weights that are not bf16 values (mid and lo split terms nonzero) for a scattered
+    subset of experts: expert blocks with all, some and none of their experts flagged (the router
+    GEMM skips the zero-term slices only where a whole block has none), and the N <= 64 router."""
+    cfg = get_config("toy", n_tokens=n, x_dtype="bf16", n_experts=384, d_ff=64, d_ff_shared=64)
+    host = generate(cfg, seed=8)
+    rw = host["router_w"].clone()
+    pert = torch.zeros(cfg.n_experts, dtype=torch.bool)
+    pert[0:128] = True                                   # block 0: every expert
+    pert[128:256:7] = True                               # block 1: some experts
+    rw[pert] = rw[pert] * (1.0 + 3.0 * 2.0 ** -12)       # no longer bf16-representable
+    assert not torch.equal(rw[pert].to(torch.bfloat16).float(), rw[pert])
+    host = dict(host, router_w=rw)
+    _say(f"case full-fp32 router N={n} E={cfg.n_experts}")
+    g = PA.run_gpu(cfg, PA.to_device(host))
+    stats = PA.full_check(cfg, host, g)
+    _say(f"  -> {stats}")
+
+
 @pytest.mark.parametrize("n", [16, 200])
 def test_128_experts(n):
     """The 128-expert shape of the predecessor model, top-6, full hidden size."""
