@@ -149,6 +149,18 @@ def test_block_act_quant():
     _say(f"  -> {stats}")
 
 
+@pytest.mark.parametrize("cfg_name,over", [
+    ("decode", dict(n_tokens=65)),                                     # first batch on the GEMM path
+    ("toy", dict(n_tokens=8, d_model=4096, n_experts=64, d_ff=512, d_ff_shared=512, x_dtype="bf16")),  # widest stream rows
+    ("toy", dict(n_tokens=16, d_model=4160, n_experts=48, d_ff=128, d_ff_shared=128, x_dtype="bf16")),  # d past the stream path
+    ("toy", dict(n_tokens=16, d_ff=640, d_ff_shared=512)),             # f past the stream path: GEMM at tiny m
+    ("toy", dict(n_tokens=100, d_model=2560, n_experts=1024, top_k=8, x_dtype="bf16")),  # most experts, largest k
+])
+def test_shape_limits(cfg_name, over):
+    """Edges of the supported shapes and of the stream/GEMM path choice."""
+    _run_full(get_config(cfg_name, **over))
+
+
 @pytest.mark.parametrize("n", [300, 40])
 def test_router_full_fp32_weights(n):
     """FP32 router weights that are not bf16 values (mid and lo split terms nonzero) for a scattered
