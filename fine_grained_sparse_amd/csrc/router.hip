@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ rw, float *__restrict__ partial,
     int N, int d, int E, int kslice, int n_tb, int n_eb, int n_jobs) {
     const int lane = threadIdx.x & 63;
-    const int job = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int job = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (job >= n_jobs) return;
     const int tb = job % n_tb;
     const int rest = job / n_tb;
@@ -164,11 +164,13 @@ hipError_t launch_router(const Plan &p) {
     int n_tb = (p.N + 16 * rt.mt - 1) / (16 * rt.mt);
     int n_eb = (p.E + 16 * rt.nt - 1) / (16 * rt.nt);
     int n_jobs = n_tb * n_eb * p.ks;
-    dim3 grid((n_jobs + 3) / 4);
     if (rt.mt == 2) {
-        hipLaunchKernelGGL((router_mfma_kernel<2, 1>), grid, dim3(256), 0, p.stream,
+        // one wave per workgroup: the few hundred jobs of a small batch spread
+        // over as many CUs, each pulling its slice of W_r with its own loads
+        hipLaunchKernelGGL((router_mfma_kernel<2, 1>), dim3(n_jobs), dim3(64), 0, p.stream,
                            x, p.rw, p.partial, p.N, p.d, p.E, p.kslice, n_tb, n_eb, n_jobs);
     } else {
+        dim3 grid((n_jobs + 3) / 4);
         hipLaunchKernelGGL((router_mfma_kernel<4, 4>), grid, dim3(256), 0, p.stream,
                            x, p.rw, p.partial, p.N, p.d, p.E, p.kslice, n_tb, n_eb, n_jobs);
     }
