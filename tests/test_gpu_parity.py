@@ -240,6 +240,49 @@ def test_graph_replay_matches_eager(cfg_name, over, aq):
                            ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref.view(torch.int32)), rep
 
 
+def test_in_place_residual():
+    """x == out with MOE_FLAG_ACCUMULATE: out = round(x + layer(x)), the in-place residual update."""
+    from fine_grained_sparse_amd import binding as B
+    from oracle import moe_oracle as O
+    from moe_inputs import to_numpy
+    cfg = get_config("decode", n_tokens=24)
+    host = generate(cfg, seed=11)
+    dev = PA.to_device(host)
+    x = dev["x"].clone()
+    layer = B.MoeLayer(cfg.top_k, dev, x.shape[0], x.dtype)
+    layer.forward(x, out=x, accumulate=True)
+    torch.cuda.synchronize()
+    npi = to_numpy(host)
+    ref = O.moe_forward(npi, cfg.top_k, cfg.w_dtype, cfg.x_dtype, residual=npi["x"])
+    got = x.float().cpu().numpy().astype(np.float64)
+    err = PA.rel_err(got, ref["out64"])
+    _say(f"case in-place residual: max rel err {err.max():.3e}")
+    assert err.max() <= PA.OUT_TOL[cfg.w_dtype]
+
+
+def test_two_streams_concurrently():
+    """Two layers with their own workspaces on two streams at once: both match their eager results."""
+    from fine_grained_sparse_amd import binding as B
+    cfgs = [get_config("decode", n_tokens=32), get_config("toy", n_tokens=300, x_dtype="bf16")]
+    devs = [PA.to_device(generate(c, seed=20 + i)) for i, c in enumerate(cfgs)]
+    layers = [B.MoeLayer(c.top_k, d, d["x"].shape[0], d["x"].dtype) for c, d in zip(cfgs, devs)]
+    refs = []
+    for lay, d in zip(layers, devs):
+        r = torch.empty_like(d["x"])
+        lay.forward(d["x"], out=r)
+        refs.append(r)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.full_like(d["x"], float("nan")) for d in devs]
+    for rep in range(5):
+        for st, lay, d, o in zip(streams, layers, devs, outs):
+            with torch.cuda.stream(st):
+                lay.forward(d["x"], out=o)
+    torch.cuda.synchronize()
+    for o, r in zip(outs, refs):
+        assert torch.equal(o.view(torch.int16), r.view(torch.int16))
+
+
 def test_zero_tokens_is_noop():
     from fine_grained_sparse_amd import binding as B
     cfg = get_config("toy")
