@@ -10,10 +10,11 @@ independent layer instances (each with its own router, bias, experts and
 token batch), as consecutive MoE layers of a model would, so that no step
 finds its expert weights in the 256 MB last-level cache.
 
-Prints one JSON line.  Besides throughput it reports the roofline of the
-dominant kernel, timed live with HIP events recorded by the library on the
-stream that runs the kernels, and the CPU oracle timed on a bounded sample of
-the same workload.
+Prints one JSON line.  Besides throughput (eager launches) it reports the
+roofline of the dominant kernel, timed live with HIP events recorded by the
+library on the stream that runs the kernels, the distribution of single-step
+times, the rate of the same steps replayed from a captured HIP graph, and the
+CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -41,8 +42,8 @@ def parse():
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "fp8", "fp8block", "zipf", "toy"])
     ap.add_argument("--tokens", type=int, default=None, help="override the batch size")
     ap.add_argument("--layers", type=int, default=4, help="independent layer instances cycled by the steps")
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the same steps replayed from a captured HIP graph")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the extra timing of the same steps replayed from a captured HIP graph")
     ap.add_argument("--act-quant", action="store_true",
                     help="FP8 x FP8 expert matmuls on 1 x 128 quantised activations (FP8 weights only)")
     ap.add_argument("--variant", default="plain", choices=["plain", "renorm", "block"],
@@ -240,31 +241,14 @@ def main():
     step_stats = {"p10": round(float(np.percentile(step_us, 10)), 2), "median": round(float(np.median(step_us)), 2),
                   "p90": round(float(np.percentile(step_us, 90)), 2), "pass": "separate, one event pair per step"}
 
-    # the same steps replayed from a HIP graph (one graph holds one step of every layer instance)
+    # the same steps replayed from a HIP graph (one graph holds one step of every
+    # layer instance); reported beside `value`, which stays the eager-launch rate
     graph = None
-    if args.graph:
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream(dev)
-        side.wait_stream(cur)
-        with torch.cuda.stream(side):
-            for i in range(L):   # warm the capture stream
-                step(i, None, side.cuda_stream)
-        cur.wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            cs = torch.cuda.current_stream(dev).cuda_stream
-            for i in range(L):
-                step(i, None, cs)
-        reps = max(1, args.steps // L)
-        g.replay()
-        torch.cuda.synchronize()
-        tg = time.perf_counter()
-        for _ in range(reps):
-            g.replay()
-        torch.cuda.synchronize()
-        gms = (time.perf_counter() - tg) * 1e3 / (reps * L)
-        graph = {"ms_per_step": round(gms, 5), "tokens_per_s": round(N / gms * 1e3, 1), "replays": reps,
-                 "steps_per_replay": L}
+    if not args.no_graph:
+        try:
+            graph = graph_replay(torch, dev, cur, step, L, N, args.steps)
+        except Exception as exc:   # a capture failure is reported, not fatal to the measurement
+            graph = {"error": f"{type(exc).__name__}: {exc}"}
 
     # per-launch durations of the expert kernels from the library's events
     gu_ms = [hip.elapsed_ms(ev_handles[i][2 * STAGE_GU], ev_handles[i][2 * STAGE_GU + 1]) for i in range(args.steps)]
@@ -363,6 +347,32 @@ def main():
         result["cpu_baseline"], result["parity_step0"] = cpu_baseline(cfg, layers[0], outs, mods, descs, ws, stream,
                                                                        args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def graph_replay(torch, dev, cur, step, L, N, steps):
+    """Capture one step of every layer instance in a HIP graph and time its replays."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        for i in range(L):   # warm the capture stream
+            step(i, None, side.cuda_stream)
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream(dev).cuda_stream
+        for i in range(L):
+            step(i, None, cs)
+    reps = max(1, steps // L)
+    g.replay()
+    torch.cuda.synchronize()
+    tg = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    gms = (time.perf_counter() - tg) * 1e3 / (reps * L)
+    return {"ms_per_step": round(gms, 5), "tokens_per_s": round(N / gms * 1e3, 1), "replays": reps,
+            "steps_per_replay": L}
 
 
 def cpu_baseline(cfg, inp0, outs, mods, descs, ws, stream, target_s):

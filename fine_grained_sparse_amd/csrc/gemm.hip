@@ -1,4 +1,4 @@
-// Grouped expert GEMMs on bf16 matrix cores (batches larger than the decode path).
+// Grouped expert GEMMs on the matrix cores (batches larger than the decode path).
 //
 // "Inside Kolibri 1" (flozi.net), section "Routing: selection bias and
 // mixture weights are separate": every routed or shared expert is a SwiGLU
@@ -12,18 +12,13 @@
 // times its block's scale, one FP32 multiply-add per accumulator per block.
 //
 // Work list: the dispatch scan writes one tile per 128 rows of every
-// non-empty group (shared expert first).  The grid is (column blocks, tiles)
-// with column blocks fastest, so the workgroups of one expert run together and
-// its weight slices are fetched from HBM once and re-read from cache by the
-// expert's other row tiles.  Skewed routing just yields more row tiles for the
-// popular experts.
+// non-empty group (shared expert first).  Work items are handed out
+// XCD-aware (xcd_item below), so the workgroups that share an expert's weight
+// slices and token rows run on one XCD and hit in its L2.  Skewed routing
+// just yields more row tiles for the popular experts.
 //
-// Workgroup tile: 128 rows x 256 GEMM columns, K step 64, 512 threads = 8
-// waves in a 2 (rows) x 4 (columns) layout, each wave 64 x 64 with 16 MFMA
-// 16x16x32 bf16 accumulators.  A 128 x 256 x 64 stage moves 48 KB for 4.2
-// MFLOP (87 flop per byte of L2 traffic).  Operand tiles pass through
-// double-buffered LDS (rows padded to 80 elements, which measured free of bank conflicts
-// for the 16-byte fragment reads); a wave skips the 16-row
+// Workgroup tile: 128 rows x 256 GEMM columns, 512 threads = 8 waves in a 2
+// (rows) x 4 (columns) layout, each wave 64 x 64; a wave skips the 16-row
 // MFMA sub-tiles that lie entirely past the group's last row.
 //   gate/up: A = x rows gathered through pair_of_row; B rows 0..127 are gate
 //            rows c0..c0+127 and B rows 128..255 the matching up rows, so
@@ -31,8 +26,19 @@
 //            column) and the SwiGLU epilogue is lane-local.  Writes H (bf16).
 //   down:    A = H rows of the group (contiguous), B = down rows; writes Y
 //            (bf16) for the combine kernel.
-// FP8 weights are decoded to bf16 (exact: E4M3 values are bf16 values) while
-// being written to LDS.
+// Three tile routines share this layout:
+//   tile_mma_dma  bf16 activations and weights: operand tiles fetched straight
+//                 into three LDS stages (64-wide K stages, unpadded rows with
+//                 an XOR chunk swizzle), MFMA 16x16x32 bf16;
+//   tile_mma      every other combination: operands through registers into
+//                 two padded LDS stages (rows of 80 elements, measured free of
+//                 bank conflicts); FP8 weights are decoded to bf16 (exact) and
+//                 FP32 activations rounded to bf16 on the way into LDS;
+//   tile_mma_f8   1 x 128 quantised activations: E4M3 operands, 128-wide K
+//                 stages of the same byte layout, MFMA 16x16x128 f8f6f4, each
+//                 stage folded in with its activation and weight scales.
+// A 128 x 256 stage of 128 bytes per row moves 48 KB for 4.2 MFLOP (bf16) or
+// 8.4 MFLOP (FP8).
 #include "moe_common.h"
 #include "moe_plan.h"
 
@@ -66,6 +72,7 @@ constexpr int kDmaStages = 3;
 constexpr int kDmaRowB = 128;
 constexpr int kDmaStageB = (kBM + kBN) * kDmaRowB;                 // 48 KiB
 constexpr size_t kGemmLdsDma = (size_t)kDmaStages * kDmaStageB;    // 144 KiB, static
+static_assert(kGemmLdsDma <= 160 * 1024, "the direct-to-LDS stages must fit one CU's LDS");
 
 // XCD-aware work order.  Workgroups are handed to the 8 XCDs round-robin by
 // launch index, and each XCD has its own L2.  Work items (column block
@@ -448,7 +455,7 @@ __device__ __forceinline__ void tile_mma_dma(const uint16_t *const (&a_src)[kAPe
 }
 
 // grid: (ceil(max(f, fs) / 128), tile capacity); block 512; LDS kGemmLds
-// (kGemmLdsDma for bf16 x and weights: direct-to-LDS tile)
+// (bf16 x and weights: none; the direct-to-LDS tile uses kGemmLdsDma of static LDS)
 template <int WM, bool XF32>
 __global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
     const void *__restrict__ x, const void *__restrict__ wg, const void *__restrict__ wu,

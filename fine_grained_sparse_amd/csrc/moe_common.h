@@ -55,30 +55,6 @@ __device__ __forceinline__ float dot8_bf16(const uint4 &a, const uint4 &b, float
     return c;
 }
 
-// ---------------------------------------------------------------- FP8 E4M3FN
-// OCP E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits, subnormals at
-// exponent 0, no infinities.  Exact decode from the bit fields; NaN codes are
-// not produced by valid weights and decode as a large finite value.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-    uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
-    float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20))
-                  : float(m) * 0.001953125f;  // m * 2^-9
-    return (c & 0x80u) ? -mag : mag;
-}
-
-// 8 FP8 codes (packed in a uint2) dotted with 8 bfloat16 activations (uint4)
-__device__ __forceinline__ float dot8_e4m3_bf16(const uint2 &w, const uint4 &x, float c) {
-    c = fmaf(e4m3_to_f32(w.x & 0xFF), bf16_lo(x.x), c);
-    c = fmaf(e4m3_to_f32((w.x >> 8) & 0xFF), bf16_hi(x.x), c);
-    c = fmaf(e4m3_to_f32((w.x >> 16) & 0xFF), bf16_lo(x.y), c);
-    c = fmaf(e4m3_to_f32(w.x >> 24), bf16_hi(x.y), c);
-    c = fmaf(e4m3_to_f32(w.y & 0xFF), bf16_lo(x.z), c);
-    c = fmaf(e4m3_to_f32((w.y >> 8) & 0xFF), bf16_hi(x.z), c);
-    c = fmaf(e4m3_to_f32((w.y >> 16) & 0xFF), bf16_lo(x.w), c);
-    c = fmaf(e4m3_to_f32(w.y >> 24), bf16_hi(x.w), c);
-    return c;
-}
-
 // ---------------------------------------------------------------- wave ops
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -10,27 +10,30 @@
 // For small batches each touched expert holds only a few token rows, so the
 // layer is bound by reading the touched experts' weights once from HBM.  The
 // kernels here give every workgroup a slice of one expert's weight rows, keep
-// those rows in registers (16-byte coalesced loads: consecutive lanes read
-// consecutive 16-byte chunks of a row), and dot them against that expert's
-// token rows staged in LDS.  Cross-lane sums use a butterfly reduce-scatter:
-// at each halving step a lane keeps half of its partial sums and trades the
-// other half with its partner, so V sums over 64 lanes cost about V shuffles.
+// those rows in registers (coalesced non-temporal loads: consecutive lanes
+// read consecutive chunks of a row), and dot them against that expert's token
+// rows, which each lane reads straight from L2 with the next token's row in
+// flight (no LDS, no barrier).  Cross-lane sums use a butterfly
+// reduce-scatter: at each halving step a lane keeps half of its partial sums
+// and trades the other half with its partner, so V sums over 64 lanes cost
+// about V shuffles.
 //
 // Work list: one tile per non-empty group (routed experts, and the shared
 // expert as group E with all N tokens), written by the dispatch scan.
 //
 // FP8 weights are decoded to bf16 (exact) before the dot products: in the
 // gate/up kernel per token (a wave holds twice as many FP8 rows, too many to
-// keep converted), in the down kernel once after the loads land.  Scales ("Inside Kolibri 1", section "The FP8 path is
-// explicitly mixed precision"): a per-output-channel scale is applied to the
-// finished dot product; with 128 x 128 block scales every 8-element partial
-// product is scaled by its own block's scale before the cross-lane sum.
-// With 1 x 128 activation quantisation (AQ) the token rows arrive as E4M3
-// codes plus one FP32 scale per 128 values; codes are exact in bf16, so the
-// same dot products run on them and each 8-element partial is multiplied by
-// its group's activation scale (times the weight block scale).  The gate/up
-// kernel then writes FP32 hidden values, which are quantised in 1 x 128
-// groups before the down kernel reads them.
+// keep converted), in the down kernel once after the loads land.  Scales
+// ("Inside Kolibri 1", section "The FP8 path is explicitly mixed precision"):
+// a per-output-channel scale is applied to the finished dot product; with
+// 128 x 128 block scales every 8-element partial product is scaled by its own
+// block's scale before the cross-lane sum.  With 1 x 128 activation
+// quantisation (AQ) the token rows arrive as E4M3 codes plus one FP32 scale
+// per 128 values; codes are exact in bf16, so the same dot products run on
+// them and each 8-element partial is multiplied by its group's activation
+// scale (times the weight block scale).  The gate/up kernel then writes FP32
+// hidden values, which are quantised in 1 x 128 groups before the down
+// kernel reads them.
 #include "moe_common.h"
 #include "moe_plan.h"
 
