@@ -11,9 +11,9 @@ namespace {
 thread_local int g_last_hip_error = 0;
 std::atomic<int> g_arch_state[64];  // 0 unknown, 1 gfx950, 2 other
 
-std::atomic<int> g_gemm_init{0};    // 0 not yet, 1 done, -1 failed
+std::atomic<int> g_gemm_init[64];   // per device: 0 not yet, 1 the GEMM kernels' LDS limits are raised
 
-int check_device() {
+int check_device(int *dev_out = nullptr) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) { g_last_hip_error = (int)e; return MOE_ERR_HIP; }
@@ -26,6 +26,7 @@ int check_device() {
         st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
         g_arch_state[dev].store(st, std::memory_order_release);
     }
+    if (dev_out) *dev_out = dev;
     return st == 1 ? MOE_OK : MOE_ERR_UNSUPPORTED;
 }
 
@@ -181,12 +182,14 @@ int run_layer(const moe_desc *desc, const void *x, const float *router_w, const 
     const Layout L = layout_for(desc);
     const size_t need = L.total + (blk ? ((xbytes + 255) & ~size_t(255)) : 0);
     if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
-    st = check_device();
+    int dev = 0;
+    st = check_device(&dev);
     if (st != MOE_OK) return st;
-    if ((!L.stream || L.rgemm) && g_gemm_init.load(std::memory_order_acquire) != 1) {
+    if ((!L.stream || L.rgemm) && g_gemm_init[dev].load(std::memory_order_acquire) != 1) {
+        // idempotent: concurrent first calls may both set the same attributes
         hipError_t e = gemm_kernels_init();
         if (e != hipSuccess) { g_last_hip_error = (int)e; return MOE_ERR_HIP; }
-        g_gemm_init.store(1, std::memory_order_release);
+        g_gemm_init[dev].store(1, std::memory_order_release);
     }
 
     char *ws = (char *)workspace;

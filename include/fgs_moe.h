@@ -39,8 +39,10 @@
  *   - dispatch is a stable counting sort of pairs by (expert, token).
  *
  * Memory: every pointer is device memory owned by the caller.  The library
- * allocates nothing, frees nothing and keeps no mutable global state besides
- * a once-per-device cache of the device architecture check.
+ * allocates nothing and frees nothing.  Its only mutable global state is set
+ * once per device on the first call there: a cache of the device architecture
+ * check and the raised LDS limit of the GEMM kernels; plus the thread-local
+ * code of the last HIP error.
  *
  * Execution: all work is enqueued on `stream` (a hipStream_t; NULL = the
  * default stream) without host synchronisation; results are valid once the
