@@ -48,7 +48,9 @@
  * default stream) without host synchronisation; results are valid once the
  * stream reaches that point.  Device faults surface at the caller's next
  * synchronisation.  Calls that share a workspace must be ordered on one
- * stream.
+ * stream.  Calls can be captured in a HIP graph (no memset or host work is
+ * enqueued); make the first call on each device outside a capture, since it
+ * queries the device and sets kernel attributes.
  */
 #ifndef FGS_MOE_H
 #define FGS_MOE_H
