@@ -349,14 +349,22 @@ enum { kWBf16 = 0, kWFp8Row = 1, kWFp8Blk = 2 };
 // DMA j of wave w covers tile rows 8 * (w * n + j) .. + 7 (n = 2 for A, 4 for
 // B): lane i fills row 8 * (w * n + j) + i / 8, position i % 8.
 //
-// Synchronisation: at the top of stage kt a wave waits until its own DMAs of
-// stage kt have landed (vmcnt counts only these loads in the loop: the later
-// stage's 6 may stay in flight), then the LDS barrier makes every wave's
-// stage-kt data visible.  Stage kt's fragment reads are issued next, then
-// stage kt + 2 is fetched into the buffer of stage kt - 1: every wave passed
-// the barrier, so every wave has consumed (waited for) all its fragment reads
-// of that buffer.  Rows past the group end hold some valid row's data; their
-// MFMAs are skipped or their outputs never stored.
+// Synchronisation and software pipeline.  Each 64-wide stage is consumed in
+// two 32-wide K halves, and a wave holds two fragment sets: while the MFMAs
+// of one half run from registers, the fragment reads of the next half are
+// issued between them (sched_group_barrier interleaves the two streams), so
+// LDS reads and matrix-core work overlap instead of alternating.  Before the
+// reads of stage kt+1 (after the first half of stage kt has been
+// multiplied) a wave waits until its own DMAs of stage kt+1 have landed
+// (vmcnt counts only these loads: stage kt+2's may stay in flight), and the
+// LDS barrier, whose release fence also completes the wave's own fragment
+// reads, makes every wave's stage kt+1 data visible.  Right after it stage
+// kt+3 is fetched into the buffer of stage kt: every wave has passed the
+// barrier, so every wave's reads of that buffer are complete.  Rows past the
+// group end hold some valid row's data; a wave's 16-row sub-tiles that lie
+// wholly past it are neither read nor multiplied (the count of live sub-tiles
+// is fixed per wave for the whole product, so each count has its own
+// straight-line loop), and the remaining junk rows are never stored.
 //
 // The DMA is issued from inline assembly: the compiler's wait insertion
 // cannot tell the three buffers apart across the loop and would wait for
@@ -385,6 +393,22 @@ __device__ __forceinline__ void dma16(const void *src, const void *lds_dst) {
         : "memory");
 }
 
+// MFMA / fragment-read interleave for the scheduler: R reads spread over M
+// MFMAs, the MFMAs first (their operands are already in registers)
+template <int R, int M>
+__device__ __forceinline__ void interleave_mfma_reads() {
+    if constexpr (R > 0) {
+        constexpr int mm = M / R;
+        if constexpr (mm > 0) __builtin_amdgcn_sched_group_barrier(0x008, mm, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        interleave_mfma_reads<R - 1, M - mm>();
+    } else if constexpr (M > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+    }
+}
+
+template <int N> struct Live { static constexpr int value = N; };
+
 // The three stage buffers are distinct LDS objects and the stage loop is
 // unrolled by three, so every buffer reference is static: the compiler then
 // knows that a stage's fragment reads never alias the DMAs just issued into
@@ -399,7 +423,7 @@ __device__ __forceinline__ void tile_mma_dma(const uint16_t *const (&a_src)[kAPe
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / kWN, wn = wave % kWN;
     const int fr = lane & 15, fg = lane >> 4;
-    const int live = min(4, max(0, (m - wm * 64 + 15) / 16));
+    const int nk = K / kBK;
     auto fetch = [&](int kt, uint8_t *buf) {
         const int k0 = kt * kBK;
 #pragma unroll
@@ -411,47 +435,76 @@ __device__ __forceinline__ void tile_mma_dma(const uint16_t *const (&a_src)[kAPe
     auto frag = [&](const uint8_t *base, int r, int c) {
         return *reinterpret_cast<const uint4 *>(base + r * kDmaRowB + ((c ^ (r & 7)) << 4));
     };
-    // stage kt: wait for own stage-kt DMAs, barrier, read stage kt's
-    // fragments, fetch stage kt + 2 into the buffer of stage kt - 1, multiply
-    const int nk = K / kBK;
-    auto step = [&](int kt, const uint8_t *cur, uint8_t *next2) {
+    auto wait_own = [&](int kt) {   // this wave's DMAs of stage kt landed (stage kt+1's may be in flight)
         if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(kAPer + kBPer));
         else __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
-        lds_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        uint4 af[2][4], bf[2][4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int c = 4 * h + fg;   // K elements 32 h + 8 (lane / 16) ..
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) bf[h][ni] = frag(cur + kBM * kDmaRowB, b_row_of(wn, ni) + fr, c);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) af[h][mi] = frag(cur, wm * 64 + mi * 16 + fr, c);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (kt + 2 < nk) fetch(kt + 2, next2);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                if (mi < live) {
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_bf16(bf[h][ni], af[h][mi], acc[mi][ni]);
-                }
-            }
-        __builtin_amdgcn_sched_barrier(0);
     };
+
     fetch(0, L0);
     if (nk > 1) fetch(1, L1);
-    int kt = 0;
-    for (; kt + 3 <= nk; kt += 3) {   // stage s uses buffer s % 3
-        step(kt, L0, L2);
-        step(kt + 1, L1, L0);
-        step(kt + 2, L2, L1);
+    wait_own(0);
+    lds_barrier();
+    if (nk > 2) fetch(2, L2);
+    __builtin_amdgcn_sched_barrier(0);
+
+    auto run = [&](auto live_c) {
+        constexpr int LV = decltype(live_c)::value;   // live 16-row sub-tiles of this wave
+        constexpr int R = LV > 0 ? 4 + LV : 0;         // fragment reads per half
+        auto read_half = [&](const uint8_t *cur, int h, uint4 (&af)[4], uint4 (&bf)[4]) {
+            if constexpr (LV > 0) {
+                const int c = 4 * h + fg;   // K elements 32 h + 8 (lane / 16) ..
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) bf[ni] = frag(cur + kBM * kDmaRowB, b_row_of(wn, ni) + fr, c);
+#pragma unroll
+                for (int mi = 0; mi < LV; ++mi) af[mi] = frag(cur, wm * 64 + mi * 16 + fr, c);
+            }
+        };
+        auto mma_half = [&](const uint4 (&af)[4], const uint4 (&bf)[4]) {
+#pragma unroll
+            for (int mi = 0; mi < LV; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_bf16(bf[ni], af[mi], acc[mi][ni]);
+        };
+        uint4 fa0[4], fb0[4], fa1[4], fb1[4];
+        read_half(L0, 0, fa0, fb0);
+        // stage kt from buffer `cur`; stage kt+1 is in `nxt`; stage kt+3 goes into `cur`
+        auto stage = [&](int kt, uint8_t *cur, const uint8_t *nxt) {
+            __builtin_amdgcn_sched_barrier(0);
+            read_half(cur, 1, fa1, fb1);
+            mma_half(fa0, fb0);
+            interleave_mfma_reads<R, 4 * LV>();
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < nk) {
+                wait_own(kt + 1);
+                lds_barrier();
+                if (kt + 3 < nk) fetch(kt + 3, cur);
+                __builtin_amdgcn_sched_barrier(0);
+                read_half(nxt, 0, fa0, fb0);
+                mma_half(fa1, fb1);
+                interleave_mfma_reads<R, 4 * LV>();
+            } else {
+                mma_half(fa1, fb1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        int kt = 0;
+        for (; kt + 3 <= nk; kt += 3) {   // stage s uses buffer s % 3
+            stage(kt, L0, L1);
+            stage(kt + 1, L1, L2);
+            stage(kt + 2, L2, L0);
+        }
+        if (kt < nk) stage(kt, L0, L1);
+        if (kt + 1 < nk) stage(kt + 1, L1, L2);
+    };
+    // wave-uniform: the scalar branch picks the straight-line loop for this wave
+    const int live = min(4, max(0, (m - wm * 64 + 15) / 16));
+    switch (live) {
+        case 4: run(Live<4>{}); break;
+        case 3: run(Live<3>{}); break;
+        case 2: run(Live<2>{}); break;
+        case 1: run(Live<1>{}); break;
+        default: run(Live<0>{}); break;
     }
-    if (kt < nk) step(kt, L0, L2);
-    if (kt + 1 < nk) step(kt + 1, L1, L0);
 }
 
 // grid: (ceil(max(f, fs) / 128), tile capacity); block 512; LDS kGemmLds

@@ -233,9 +233,11 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
     }
 }
 
-// output rows per wave (16 for FP8 weights, i.e. the same bytes in flight as
-// bf16, measured slower: fewer workgroups and a longer reduction per token)
-template <bool FP8> constexpr int dn_rows_per_wave() { return 8; }
+// output rows per wave: 4 KB of weights per wave in both formats (4 bf16 rows
+// of 512, 8 E4M3 rows).  Measured at decode size, 2, 8 and 16 bf16 rows and
+// 4 or 16 FP8 rows are slower: fewer, larger workgroups leave more of the
+// machine idle behind each one's index loads and at the grid's tail.
+template <bool FP8> constexpr int dn_rows_per_wave() { return FP8 ? 8 : 4; }
 template <bool FP8> constexpr int dn_rows_per_block() { return 4 * dn_rows_per_wave<FP8>(); }
 
 // grid: (d / dn_rows_per_block, tile list capacity); block 256.  Needs f, fs <= 512.

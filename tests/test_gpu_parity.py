@@ -150,7 +150,9 @@ def test_block_act_quant():
 
 
 @pytest.mark.parametrize("cfg_name,over", [
+    ("decode", dict(n_tokens=64)),                                     # largest batch on the stream path
     ("decode", dict(n_tokens=65)),                                     # first batch on the GEMM path
+    ("toy", dict(n_tokens=40, n_experts=448, top_k=8)),                # small batch, 7 experts per lane in top-k
     ("toy", dict(n_tokens=8, d_model=4096, n_experts=64, d_ff=512, d_ff_shared=512, x_dtype="bf16")),  # widest stream rows
     ("toy", dict(n_tokens=16, d_model=4160, n_experts=48, d_ff=128, d_ff_shared=128, x_dtype="bf16")),  # d past the stream path
     ("toy", dict(n_tokens=16, d_ff=640, d_ff_shared=512)),             # f past the stream path: GEMM at tiny m
