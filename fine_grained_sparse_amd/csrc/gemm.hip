@@ -26,10 +26,13 @@
 //            column) and the SwiGLU epilogue is lane-local.  Writes H (bf16).
 //   down:    A = H rows of the group (contiguous), B = down rows; writes Y
 //            (bf16) for the combine kernel.
-// Three tile routines share this layout:
+// Four tile routines share this layout:
 //   tile_mma_dma  bf16 activations and weights: operand tiles fetched straight
 //                 into three LDS stages (64-wide K stages, unpadded rows with
 //                 an XOR chunk swizzle), MFMA 16x16x32 bf16;
+//   tile_mma_dma_w8  bf16 activations, FP8 weights with per-channel scales:
+//                 the same with E4M3 weight rows (64 bytes per stage), four
+//                 stages, codes widened to bf16 (exact) as fragments are read;
 //   tile_mma      every other combination: operands through registers into
 //                 two padded LDS stages (rows of 80 elements, measured free of
 //                 bank conflicts); FP8 weights are decoded to bf16 (exact) and
@@ -507,6 +510,123 @@ __device__ __forceinline__ void tile_mma_dma(const uint16_t *const (&a_src)[kAPe
     }
 }
 
+// ---------------------------------------------------------------- FP8 weights, direct to LDS
+// bf16 activations x E4M3 weights (one scale per output channel, applied in
+// the epilogue) with both operand tiles fetched straight into LDS.  A 64-wide
+// K stage holds 128 activation rows of 128 bytes and 256 weight rows of 64
+// bytes, 32 KB, so four stages fit and the prefetch runs one stage deeper
+// than the bf16 tile.  Weight rows: 16-byte chunk c of row r sits at
+// position c ^ ((r >> 2) & 3), which spreads the 8-byte fragment reads of
+// 16 consecutive rows over all banks.  A fragment read takes the 8 code bytes
+// of its K range and widens them to bf16 exactly.  Synchronisation as in
+// tile_mma_dma, with stage kt+4 fetched into the buffer of stage kt.
+constexpr int kW8RowB = 64;                                  // weight-row bytes per stage
+constexpr int kW8StageB = kBM * kDmaRowB + kBN * kW8RowB;    // 32 KiB
+static_assert(4 * kW8StageB <= 160 * 1024, "four FP8-weight stages must fit one CU's LDS");
+
+__device__ __forceinline__ void tile_mma_dma_w8(const uint16_t *const (&a_src)[kAPer],
+                                                const uint8_t *const (&b_src)[2], int K, int m,
+                                                f32x4_t (&acc)[4][4]) {
+    constexpr int G = kAPer + 2;   // DMAs per wave and stage
+    __shared__ __attribute__((aligned(16))) uint8_t L0[kW8StageB];
+    __shared__ __attribute__((aligned(16))) uint8_t L1[kW8StageB];
+    __shared__ __attribute__((aligned(16))) uint8_t L2[kW8StageB];
+    __shared__ __attribute__((aligned(16))) uint8_t L3[kW8StageB];
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / kWN, wn = wave % kWN;
+    const int fr = lane & 15, fg = lane >> 4;
+    const int nk = K / kBK;
+    auto fetch = [&](int kt, uint8_t *buf) {
+        const int k0 = kt * kBK;
+#pragma unroll
+        for (int j = 0; j < kAPer; ++j) dma16(a_src[j] + k0, buf + (wave * kAPer + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dma16(b_src[j] + k0, buf + kBM * kDmaRowB + (wave * 2 + j) * 1024);
+    };
+    auto frag_a = [&](const uint8_t *base, int r, int c) {
+        return *reinterpret_cast<const uint4 *>(base + r * kDmaRowB + ((c ^ (r & 7)) << 4));
+    };
+    // 8 weights of row r, K elements 8 u .. 8 u + 7 of the stage, as bf16
+    auto frag_b = [&](const uint8_t *base, int r, int u) {
+        const uint2 q = *reinterpret_cast<const uint2 *>(base + kBM * kDmaRowB + r * kW8RowB +
+                                                         ((((u >> 1) ^ (r >> 2)) & 3) << 4) + ((u & 1) << 3));
+        return e4m3x8_to_bf16x8(q);
+    };
+    // this wave's DMAs of stage kt+1 landed; later stages' may stay in flight
+    auto wait_next = [&](int kt) {
+        const int later = min(2, nk - 2 - kt);   // stages kt+2, kt+3 already issued
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(2 * G));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(G));
+        else __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
+    };
+
+    fetch(0, L0);
+    if (nk > 1) fetch(1, L1);
+    if (nk > 2) fetch(2, L2);
+    wait_next(-1);
+    lds_barrier();
+    if (nk > 3) fetch(3, L3);
+    __builtin_amdgcn_sched_barrier(0);
+
+    auto run = [&](auto live_c) {
+        constexpr int LV = decltype(live_c)::value;
+        constexpr int R = LV > 0 ? 4 + LV : 0;
+        auto read_half = [&](const uint8_t *cur, int h, uint4 (&af)[4], uint4 (&bf)[4]) {
+            if constexpr (LV > 0) {
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) bf[ni] = frag_b(cur, b_row_of(wn, ni) + fr, 4 * h + fg);
+#pragma unroll
+                for (int mi = 0; mi < LV; ++mi) af[mi] = frag_a(cur, wm * 64 + mi * 16 + fr, 4 * h + fg);
+            }
+        };
+        auto mma_half = [&](const uint4 (&af)[4], const uint4 (&bf)[4]) {
+#pragma unroll
+            for (int mi = 0; mi < LV; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_bf16(bf[ni], af[mi], acc[mi][ni]);
+        };
+        uint4 fa0[4], fb0[4], fa1[4], fb1[4];
+        read_half(L0, 0, fa0, fb0);
+        auto stage = [&](int kt, uint8_t *cur, const uint8_t *nxt) {
+            __builtin_amdgcn_sched_barrier(0);
+            read_half(cur, 1, fa1, fb1);
+            mma_half(fa0, fb0);
+            interleave_mfma_reads<R, 4 * LV>();
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < nk) {
+                wait_next(kt);
+                lds_barrier();
+                if (kt + 4 < nk) fetch(kt + 4, cur);
+                __builtin_amdgcn_sched_barrier(0);
+                read_half(nxt, 0, fa0, fb0);
+                mma_half(fa1, fb1);
+                interleave_mfma_reads<R, 4 * LV>();
+            } else {
+                mma_half(fa1, fb1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        int kt = 0;
+        for (; kt + 4 <= nk; kt += 4) {   // stage s uses buffer s % 4
+            stage(kt, L0, L1);
+            stage(kt + 1, L1, L2);
+            stage(kt + 2, L2, L3);
+            stage(kt + 3, L3, L0);
+        }
+        if (kt < nk) stage(kt, L0, L1);
+        if (kt + 1 < nk) stage(kt + 1, L1, L2);
+        if (kt + 2 < nk) stage(kt + 2, L2, L3);
+    };
+    const int live = min(4, max(0, (m - wm * 64 + 15) / 16));
+    switch (live) {
+        case 4: run(Live<4>{}); break;
+        case 3: run(Live<3>{}); break;
+        case 2: run(Live<2>{}); break;
+        case 1: run(Live<1>{}); break;
+        default: run(Live<0>{}); break;
+    }
+}
+
 // grid: (ceil(max(f, fs) / 128), tile capacity); block 512; LDS kGemmLds
 // (bf16 x and weights: none; the direct-to-LDS tile uses kGemmLdsDma of static LDS)
 template <int WM, bool XF32>
@@ -577,6 +697,28 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
             b_src[j] = wb + (wrow0 + (c < fg ? c : c0)) * (size_t)d + ((pos ^ (r & 7)) << 3);
         }
         tile_mma_dma(a_src, b_src, d, m, acc);
+    } else if constexpr (WM == kWFp8Row && !XF32) {
+        // FP8 weights direct to LDS: activations as in the bf16 tile; lane i
+        // of weight DMA j of wave w fills weight row 16 (2 w + j) + i / 4 at
+        // chunk position i % 4 (source chunk (i % 4) ^ ((row >> 2) & 3))
+        const int lane = tid & 63, w = tid >> 6, pos = lane & 7;
+        const uint16_t *a_src[kAPer];
+        const uint8_t *b_src[2];
+#pragma unroll
+        for (int j = 0; j < kAPer; ++j) {
+            const int r = 8 * (w * kAPer + j) + (lane >> 3);
+            const int t = token_row(r < m ? r : 0);
+            a_src[j] = (const uint16_t *)x + (size_t)t * d + ((pos ^ (r & 7)) << 3);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = 16 * (w * 2 + j) + (lane >> 2);
+            const bool up = r >= kHalf;
+            const int c = c0 + (r & (kHalf - 1));
+            const uint8_t *wb = (const uint8_t *)(up ? (shared ? wsu : wu) : (shared ? wsg : wg));
+            b_src[j] = wb + (wrow0 + (c < fg ? c : c0)) * (size_t)d + ((((lane & 3) ^ (r >> 2)) & 3) << 4);
+        }
+        tile_mma_dma_w8(a_src, b_src, d, m, acc);
     } else {
         // block scales: the tile's 128 gate (and up) rows are output block c0/128
         const float *sc_lo = nullptr, *sc_hi = nullptr;
@@ -675,6 +817,23 @@ __global__ __launch_bounds__(kThreads) void down_gemm_kernel(
             b_src[j] = (const uint16_t *)base + (obase + (o0 + r < d ? o0 + r : 0)) * (size_t)fg + ((pos ^ (r & 7)) << 3);
         }
         tile_mma_dma(a_src, b_src, fg, m, acc);
+    } else if constexpr (WM == kWFp8Row) {
+        // FP8 weights direct to LDS (see the gate/up kernel for the lane -> row map)
+        const int lane = tid & 63, w = tid >> 6, pos = lane & 7;
+        const uint16_t *a_src[kAPer];
+        const uint8_t *b_src[2];
+#pragma unroll
+        for (int j = 0; j < kAPer; ++j) {
+            const int r = 8 * (w * kAPer + j) + (lane >> 3);
+            a_src[j] = H + (size_t)(row0 + (r < m ? r : 0)) * ldh + ((pos ^ (r & 7)) << 3);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = 16 * (w * 2 + j) + (lane >> 2);
+            b_src[j] = (const uint8_t *)base + (obase + (o0 + r < d ? o0 + r : 0)) * (size_t)fg +
+                       ((((lane & 3) ^ (r >> 2)) & 3) << 4);
+        }
+        tile_mma_dma_w8(a_src, b_src, fg, m, acc);
     } else {
         // block scales: B rows [0, 128) are output block o0/128, rows [128, 256)
         // the next one (clamped at the end of d: those rows are never stored)
@@ -1192,11 +1351,9 @@ static hipError_t allow_lds(K kernel, size_t bytes = kGemmLds) {
 hipError_t gemm_kernels_init() {
     hipError_t e;
     if ((e = allow_lds(gate_up_gemm_kernel<kWBf16, true>)) != hipSuccess) return e;
-    if ((e = allow_lds(gate_up_gemm_kernel<kWFp8Row, false>)) != hipSuccess) return e;
     if ((e = allow_lds(gate_up_gemm_kernel<kWFp8Row, true>)) != hipSuccess) return e;
     if ((e = allow_lds(gate_up_gemm_kernel<kWFp8Blk, false>)) != hipSuccess) return e;
     if ((e = allow_lds(gate_up_gemm_kernel<kWFp8Blk, true>)) != hipSuccess) return e;
-    if ((e = allow_lds(down_gemm_kernel<kWFp8Row>)) != hipSuccess) return e;
     if ((e = allow_lds(down_gemm_kernel<kWFp8Blk>)) != hipSuccess) return e;
     if ((e = allow_lds(gate_up_gemm_f8_kernel<true>)) != hipSuccess) return e;
     if ((e = allow_lds(gate_up_gemm_f8_kernel<false>)) != hipSuccess) return e;
@@ -1205,7 +1362,9 @@ hipError_t gemm_kernels_init() {
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(router_gemm_kernel),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)Geo<2>::kLds)) != hipSuccess)
         return e;
-    return hipSuccess;   // the bf16 kernels' tile buffers are static LDS
+    // the direct-to-LDS kernels (bf16 x with bf16 or per-channel FP8 weights)
+    // use static LDS only
+    return hipSuccess;
 }
 
 hipError_t launch_gate_up_gemm(const Plan &p) {
@@ -1227,7 +1386,7 @@ hipError_t launch_gate_up_gemm(const Plan &p) {
     }
 #define FGS_GUG(WM, XF)                                                                                         \
     hipLaunchKernelGGL((gate_up_gemm_kernel<WM, XF>), grid, block,                                               \
-                       (WM == kWBf16 && !XF) ? 0 : kGemmLds, p.stream, p.x, p.W.w_gate, p.W.w_up,               \
+                       ((WM == kWBf16 || WM == kWFp8Row) && !XF) ? 0 : kGemmLds, p.stream, p.x, p.W.w_gate, p.W.w_up, \
                        p.W.s_gate, p.W.s_up, p.W.ws_gate, p.W.ws_up, p.W.ss_gate, p.W.ss_up, p.tiles, p.n_tiles,  \
                        p.offsets, p.por, p.H, p.ldh, p.d, p.E, p.k, p.f, p.fs)
     const bool xf32 = p.xdt == MOE_DTYPE_F32;
@@ -1252,7 +1411,7 @@ hipError_t launch_down_gemm(const Plan &p) {
         return hipGetLastError();
     }
 #define FGS_DNG(WM)                                                                                       \
-    hipLaunchKernelGGL((down_gemm_kernel<WM>), grid, block, WM == kWBf16 ? 0 : kGemmLds, p.stream, p.H,            \
+    hipLaunchKernelGGL((down_gemm_kernel<WM>), grid, block, (WM == kWBf16 || WM == kWFp8Row) ? 0 : kGemmLds, p.stream, p.H, \
                        p.ldh, p.W.w_down, p.W.s_down,                                                                \
                        p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs)
     if (p.wdt != MOE_DTYPE_FP8_E4M3) FGS_DNG(kWBf16);
