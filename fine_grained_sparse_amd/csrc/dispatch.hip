@@ -191,31 +191,46 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t *blk, int n
     __shared__ int off[1026];
     __shared__ int ntile[1025];
     __shared__ int wsum[17];
+    constexpr int kChunk = 8192;    // block counts staged in LDS per pass
+    __shared__ int stage[kChunk];
     const int tid = threadIdx.x;
-    // per expert: exclusive prefix over blocks (in place), total count
-    for (int e = tid; e < E; e += blockDim.x) {
-        int run = 0;
-        for (int b = 0; b < nblk; ++b) {
-            int c = blk[(size_t)b * E + e];
-            blk[(size_t)b * E + e] = run;
-            run += c;
+    // per expert: exclusive prefix over blocks (in place), total count.  The
+    // counts of cb blocks at a time are loaded by the whole workgroup at once
+    // (coalesced, all loads in flight), scanned per expert in LDS and stored back.
+    for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
+    const int cb = kChunk / E;   // E <= 1024: at least 8 blocks per pass
+    for (int b0 = 0; b0 < nblk; b0 += cb) {
+        const int nb = min(cb, nblk - b0), n = nb * E;
+        const int32_t *src = blk + (size_t)b0 * E;
+        for (int i = tid; i < n; i += blockDim.x) stage[i] = src[i];
+        __syncthreads();
+        for (int e = tid; e < E; e += blockDim.x) {
+            int run = cnt[e];
+            for (int b = 0; b < nb; ++b) {
+                const int c = stage[b * E + e];
+                stage[b * E + e] = run;
+                run += c;
+            }
+            cnt[e] = run;
         }
-        cnt[e] = run;
+        __syncthreads();
+        for (int i = tid; i < n; i += blockDim.x) blk[(size_t)b0 * E + i] = stage[i];
+        __syncthreads();
     }
-    __syncthreads();
     offsets_and_tiles(cnt, off, ntile, wsum, N, k, E, bm, g_offsets, g_exp_off, tiles, n_tiles);
-    __syncthreads();
-    for (int e = tid; e < E; e += blockDim.x)
-        for (int b = 0; b < nblk; ++b) blk[(size_t)b * E + e] += off[e];
 }
 
+// blk[b][e]: rows of expert e in the blocks before b (from the scan)
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t *__restrict__ ids, const int32_t *blk,
-                                                               int N, int k, int E, int32_t *por, int32_t *rop) {
+                                                               const int32_t *__restrict__ offsets, int N, int k,
+                                                               int E, int32_t *por, int32_t *rop) {
     __shared__ uint32_t bits[1024 * kBTW];
+    __shared__ int base[1024];
     const int t = blockIdx.x * kBT + threadIdx.x;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) base[e] = offsets[e] + blk[(size_t)blockIdx.x * E + e];
     int my[8];
     load_token_ids(ids, t, k, t < N, my);
-    block_scatter(my, bits, blk + (size_t)blockIdx.x * E, blockIdx.x, N, k, E, por, rop);
+    block_scatter(my, bits, base, blockIdx.x, N, k, E, por, rop);   // its first barrier publishes base
 }
 
 hipError_t launch_dispatch(const Plan &p) {
@@ -231,8 +246,8 @@ hipError_t launch_dispatch(const Plan &p) {
                        p.offsets, p.exp_off_out, p.tiles, p.n_tiles);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(p.nblk), dim3(256), 0, p.stream, p.ids, p.blk, p.N, p.k, p.E,
-                       p.por, p.rop);
+    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(p.nblk), dim3(256), 0, p.stream, p.ids, p.blk, p.offsets, p.N,
+                       p.k, p.E, p.por, p.rop);
     return hipGetLastError();
 }
 

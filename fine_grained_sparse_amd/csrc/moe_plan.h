@@ -26,7 +26,7 @@ struct Plan {
     int32_t *ids;        // [N][k]
     float *tw;           // [N][k]
     float *gap;          // [N] or nullptr
-    int32_t *blk;        // [nblk][E] per-block counts, then absolute bases
+    int32_t *blk;        // [nblk][E] per-block counts, then rows of each expert in earlier blocks
     int nblk;
     int32_t *offsets;    // [E+2]: routed groups, then the shared group's rows
     int32_t *exp_off_out;// caller's [E+1] copy, or nullptr
