@@ -11,10 +11,12 @@ token batch), as consecutive MoE layers of a model would, so that no step
 finds its expert weights in the 256 MB last-level cache.
 
 Prints one JSON line.  Besides throughput (eager launches) it reports the
-roofline of the dominant kernel, timed live with HIP events recorded by the
-library on the stream that runs the kernels, the distribution of single-step
-times, the rate of the same steps replayed from a captured HIP graph, and the
-CPU oracle timed on a bounded sample of the same workload.
+roofline of the dominant kernel, timed live with HIP events that the library
+records on the stream that runs the kernels (on every fifth timed step: each
+event record drains the queue and would otherwise slow the steps it
+measures), the distribution of single-step times, the rate of the same steps
+replayed from a captured HIP graph, and the CPU oracle timed on a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
@@ -42,6 +44,10 @@ def parse():
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "fp8", "fp8block", "zipf", "toy"])
     ap.add_argument("--tokens", type=int, default=None, help="override the batch size")
     ap.add_argument("--layers", type=int, default=4, help="independent layer instances cycled by the steps")
+    ap.add_argument("--event-stride", type=int, default=5,
+                    help="the timed loop records the expert kernels' HIP events on every n-th step (n coprime "
+                         "with --layers samples every layer instance); each event record drains the queue, "
+                         "so events on every step cost the step about 14 us at decode size")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the extra timing of the same steps replayed from a captured HIP graph")
     ap.add_argument("--act-quant", action="store_true",
@@ -181,7 +187,9 @@ def main():
     n_ev = 2 * B.MOE_NUM_STAGES
     ev_arrays = []
     ev_handles = []
-    for i in range(args.steps):
+    stride = max(1, args.event_stride)
+    sampled = list(range(0, args.steps, stride))   # timed steps that carry the kernel events
+    for i in sampled:
         arr = (ctypes.c_void_p * n_ev)()
         hs = {}
         for s in (STAGE_GU, STAGE_DN):
@@ -190,8 +198,8 @@ def main():
                 arr[j] = hs[j]
         ev_arrays.append(arr)
         ev_handles.append(hs)
-    aux_timed = [B.MoeAux(None, None, None, None, None, None, None, ctypes.cast(a, ctypes.c_void_p))
-                 for a in ev_arrays]
+    aux_timed = {i: B.MoeAux(None, None, None, None, None, None, None, ctypes.cast(a, ctypes.c_void_p))
+                 for i, a in zip(sampled, ev_arrays)}
 
     def step(i, aux=None, strm=None):
         li = i % L
@@ -223,7 +231,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, aux_timed[i])
+        step(i, aux_timed.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
@@ -251,8 +259,8 @@ def main():
             graph = {"error": f"{type(exc).__name__}: {exc}"}
 
     # per-launch durations of the expert kernels from the library's events
-    gu_ms = [hip.elapsed_ms(ev_handles[i][2 * STAGE_GU], ev_handles[i][2 * STAGE_GU + 1]) for i in range(args.steps)]
-    dn_ms = [hip.elapsed_ms(ev_handles[i][2 * STAGE_DN], ev_handles[i][2 * STAGE_DN + 1]) for i in range(args.steps)]
+    gu_ms = [hip.elapsed_ms(hs[2 * STAGE_GU], hs[2 * STAGE_GU + 1]) for hs in ev_handles]
+    dn_ms = [hip.elapsed_ms(hs[2 * STAGE_DN], hs[2 * STAGE_DN + 1]) for hs in ev_handles]
     for hs in ev_handles:
         for e in hs.values():
             hip.destroy(e)
@@ -296,11 +304,11 @@ def main():
                   "hbm_frac": round(hbm_frac, 4), f"mfma_frac_{mfma_dtype}": round(mfma_frac, 4)})
         return r
 
-    gu_b = sum(gu_bytes(touched[i % L]) for i in range(args.steps))
-    dn_b = sum(dn_bytes(touched[i % L]) for i in range(args.steps))
+    gu_b = sum(gu_bytes(touched[i % L]) for i in sampled)
+    dn_b = sum(dn_bytes(touched[i % L]) for i in sampled)
     gu_t, dn_t = sum(gu_ms) * 1e-3, sum(dn_ms) * 1e-3
-    r_gu = roof(f"gate_up_{kind}", gu_b, gu_flops * args.steps, gu_t, len(gu_ms))
-    r_dn = roof(f"down_{kind}", dn_b, dn_flops * args.steps, dn_t, len(dn_ms))
+    r_gu = roof(f"gate_up_{kind}", gu_b, gu_flops * len(sampled), gu_t, len(gu_ms))
+    r_dn = roof(f"down_{kind}", dn_b, dn_flops * len(sampled), dn_t, len(dn_ms))
     dom = r_gu if gu_t >= dn_t else r_dn
 
     layer_bytes = [N * d * sx + E * d * 4 + E * 4 + touched[li] * 3 * (d * f * sw)
@@ -321,6 +329,8 @@ def main():
     roofline["traffic"] = traffic
     roofline.update({k2: v for k2, v in dom.items() if k2 not in roofline})
     roofline["other_expert_kernel"] = r_dn if dom is r_gu else r_gu
+    roofline["timing"] = (f"HIP events around the expert kernels on every {stride}-th timed step "
+                          f"({len(sampled)} of {args.steps})")
     roofline["whole_step"] = {"hbm_frac": round(layer_b / elapsed / 1e9 / HBM_PEAK_GBS, 4),
                               f"mfma_frac_{mfma_dtype}": round(layer_flops / elapsed / 1e12 / mfma_peak, 4),
                               "algorithmic_bytes": int(layer_b / args.steps),

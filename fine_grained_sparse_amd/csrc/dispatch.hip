@@ -191,14 +191,14 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t *blk, int n
     __shared__ int off[1026];
     __shared__ int ntile[1025];
     __shared__ int wsum[17];
-    constexpr int kChunk = 8192;    // block counts staged in LDS per pass
+    constexpr int kChunk = 32768;   // block counts staged in LDS per pass (128 KB)
     __shared__ int stage[kChunk];
     const int tid = threadIdx.x;
     // per expert: exclusive prefix over blocks (in place), total count.  The
     // counts of cb blocks at a time are loaded by the whole workgroup at once
     // (coalesced, all loads in flight), scanned per expert in LDS and stored back.
     for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
-    const int cb = kChunk / E;   // E <= 1024: at least 8 blocks per pass
+    const int cb = kChunk / E;   // E <= 1024: at least 32 blocks per pass
     for (int b0 = 0; b0 < nblk; b0 += cb) {
         const int nb = min(cb, nblk - b0), n = nb * E;
         const int32_t *src = blk + (size_t)b0 * E;
