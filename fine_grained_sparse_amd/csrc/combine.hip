@@ -12,20 +12,25 @@
 
 namespace fgs {
 
+// VEC consecutive values of Y as floats: 8 bf16 (16 bytes) or 4 FP32 (16 bytes)
 template <bool YBF16>
-__device__ __forceinline__ float4 load_y4(const void *Y, size_t elem) {
+__device__ __forceinline__ void load_y(const void *Y, size_t elem, float (&v)[YBF16 ? 8 : 4]) {
     if constexpr (YBF16) {
-        const uint2 v = *reinterpret_cast<const uint2 *>((const uint16_t *)Y + elem);
-        return make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+        const uint4 q = *reinterpret_cast<const uint4 *>((const uint16_t *)Y + elem);
+        v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+        v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
     } else {
-        return *reinterpret_cast<const float4 *>((const float *)Y + elem);
+        const float4 q = *reinterpret_cast<const float4 *>((const float *)Y + elem);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
     }
 }
 
+// grid: (N, column blocks); each thread combines VEC consecutive columns per pass
 template <bool BF16OUT, bool YBF16>
-__global__ __launch_bounds__(256) void combine_kernel(
+__global__ __launch_bounds__(1024) void combine_kernel(
     const void *__restrict__ Y, const float *__restrict__ tw, const int32_t *__restrict__ rop, void *out,
     int N, int d, int k, bool accumulate) {
+    constexpr int VEC = YBF16 ? 8 : 4;
     const int t = blockIdx.x;
     // the token's k <= 8 rows and weights: uniform addresses, so scalar loads
     // (slots past k repeat slot k-1 and are not added)
@@ -38,35 +43,42 @@ __global__ __launch_bounds__(256) void combine_kernel(
         ws[j] = tw[(size_t)t * k + jj];
     }
     const size_t shared_row = (size_t)N * k + t;
-    for (int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4; c < d; c += gridDim.y * blockDim.x * 4) {
+    for (int c = (blockIdx.y * blockDim.x + threadIdx.x) * VEC; c < d; c += gridDim.y * blockDim.x * VEC) {
         // all rows are requested at once, then added in slot order
-        float4 a = load_y4<YBF16>(Y, shared_row * d + c);
-        float4 y[8];
+        float a[VEC], y[8][VEC];
+        load_y<YBF16>(Y, shared_row * d + c, a);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) y[j] = load_y4<YBF16>(Y, (size_t)rs[j] * d + c);
+        for (int j = 0; j < 8; ++j) load_y<YBF16>(Y, (size_t)rs[j] * d + c, y[j]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {   // per-value selects, not branches: the loads stay ahead of every use
             const bool on = j < k;
-            a.x = on ? fmaf(ws[j], y[j].x, a.x) : a.x;
-            a.y = on ? fmaf(ws[j], y[j].y, a.y) : a.y;
-            a.z = on ? fmaf(ws[j], y[j].z, a.z) : a.z;
-            a.w = on ? fmaf(ws[j], y[j].w, a.w) : a.w;
+#pragma unroll
+            for (int q = 0; q < VEC; ++q) a[q] = on ? fmaf(ws[j], y[j][q], a[q]) : a[q];
         }
         if (BF16OUT) {
-            uint2 *o = reinterpret_cast<uint2 *>((uint16_t *)out + (size_t)t * d + c);
+            uint16_t *o = (uint16_t *)out + (size_t)t * d + c;
+            uint32_t w[VEC / 2];
             if (accumulate) {
-                uint2 old = *o;
-                a.x += bf16_lo(old.x); a.y += bf16_hi(old.x);
-                a.z += bf16_lo(old.y); a.w += bf16_hi(old.y);
+#pragma unroll
+                for (int q = 0; q < VEC / 2; ++q) w[q] = reinterpret_cast<const uint32_t *>(o)[q];
+#pragma unroll
+                for (int q = 0; q < VEC / 2; ++q) { a[2 * q] += bf16_lo(w[q]); a[2 * q + 1] += bf16_hi(w[q]); }
             }
-            *o = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
+#pragma unroll
+            for (int q = 0; q < VEC / 2; ++q) w[q] = pack_bf16x2(a[2 * q], a[2 * q + 1]);
+            if constexpr (VEC == 8) *reinterpret_cast<uint4 *>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+            else *reinterpret_cast<uint2 *>(o) = make_uint2(w[0], w[1]);
         } else {
-            float4 *o = reinterpret_cast<float4 *>((float *)out + (size_t)t * d + c);
-            if (accumulate) {
-                float4 old = *o;
-                a.x += old.x; a.y += old.y; a.z += old.z; a.w += old.w;
+            float *o = (float *)out + (size_t)t * d + c;
+#pragma unroll
+            for (int q = 0; q < VEC; q += 4) {
+                float4 v = make_float4(a[q], a[q + 1], a[q + 2], a[q + 3]);
+                if (accumulate) {
+                    const float4 old = *reinterpret_cast<const float4 *>(o + q);
+                    v.x += old.x; v.y += old.y; v.z += old.z; v.w += old.w;
+                }
+                *reinterpret_cast<float4 *>(o + q) = v;
             }
-            *o = a;
         }
     }
 }
@@ -74,7 +86,12 @@ __global__ __launch_bounds__(256) void combine_kernel(
 hipError_t launch_combine(const Plan &p) {
     const bool acc = (p.flags & MOE_FLAG_ACCUMULATE) != 0;
     const bool ybf16 = !p.use_stream;  // the grouped GEMMs store Y in bfloat16
-    dim3 grid(p.N, (p.d + 1023) / 1024), block(256);
+    // stream path (FP32 Y, small N): 256 threads x 4 columns per block, several
+    // blocks per token; GEMM path (bf16 Y): one block per token covering the row
+    // in 8-column pieces (d = 2560: 320 threads)
+    const int vec = ybf16 ? 8 : 4;
+    const int threads = ybf16 ? min(1024, ((p.d / vec + 63) / 64) * 64) : 256;
+    dim3 grid(p.N, (p.d + threads * vec - 1) / (threads * vec)), block(threads);
 #define FGS_COMBINE(OB, YB) hipLaunchKernelGGL((combine_kernel<OB, YB>), grid, block, 0, p.stream, p.Y, p.tw, p.rop, \
                                              p.out, p.N, p.d, p.k, acc)
     if (p.xdt == MOE_DTYPE_BF16) {
