@@ -12,7 +12,8 @@
 // k+1 rounds takes the wave-wide maximum of a 64-bit key built from the score
 // (order-preserving bit map, -0 folded onto +0) and the complemented expert
 // id, so equal scores go to the lower id and the result is independent of the
-// reduction order.  The (k+1)-th round only yields the selection gap.
+// reduction order.  A (k+1)-th round, run only when the gap is requested,
+// yields the selection gap.
 #include "moe_common.h"
 #include "moe_plan.h"
 
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
     int sel[8];
     float selh[8];
     float sk = 0.f, sk1 = 0.f;
-    const int rounds = (k < E) ? k + 1 : k;
+    const int rounds = (gap && k < E) ? k + 1 : k;   // the extra round only measures the gap
 #pragma unroll
     for (int r = 0; r < 9; ++r) {
         if (r < 8) { sel[r] = 0x7FFFFFFF; selh[r] = 0.f; }
