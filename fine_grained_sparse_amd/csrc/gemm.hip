@@ -26,7 +26,7 @@
 //            column) and the SwiGLU epilogue is lane-local.  Writes H (bf16).
 //   down:    A = H rows of the group (contiguous), B = down rows; writes Y
 //            (bf16) for the combine kernel.
-// Four tile routines share this layout:
+// The tile routines share this layout:
 //   tile_mma_dma  bf16 activations and weights: operand tiles fetched straight
 //                 into three LDS stages (64-wide K stages, unpadded rows with
 //                 an XOR chunk swizzle), MFMA 16x16x32 bf16;
@@ -39,7 +39,9 @@
 //                 FP32 activations rounded to bf16 on the way into LDS;
 //   tile_mma_f8   1 x 128 quantised activations: E4M3 operands, 128-wide K
 //                 stages of the same byte layout, MFMA 16x16x128 f8f6f4, each
-//                 stage folded in with its activation and weight scales.
+//                 stage folded in with its activation and weight scales;
+//                 tile_mma_dma_f8 is the same product with both operand tiles
+//                 fetched straight into LDS (K up to 24 blocks of 128).
 // A 128 x 256 stage of 128 bytes per row moves 48 KB for 4.2 MFLOP (bf16) or
 // 8.4 MFLOP (FP8).
 #include "moe_common.h"
@@ -1027,11 +1029,136 @@ __device__ __forceinline__ void tile_mma_f8(const uint8_t *a_base, const size_t 
     }
 }
 
+// ---- FP8 x FP8 with both operand tiles fetched straight into LDS: the
+// bf16 direct-to-LDS tile's three stages and swizzled 128-byte rows, one
+// 128-wide K block per stage.  A lane's 32 K bytes are chunks 2 (lane / 16)
+// and 2 (lane / 16) + 1 of its row, two 16-byte reads.  The activation scales
+// of the tile's rows and the weight block scales of the whole K range go to
+// LDS once, before the loop (loads the compiler tracks must not follow the
+// DMAs it cannot see: its waits for them would also wait for every DMA), so K
+// is limited to kF8DmaMaxKb blocks.
+constexpr int kF8DmaMaxKb = 24;
+static_assert(3 * kDmaStageB + kF8DmaMaxKb * (kBM + 2) * 4 + kBM * 4 * 4 <= 160 * 1024,
+              "stages, scales and the epilogue's row maxima must fit one CU's LDS");
+
+// sa_row[j]: activation scales (one per K block) of this lane's DMA row j
+// (clamped to the group); BLKW: sw_lo / sw_hi the weight block scales of the
+// two column halves.  Same accumulation order as tile_mma_f8.
+template <bool BLKW>
+__device__ __forceinline__ void tile_mma_dma_f8(const uint8_t *const (&a_src)[kAPer],
+                                                const uint8_t *const (&b_src)[kBPer],
+                                                const float *const (&sa_row)[kAPer], const float *sw_lo,
+                                                const float *sw_hi, int K, int m, f32x4_t (&acc)[4][4]) {
+    static_assert(kAPer == 2 && kBPer == 4, "six DMAs per wave and stage");
+    __shared__ __attribute__((aligned(16))) uint8_t L0[kDmaStageB];
+    __shared__ __attribute__((aligned(16))) uint8_t L1[kDmaStageB];
+    __shared__ __attribute__((aligned(16))) uint8_t L2[kDmaStageB];
+    __shared__ float sa_l[kF8DmaMaxKb][kBM];
+    __shared__ float sw_l[2][kF8DmaMaxKb];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / kWN, wn = wave % kWN;
+    const int fr = lane & 15, fg = lane >> 4;
+    const int nk = K / 128;
+    auto fetch = [&](int kt, uint8_t *buf) {
+        const int k0 = kt * 128;
+#pragma unroll
+        for (int j = 0; j < kAPer; ++j) dma16(a_src[j] + k0, buf + (wave * kAPer + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < kBPer; ++j) dma16(b_src[j] + k0, buf + kBM * kDmaRowB + (wave * kBPer + j) * 1024);
+    };
+    auto frag = [&](const uint8_t *base, int r, int c) {
+        return *reinterpret_cast<const uint4 *>(base + r * kDmaRowB + ((c ^ (r & 7)) << 4));
+    };
+    auto wait_own = [&](int kt) {
+        if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(kAPer + kBPer));
+        else __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
+    };
+
+    fetch(0, L0);
+    if (nk > 1) fetch(1, L1);
+    // scales: the 8 lanes that fetch a row split its K blocks (block 8 q + lane % 8)
+    const int pos = lane & 7;
+    float sv[kAPer][3];
+#pragma unroll
+    for (int j = 0; j < kAPer; ++j)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) sv[j][q] = pos + 8 * q < nk ? sa_row[j][pos + 8 * q] : 0.f;
+    const float wv = (BLKW && tid < 2 * nk) ? (tid < nk ? sw_lo[tid] : sw_hi[tid - nk]) : 0.f;
+    wait_own(0);
+#pragma unroll
+    for (int j = 0; j < kAPer; ++j) {
+        const int r = 8 * (wave * kAPer + j) + (lane >> 3);
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            if (pos + 8 * q < nk) sa_l[pos + 8 * q][r] = sv[j][q];
+    }
+    if (BLKW && tid < 2 * nk) sw_l[tid / nk][tid % nk] = wv;
+    lds_barrier();
+    if (nk > 2) fetch(2, L2);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int live = min(4, max(0, (m - wm * 64 + 15) / 16));
+    auto compute = [&](int kt, const uint8_t *cur) {
+        uint4 bf[4][2];
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int r = b_row_of(wn, ni) + fr;
+            bf[ni][0] = frag(cur + kBM * kDmaRowB, r, 2 * fg);
+            bf[ni][1] = frag(cur + kBM * kDmaRowB, r, 2 * fg + 1);
+        }
+        const float wlo = BLKW ? sw_l[0][kt] : 1.f, whi = BLKW ? sw_l[1][kt] : 1.f;
+        auto products = [&](int mi, f32x4_t (&pr)[4]) {
+            const int r = wm * 64 + mi * 16 + fr;
+            const uint4 a0 = frag(cur, r, 2 * fg), a1 = frag(cur, r, 2 * fg + 1);
+            // B fragment first: transposed result, a lane holds 4 consecutive columns of one row
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) pr[ni] = mfma_f8(bf[ni][0], bf[ni][1], a0, a1);
+        };
+        auto fold = [&](int mi, const f32x4_t (&pr)[4]) {
+            const float sa = sa_l[kt][wm * 64 + mi * 16 + fr];
+            const float clo = sa * wlo, chi = sa * whi;
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                const float c = ni < 2 ? clo : chi;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[mi][ni][q] = fmaf(pr[ni][q], c, acc[mi][ni][q]);
+            }
+        };
+        f32x4_t p0[4], p1[4];
+        if (live > 0) products(0, p0);
+        if (live > 1) products(1, p1);
+        if (live > 0) fold(0, p0);
+        if (live > 2) products(2, p0);
+        if (live > 1) fold(1, p1);
+        if (live > 3) products(3, p1);
+        if (live > 2) fold(2, p0);
+        if (live > 3) fold(3, p1);
+    };
+    // stage kt: wait for own stage-kt DMAs, barrier, fetch stage kt + 2 into
+    // the buffer of stage kt - 1, multiply
+    auto step = [&](int kt, const uint8_t *cur, uint8_t *next2) {
+        wait_own(kt);
+        lds_barrier();
+        if (kt + 2 < nk) fetch(kt + 2, next2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(kt, cur);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + 3 <= nk; kt += 3) {   // stage s uses buffer s % 3
+        step(kt, L0, L2);
+        step(kt + 1, L1, L0);
+        step(kt + 2, L2, L1);
+    }
+    if (kt < nk) step(kt, L0, L2);
+    if (kt + 1 < nk) step(kt + 1, L1, L0);
+}
+
 // grid: (ceil(max(f, fs) / 128), tile capacity); block 512; LDS kGemmLds.
 // A = E4M3 codes of x rows gathered through pair_of_row, scales xs [N][d/128].
 // The epilogue quantises each row's 128 H columns of the tile (one 1 x 128
 // group) to hq / hs.
-template <bool BLKW>
+template <bool BLKW, bool DMA>
 __global__ __launch_bounds__(kThreads) void gate_up_gemm_f8_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ xs, const void *__restrict__ wg,
     const void *__restrict__ wu, const float *__restrict__ sg, const float *__restrict__ su,
@@ -1092,7 +1219,32 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemm_f8_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    tile_mma_f8<BLKW>(xq, a_off, a_ok, b_base, b_off, d, xs, sa_off, sw_lo, sw_hi, m, ldsb, acc);
+    float *red;   // [128 rows][4 column waves] for the epilogue's row maxima
+    if constexpr (DMA) {
+        // direct-to-LDS: lane i of DMA j of wave w fetches tile row 8 (w n + j) + i / 8
+        // into chunk position i % 8 (source chunk (i % 8) ^ (row & 7))
+        __shared__ float red_l[kBM * 4];
+        red = red_l;
+        const int pos = lane & 7;
+        const uint8_t *a_src[kAPer], *b_src[kBPer];
+        const float *sa_row[kAPer];
+#pragma unroll
+        for (int j = 0; j < kAPer; ++j) {
+            const int r = 8 * (wave * kAPer + j) + (lane >> 3);
+            const int t = token_of(r < m ? r : 0);
+            a_src[j] = xq + (size_t)t * d + ((pos ^ (r & 7)) << 4);
+            sa_row[j] = xs + (size_t)t * nkb;
+        }
+#pragma unroll
+        for (int j = 0; j < kBPer; ++j) {
+            const int r = 8 * (wave * kBPer + j) + (lane >> 3);
+            b_src[j] = (r >= kHalf ? ubase : gbase) + (size_t)(r & (kHalf - 1)) * d + ((pos ^ (r & 7)) << 4);
+        }
+        tile_mma_dma_f8<BLKW>(a_src, b_src, sa_row, sw_lo, sw_hi, d, m, acc);
+    } else {
+        red = reinterpret_cast<float *>(ldsb);
+        tile_mma_f8<BLKW>(xq, a_off, a_ok, b_base, b_off, d, xs, sa_off, sw_lo, sw_hi, m, ldsb, acc);
+    }
 
     // SwiGLU: hv[mi][ni][q] is row wm*64 + mi*16 + lane%16, H column
     // c0 + wn*32 + ni*16 + 4*(lane/16) + q
@@ -1114,7 +1266,6 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemm_f8_kernel(
             for (int q = 0; q < 4; ++q) hv[mi][ni][q] = silu(acc[mi][ni][q] * gs[q]) * (acc[mi][ni + 2][q] * us[q]);
     }
     // row maxima over the tile's 128 columns: this wave's 32, then across the 4 column waves in LDS
-    float *red = reinterpret_cast<float *>(ldsb);   // [128 rows][4 column waves]
     float amax[4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
@@ -1158,7 +1309,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemm_f8_kernel(
 
 // grid: (ceil(d / 256), tile capacity); block 512; LDS kGemmLds.
 // A = E4M3 codes of the group's hidden rows (contiguous), scales hs.
-template <bool BLKW>
+template <bool BLKW, bool DMA>
 __global__ __launch_bounds__(kThreads) void down_gemm_f8_kernel(
     const uint8_t *__restrict__ hq, const float *__restrict__ hs, int ldh, const void *__restrict__ wd,
     const float *__restrict__ sd, const void *__restrict__ wsd, const float *__restrict__ ssd,
@@ -1213,7 +1364,27 @@ __global__ __launch_bounds__(kThreads) void down_gemm_f8_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    tile_mma_f8<BLKW>(hq, a_off, a_ok, b_base, b_off, fg, hs, sa_off, sw_lo, sw_hi, m, ldsb, acc);
+    if constexpr (DMA) {
+        // direct-to-LDS (see the gate/up kernel for the lane -> row map)
+        const int pos = lane & 7;
+        const uint8_t *a_src[kAPer], *b_src[kBPer];
+        const float *sa_row[kAPer];
+#pragma unroll
+        for (int j = 0; j < kAPer; ++j) {
+            const int r = 8 * (wave * kAPer + j) + (lane >> 3);
+            const size_t row = (size_t)row0 + (r < m ? r : 0);
+            a_src[j] = hq + row * ldh + ((pos ^ (r & 7)) << 4);
+            sa_row[j] = hs + row * nhb;
+        }
+#pragma unroll
+        for (int j = 0; j < kBPer; ++j) {
+            const int r = 8 * (wave * kBPer + j) + (lane >> 3);
+            b_src[j] = ebase + (size_t)(o0 + r < d ? o0 + r : 0) * fg + ((pos ^ (r & 7)) << 4);
+        }
+        tile_mma_dma_f8<BLKW>(a_src, b_src, sa_row, sw_lo, sw_hi, fg, m, acc);
+    } else {
+        tile_mma_f8<BLKW>(hq, a_off, a_ok, b_base, b_off, fg, hs, sa_off, sw_lo, sw_hi, m, ldsb, acc);
+    }
 
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
@@ -1355,16 +1526,22 @@ hipError_t gemm_kernels_init() {
     if ((e = allow_lds(gate_up_gemm_kernel<kWFp8Blk, false>)) != hipSuccess) return e;
     if ((e = allow_lds(gate_up_gemm_kernel<kWFp8Blk, true>)) != hipSuccess) return e;
     if ((e = allow_lds(down_gemm_kernel<kWFp8Blk>)) != hipSuccess) return e;
-    if ((e = allow_lds(gate_up_gemm_f8_kernel<true>)) != hipSuccess) return e;
-    if ((e = allow_lds(gate_up_gemm_f8_kernel<false>)) != hipSuccess) return e;
-    if ((e = allow_lds(down_gemm_f8_kernel<true>)) != hipSuccess) return e;
-    if ((e = allow_lds(down_gemm_f8_kernel<false>)) != hipSuccess) return e;
+    if ((e = allow_lds(gate_up_gemm_f8_kernel<true, false>)) != hipSuccess) return e;
+    if ((e = allow_lds(gate_up_gemm_f8_kernel<false, false>)) != hipSuccess) return e;
+    if ((e = allow_lds(down_gemm_f8_kernel<true, false>)) != hipSuccess) return e;
+    if ((e = allow_lds(down_gemm_f8_kernel<false, false>)) != hipSuccess) return e;
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(router_gemm_kernel),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)Geo<2>::kLds)) != hipSuccess)
         return e;
     // the direct-to-LDS kernels (bf16 x with bf16 or per-channel FP8 weights)
     // use static LDS only
     return hipSuccess;
+}
+
+// FP8 x FP8 products with every K range within kF8DmaMaxKb blocks run the
+// direct-to-LDS tile (its scales live in LDS for the whole K range)
+static bool f8_dma(const Plan &p) {
+    return p.d / 128 <= kF8DmaMaxKb && p.f / 128 <= kF8DmaMaxKb && p.fs / 128 <= kF8DmaMaxKb;
 }
 
 hipError_t launch_gate_up_gemm(const Plan &p) {
@@ -1375,12 +1552,13 @@ hipError_t launch_gate_up_gemm(const Plan &p) {
     if (p.aq) {
         hipError_t e = launch_quant_groups(p.x, 1, p.d, p.N, p.d, p.xq, p.d, p.xs, p.d / 128, p.stream);
         if (e != hipSuccess) return e;
-#define FGS_GUF(B)                                                                                            \
-    hipLaunchKernelGGL((gate_up_gemm_f8_kernel<B>), grid, block, kGemmLds, p.stream, p.xq, p.xs, p.W.w_gate,   \
-                       p.W.w_up, p.W.s_gate, p.W.s_up, p.W.ws_gate, p.W.ws_up, p.W.ss_gate, p.W.ss_up, p.tiles, \
-                       p.n_tiles, p.offsets, p.por, p.hq, p.hs, p.ldh, p.d, p.E, p.k, p.f, p.fs)
-        if (p.flags & MOE_FLAG_FP8_BLOCK128) FGS_GUF(true);
-        else FGS_GUF(false);
+#define FGS_GUF(B, D)                                                                                         \
+    hipLaunchKernelGGL((gate_up_gemm_f8_kernel<B, D>), grid, block, D ? 0 : kGemmLds, p.stream, p.xq, p.xs,        \
+                       p.W.w_gate, p.W.w_up, p.W.s_gate, p.W.s_up, p.W.ws_gate, p.W.ws_up, p.W.ss_gate, p.W.ss_up,  \
+                       p.tiles, p.n_tiles, p.offsets, p.por, p.hq, p.hs, p.ldh, p.d, p.E, p.k, p.f, p.fs)
+        const bool blk = (p.flags & MOE_FLAG_FP8_BLOCK128) != 0;
+        if (f8_dma(p)) { if (blk) FGS_GUF(true, true); else FGS_GUF(false, true); }
+        else { if (blk) FGS_GUF(true, false); else FGS_GUF(false, false); }
 #undef FGS_GUF
         return hipGetLastError();
     }
@@ -1402,11 +1580,13 @@ hipError_t launch_down_gemm(const Plan &p) {
     dim3 grid(gx, p.max_tiles + kXcds * kXcdTiles), block(kThreads);
     uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y);
     if (p.aq) {
-#define FGS_DNF(B)                                                                                             \
-    hipLaunchKernelGGL((down_gemm_f8_kernel<B>), grid, block, kGemmLds, p.stream, p.hq, p.hs, p.ldh, p.W.w_down, \
-                       p.W.s_down, p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs)
-        if (p.flags & MOE_FLAG_FP8_BLOCK128) FGS_DNF(true);
-        else FGS_DNF(false);
+#define FGS_DNF(B, D)                                                                                          \
+    hipLaunchKernelGGL((down_gemm_f8_kernel<B, D>), grid, block, D ? 0 : kGemmLds, p.stream, p.hq, p.hs, p.ldh,     \
+                       p.W.w_down, p.W.s_down, p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, Y, p.d, p.E, \
+                       p.f, p.fs)
+        const bool blk = (p.flags & MOE_FLAG_FP8_BLOCK128) != 0;
+        if (f8_dma(p)) { if (blk) FGS_DNF(true, true); else FGS_DNF(false, true); }
+        else { if (blk) FGS_DNF(true, false); else FGS_DNF(false, false); }
 #undef FGS_DNF
         return hipGetLastError();
     }
