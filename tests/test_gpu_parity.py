@@ -127,10 +127,12 @@ def test_quantize_groups_bit_exact(dtype, rows, cols):
     dict(n_tokens=16), dict(n_tokens=128), dict(n_tokens=600), dict(n_tokens=16, scale_block=0),
     dict(n_tokens=200, scale_block=0), dict(n_tokens=9, d_model=384, d_ff=256, d_ff_shared=128),
     dict(n_tokens=200, d_model=384, d_ff=256, d_ff_shared=128),
+    dict(n_tokens=150, d_model=3072, d_ff=256, d_ff_shared=128),   # 24 K blocks: the direct-to-LDS tile's limit
+    dict(n_tokens=150, d_model=3200, d_ff=256, d_ff_shared=128),   # 25 K blocks: the register-staged tile
 ])
 def test_fp8_act_quant_toy(over):
     """1 x 128 activation quantisation with FP8 x FP8 matmuls (MOE_FLAG_FP8_ACT_QUANT): stream and
-    GEMM paths, block and per-channel weight scales, odd block counts, f != f_s."""
+    GEMM paths, block and per-channel weight scales, odd block counts, f != f_s, both GEMM tiles."""
     base = dict(x_dtype="bf16", w_dtype="fp8", scale_block=128, d_ff=128, d_ff_shared=128)
     base.update(over)
     _run_full(get_config("toy", **base), act_quant=True)
