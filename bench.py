@@ -318,7 +318,7 @@ def main():
     layer_flops = (2.0 * N * d * E + gu_flops + dn_flops) * args.steps
 
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.json")
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}{'_aq' if args.act_quant else ''}.json")
     if os.path.exists(tpath):
         with open(tpath) as fh:
             tr = json.load(fh)
