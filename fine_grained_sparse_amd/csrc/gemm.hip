@@ -33,6 +33,8 @@
 //   tile_mma_dma_w8  bf16 activations, FP8 weights with per-channel scales:
 //                 the same with E4M3 weight rows (64 bytes per stage), four
 //                 stages, codes widened to bf16 (exact) as fragments are read;
+//                 tile_mma_dma_w8b the same for 128 x 128 block scales (each
+//                 stage's products folded in with its block's scale);
 //   tile_mma      every other combination: operands through registers into
 //                 two padded LDS stages (rows of 80 elements, measured free of
 //                 bank conflicts); FP8 weights are decoded to bf16 (exact) and
@@ -339,7 +341,8 @@ __device__ __forceinline__ void tile_mma(const void *a_base, const size_t (&a_of
 }
 
 // weight modes: bfloat16, FP8 with per-channel scales, FP8 with 128x128 block scales
-enum { kWBf16 = 0, kWFp8Row = 1, kWFp8Blk = 2 };
+// (kWFp8BlkDma: block scales on the direct-to-LDS tile, chosen by the launcher)
+enum { kWBf16 = 0, kWFp8Row = 1, kWFp8Blk = 2, kWFp8BlkDma = 3 };
 
 // ---------------------------------------------------------------- direct-to-LDS tile
 // bf16 x bf16 tile product with the operand tiles fetched straight into LDS
@@ -522,6 +525,9 @@ __device__ __forceinline__ void tile_mma_dma(const uint16_t *const (&a_src)[kAPe
 // 16 consecutive rows over all banks.  A fragment read takes the 8 code bytes
 // of its K range and widens them to bf16 exactly.  Synchronisation as in
 // tile_mma_dma, with stage kt+4 fetched into the buffer of stage kt.
+// K blocks of 128 whose scales a direct-to-LDS tile keeps in LDS for the whole
+// product (K <= 3072); larger K takes the register-staged tiles
+constexpr int kF8DmaMaxKb = 24;
 constexpr int kW8RowB = 64;                                  // weight-row bytes per stage
 constexpr int kW8StageB = kBM * kDmaRowB + kBN * kW8RowB;    // 32 KiB
 static_assert(4 * kW8StageB <= 160 * 1024, "four FP8-weight stages must fit one CU's LDS");
@@ -629,6 +635,112 @@ __device__ __forceinline__ void tile_mma_dma_w8(const uint16_t *const (&a_src)[k
     }
 }
 
+// ---- FP8 weights with 128 x 128 block scales, bf16 activations, direct to
+// LDS: the stages and swizzles of tile_mma_dma_w8 without its fragment
+// pipeline.  The scale changes every other 64-wide stage, so each stage's
+// products of a 16-row sub-tile are formed in fresh accumulators and folded
+// into the running sum times the block's scale (the two stages of a block
+// fold with the same scale), one sub-tile row behind the MFMAs as in
+// tile_mma_f8.  The weight block scales of the whole K range are staged in
+// LDS before the loop (K up to kF8DmaMaxKb blocks).
+__device__ __forceinline__ void tile_mma_dma_w8b(const uint16_t *const (&a_src)[kAPer],
+                                                 const uint8_t *const (&b_src)[2], const float *sw_lo,
+                                                 const float *sw_hi, int K, int m, f32x4_t (&acc)[4][4]) {
+    constexpr int G = kAPer + 2;   // DMAs per wave and stage
+    __shared__ __attribute__((aligned(16))) uint8_t L0[kW8StageB];
+    __shared__ __attribute__((aligned(16))) uint8_t L1[kW8StageB];
+    __shared__ __attribute__((aligned(16))) uint8_t L2[kW8StageB];
+    __shared__ __attribute__((aligned(16))) uint8_t L3[kW8StageB];
+    __shared__ float sw_l[2][kF8DmaMaxKb];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / kWN, wn = wave % kWN;
+    const int fr = lane & 15, fg = lane >> 4;
+    const int nk = K / kBK, nkb = K / 128;
+    auto fetch = [&](int kt, uint8_t *buf) {
+        const int k0 = kt * kBK;
+#pragma unroll
+        for (int j = 0; j < kAPer; ++j) dma16(a_src[j] + k0, buf + (wave * kAPer + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dma16(b_src[j] + k0, buf + kBM * kDmaRowB + (wave * 2 + j) * 1024);
+    };
+    auto frag_a = [&](const uint8_t *base, int r, int c) {
+        return *reinterpret_cast<const uint4 *>(base + r * kDmaRowB + ((c ^ (r & 7)) << 4));
+    };
+    auto frag_b = [&](const uint8_t *base, int r, int u) {
+        const uint2 q = *reinterpret_cast<const uint2 *>(base + kBM * kDmaRowB + r * kW8RowB +
+                                                         ((((u >> 1) ^ (r >> 2)) & 3) << 4) + ((u & 1) << 3));
+        return e4m3x8_to_bf16x8(q);
+    };
+    // this wave's DMAs of stage kt landed; stages kt+1, kt+2 (issued) may stay in flight
+    auto wait_own = [&](int kt) {
+        const int later = min(2, nk - 1 - kt);
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(2 * G));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(G));
+        else __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
+    };
+
+    fetch(0, L0);
+    if (nk > 1) fetch(1, L1);
+    if (nk > 2) fetch(2, L2);
+    const float wv = tid < 2 * nkb ? (tid < nkb ? sw_lo[tid] : sw_hi[tid - nkb]) : 0.f;
+    if (tid < 2 * nkb) sw_l[tid / nkb][tid % nkb] = wv;   // waits for the loads above: prologue only
+
+    const int live = min(4, max(0, (m - wm * 64 + 15) / 16));
+    auto compute = [&](int kt, const uint8_t *cur) {
+        uint4 bf[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) bf[h][ni] = frag_b(cur, b_row_of(wn, ni) + fr, 4 * h + fg);
+        const float slo = sw_l[0][kt >> 1], shi = sw_l[1][kt >> 1];
+        auto products = [&](int mi, f32x4_t (&pr)[4]) {
+            const int r = wm * 64 + mi * 16 + fr;
+            const uint4 a0 = frag_a(cur, r, fg), a1 = frag_a(cur, r, 4 + fg);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                pr[ni] = mfma_bf16(bf[1][ni], a1, mfma_bf16(bf[0][ni], a0, f32x4_t{0.f, 0.f, 0.f, 0.f}));
+        };
+        auto fold = [&](int mi, const f32x4_t (&pr)[4]) {
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                const float c = ni < 2 ? slo : shi;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[mi][ni][q] = fmaf(pr[ni][q], c, acc[mi][ni][q]);
+            }
+        };
+        f32x4_t p0[4], p1[4];
+        if (live > 0) products(0, p0);
+        if (live > 1) products(1, p1);
+        if (live > 0) fold(0, p0);
+        if (live > 2) products(2, p0);
+        if (live > 1) fold(1, p1);
+        if (live > 3) products(3, p1);
+        if (live > 2) fold(2, p0);
+        if (live > 3) fold(3, p1);
+    };
+    // stage kt: own DMAs landed, barrier (every wave's stage kt visible, every
+    // wave done with stage kt - 1), fetch stage kt + 3 into the buffer of
+    // stage kt - 1, multiply
+    auto step = [&](int kt, const uint8_t *cur, uint8_t *refill) {
+        wait_own(kt);
+        lds_barrier();
+        if (kt + 3 < nk) fetch(kt + 3, refill);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(kt, cur);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + 4 <= nk; kt += 4) {   // stage s uses buffer s % 4
+        step(kt, L0, L3);
+        step(kt + 1, L1, L0);
+        step(kt + 2, L2, L1);
+        step(kt + 3, L3, L2);
+    }
+    if (kt < nk) step(kt, L0, L3);
+    if (kt + 1 < nk) step(kt + 1, L1, L0);
+    if (kt + 2 < nk) step(kt + 2, L2, L1);
+}
+
 // grid: (ceil(max(f, fs) / 128), tile capacity); block 512; LDS kGemmLds
 // (bf16 x and weights: none; the direct-to-LDS tile uses kGemmLdsDma of static LDS)
 template <int WM, bool XF32>
@@ -638,7 +750,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
     const void *__restrict__ wsu, const float *__restrict__ ssg, const float *__restrict__ ssu,
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ por, uint16_t *__restrict__ H, int ldh, int d, int E, int k, int f, int fs) {
-    constexpr bool FP8 = WM != kWBf16, BLK = WM == kWFp8Blk;
+    constexpr bool FP8 = WM != kWBf16, BLK = WM == kWFp8Blk || WM == kWFp8BlkDma;
     extern __shared__ uint16_t lds[];
     int item;
     if (!xcd_item(*n_tiles * (int)gridDim.x, item)) return;
@@ -699,7 +811,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
             b_src[j] = wb + (wrow0 + (c < fg ? c : c0)) * (size_t)d + ((pos ^ (r & 7)) << 3);
         }
         tile_mma_dma(a_src, b_src, d, m, acc);
-    } else if constexpr (WM == kWFp8Row && !XF32) {
+    } else if constexpr ((WM == kWFp8Row || WM == kWFp8BlkDma) && !XF32) {
         // FP8 weights direct to LDS: activations as in the bf16 tile; lane i
         // of weight DMA j of wave w fills weight row 16 (2 w + j) + i / 4 at
         // chunk position i % 4 (source chunk (i % 4) ^ ((row >> 2) & 3))
@@ -720,7 +832,13 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
             const uint8_t *wb = (const uint8_t *)(up ? (shared ? wsu : wu) : (shared ? wsg : wg));
             b_src[j] = wb + (wrow0 + (c < fg ? c : c0)) * (size_t)d + ((((lane & 3) ^ (r >> 2)) & 3) << 4);
         }
-        tile_mma_dma_w8(a_src, b_src, d, m, acc);
+        if constexpr (WM == kWFp8BlkDma) {
+            // the tile's 128 gate (and up) rows are output block c0/128
+            const size_t sb = ((shared ? 0 : (size_t)g * (f / 128)) + c0 / 128) * (size_t)(d / 128);
+            tile_mma_dma_w8b(a_src, b_src, (shared ? ssg : sg) + sb, (shared ? ssu : su) + sb, d, m, acc);
+        } else {
+            tile_mma_dma_w8(a_src, b_src, d, m, acc);
+        }
     } else {
         // block scales: the tile's 128 gate (and up) rows are output block c0/128
         const float *sc_lo = nullptr, *sc_hi = nullptr;
@@ -769,7 +887,7 @@ __global__ __launch_bounds__(kThreads) void down_gemm_kernel(
     const void *__restrict__ wsd, const float *__restrict__ ssd, const int32_t *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets, uint16_t *__restrict__ Y, int d, int E,
     int f, int fs) {
-    constexpr bool FP8 = WM != kWBf16, BLK = WM == kWFp8Blk;
+    constexpr bool FP8 = WM != kWBf16, BLK = WM == kWFp8Blk || WM == kWFp8BlkDma;
     extern __shared__ uint16_t lds[];
     int item;
     if (!xcd_item(*n_tiles * (int)gridDim.x, item)) return;
@@ -819,7 +937,7 @@ __global__ __launch_bounds__(kThreads) void down_gemm_kernel(
             b_src[j] = (const uint16_t *)base + (obase + (o0 + r < d ? o0 + r : 0)) * (size_t)fg + ((pos ^ (r & 7)) << 3);
         }
         tile_mma_dma(a_src, b_src, fg, m, acc);
-    } else if constexpr (WM == kWFp8Row) {
+    } else if constexpr (WM == kWFp8Row || WM == kWFp8BlkDma) {
         // FP8 weights direct to LDS (see the gate/up kernel for the lane -> row map)
         const int lane = tid & 63, w = tid >> 6, pos = lane & 7;
         const uint16_t *a_src[kAPer];
@@ -835,7 +953,16 @@ __global__ __launch_bounds__(kThreads) void down_gemm_kernel(
             b_src[j] = (const uint8_t *)base + (obase + (o0 + r < d ? o0 + r : 0)) * (size_t)fg +
                        ((((lane & 3) ^ (r >> 2)) & 3) << 4);
         }
-        tile_mma_dma_w8(a_src, b_src, fg, m, acc);
+        if constexpr (WM == kWFp8BlkDma) {
+            // B rows [0, 128) are output block o0/128, rows [128, 256) the next
+            // one (clamped at the end of d: those rows are never stored)
+            const int nkb = fg / 128, nob = d / 128, ob = o0 / 128;
+            const float *sp = shared ? ssd : sd + (size_t)g * nob * nkb;
+            tile_mma_dma_w8b(a_src, b_src, sp + (size_t)ob * nkb, sp + (size_t)(ob + 1 < nob ? ob + 1 : ob) * nkb,
+                             fg, m, acc);
+        } else {
+            tile_mma_dma_w8(a_src, b_src, fg, m, acc);
+        }
     } else {
         // block scales: B rows [0, 128) are output block o0/128, rows [128, 256)
         // the next one (clamped at the end of d: those rows are never stored)
@@ -1037,7 +1164,6 @@ __device__ __forceinline__ void tile_mma_f8(const uint8_t *a_base, const size_t 
 // LDS once, before the loop (loads the compiler tracks must not follow the
 // DMAs it cannot see: its waits for them would also wait for every DMA), so K
 // is limited to kF8DmaMaxKb blocks.
-constexpr int kF8DmaMaxKb = 24;
 static_assert(3 * kDmaStageB + kF8DmaMaxKb * (kBM + 2) * 4 + kBM * 4 * 4 <= 160 * 1024,
               "stages, scales and the epilogue's row maxima must fit one CU's LDS");
 
@@ -1540,6 +1666,10 @@ hipError_t gemm_kernels_init() {
 
 // FP8 x FP8 products with every K range within kF8DmaMaxKb blocks run the
 // direct-to-LDS tile (its scales live in LDS for the whole K range)
+static bool w8b_dma(const Plan &p) {   // block-scaled FP8 weights, bf16 activations: the same K bound
+    return p.d / 128 <= kF8DmaMaxKb && p.f / 128 <= kF8DmaMaxKb && p.fs / 128 <= kF8DmaMaxKb;
+}
+
 static bool f8_dma(const Plan &p) {
     return p.d / 128 <= kF8DmaMaxKb && p.f / 128 <= kF8DmaMaxKb && p.fs / 128 <= kF8DmaMaxKb;
 }
@@ -1564,12 +1694,17 @@ hipError_t launch_gate_up_gemm(const Plan &p) {
     }
 #define FGS_GUG(WM, XF)                                                                                         \
     hipLaunchKernelGGL((gate_up_gemm_kernel<WM, XF>), grid, block,                                               \
-                       ((WM == kWBf16 || WM == kWFp8Row) && !XF) ? 0 : kGemmLds, p.stream, p.x, p.W.w_gate, p.W.w_up, \
+                       ((WM == kWBf16 || WM == kWFp8Row || WM == kWFp8BlkDma) && !XF) ? 0 : kGemmLds, p.stream, p.x,    \
+                       p.W.w_gate, p.W.w_up,                                                                           \
                        p.W.s_gate, p.W.s_up, p.W.ws_gate, p.W.ws_up, p.W.ss_gate, p.W.ss_up, p.tiles, p.n_tiles,  \
                        p.offsets, p.por, p.H, p.ldh, p.d, p.E, p.k, p.f, p.fs)
     const bool xf32 = p.xdt == MOE_DTYPE_F32;
     if (p.wdt != MOE_DTYPE_FP8_E4M3) { if (xf32) FGS_GUG(kWBf16, true); else FGS_GUG(kWBf16, false); }
-    else if (p.flags & MOE_FLAG_FP8_BLOCK128) { if (xf32) FGS_GUG(kWFp8Blk, true); else FGS_GUG(kWFp8Blk, false); }
+    else if (p.flags & MOE_FLAG_FP8_BLOCK128) {
+        if (xf32) FGS_GUG(kWFp8Blk, true);
+        else if (w8b_dma(p)) FGS_GUG(kWFp8BlkDma, false);
+        else FGS_GUG(kWFp8Blk, false);
+    }
     else { if (xf32) FGS_GUG(kWFp8Row, true); else FGS_GUG(kWFp8Row, false); }
 #undef FGS_GUG
     return hipGetLastError();
@@ -1591,11 +1726,15 @@ hipError_t launch_down_gemm(const Plan &p) {
         return hipGetLastError();
     }
 #define FGS_DNG(WM)                                                                                       \
-    hipLaunchKernelGGL((down_gemm_kernel<WM>), grid, block, (WM == kWBf16 || WM == kWFp8Row) ? 0 : kGemmLds, p.stream, p.H, \
+    hipLaunchKernelGGL((down_gemm_kernel<WM>), grid, block,                                                       \
+                       (WM == kWBf16 || WM == kWFp8Row || WM == kWFp8BlkDma) ? 0 : kGemmLds, p.stream, p.H,             \
                        p.ldh, p.W.w_down, p.W.s_down,                                                                \
                        p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs)
     if (p.wdt != MOE_DTYPE_FP8_E4M3) FGS_DNG(kWBf16);
-    else if (p.flags & MOE_FLAG_FP8_BLOCK128) FGS_DNG(kWFp8Blk);
+    else if (p.flags & MOE_FLAG_FP8_BLOCK128) {
+        if (w8b_dma(p)) FGS_DNG(kWFp8BlkDma);
+        else FGS_DNG(kWFp8Blk);
+    }
     else FGS_DNG(kWFp8Row);
 #undef FGS_DNG
     return hipGetLastError();

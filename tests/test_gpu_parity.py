@@ -81,10 +81,13 @@ def test_renormalized_gate(cfg_name, over):
     dict(n_tokens=16), dict(n_tokens=128), dict(n_tokens=600),
     dict(n_tokens=9, x_dtype="bf16", d_model=384, d_ff=256, d_ff_shared=128),
     dict(n_tokens=200, x_dtype="bf16", d_model=384, d_ff=256, d_ff_shared=128),
+    dict(n_tokens=150, x_dtype="bf16", d_model=3072, d_ff=256, d_ff_shared=128),   # 24 K blocks: direct-to-LDS tile
+    dict(n_tokens=150, x_dtype="bf16", d_model=3200, d_ff=256, d_ff_shared=128),   # 25 K blocks: register-staged tile
 ])
 def test_fp8_block_scales_toy(over):
     """FP8 weights with one scale per 128 x 128 block (MOE_FLAG_FP8_BLOCK128): stream and GEMM
-    paths, FP32 and bf16 activations, an odd count of 128-row output blocks, f != f_s."""
+    paths, FP32 and bf16 activations, an odd count of 128-row output blocks, f != f_s, both GEMM
+    tiles."""
     base = dict(w_dtype="fp8", scale_block=128, d_ff=128, d_ff_shared=128)
     base.update(over)
     _run_full(get_config("toy", **base))
