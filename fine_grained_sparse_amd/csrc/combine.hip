@@ -12,32 +12,36 @@
 
 namespace fgs {
 
-// VEC consecutive values of Y as floats: 8 bf16 (16 bytes) or 4 FP32 (16 bytes)
+// VEC consecutive values of Y as floats: 8 bf16 (16 bytes) or 4 FP32 (16
+// bytes).  Y is read exactly once: non-temporal loads.
 template <bool YBF16>
 __device__ __forceinline__ void load_y(const void *Y, size_t elem, float (&v)[YBF16 ? 8 : 4]) {
     if constexpr (YBF16) {
-        const uint4 q = *reinterpret_cast<const uint4 *>((const uint16_t *)Y + elem);
+        const uint4 q = ld_stream16((const uint16_t *)Y + elem);
         v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
         v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
     } else {
-        const float4 q = *reinterpret_cast<const float4 *>((const float *)Y + elem);
-        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+        const uint4 q = ld_stream16((const float *)Y + elem);
+        v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y); v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
     }
 }
 
-// grid: (N, column blocks); each thread combines VEC consecutive columns per pass
-template <bool BF16OUT, bool YBF16>
+// grid: (N, column blocks); each thread combines VEC consecutive columns per pass.
+// KT: the top-k (6 or 8) as a constant, or 0 for any k <= 8 (slots past k then
+// repeat slot k-1 and are not added)
+template <bool BF16OUT, bool YBF16, int KT>
 __global__ __launch_bounds__(1024) void combine_kernel(
     const void *__restrict__ Y, const float *__restrict__ tw, const int32_t *__restrict__ rop, void *out,
-    int N, int d, int k, bool accumulate) {
+    int N, int d, int k_arg, bool accumulate) {
     constexpr int VEC = YBF16 ? 8 : 4;
+    constexpr int KS = KT ? KT : 8;   // slots loaded
+    const int k = KT ? KT : k_arg;
     const int t = blockIdx.x;
-    // the token's k <= 8 rows and weights: uniform addresses, so scalar loads
-    // (slots past k repeat slot k-1 and are not added)
-    int rs[8];
-    float ws[8];
+    // the token's rows and weights: uniform addresses, so scalar loads
+    int rs[KS];
+    float ws[KS];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < KS; ++j) {
         const int jj = j < k ? j : k - 1;
         rs[j] = rop[(size_t)t * k + jj];
         ws[j] = tw[(size_t)t * k + jj];
@@ -45,12 +49,12 @@ __global__ __launch_bounds__(1024) void combine_kernel(
     const size_t shared_row = (size_t)N * k + t;
     for (int c = (blockIdx.y * blockDim.x + threadIdx.x) * VEC; c < d; c += gridDim.y * blockDim.x * VEC) {
         // all rows are requested at once, then added in slot order
-        float a[VEC], y[8][VEC];
+        float a[VEC], y[KS][VEC];
         load_y<YBF16>(Y, shared_row * d + c, a);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) load_y<YBF16>(Y, (size_t)rs[j] * d + c, y[j]);
+        for (int j = 0; j < KS; ++j) load_y<YBF16>(Y, (size_t)rs[j] * d + c, y[j]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {   // per-value selects, not branches: the loads stay ahead of every use
+        for (int j = 0; j < KS; ++j) {   // per-value selects, not branches: the loads stay ahead of every use
             const bool on = j < k;
 #pragma unroll
             for (int q = 0; q < VEC; ++q) a[q] = on ? fmaf(ws[j], y[j][q], a[q]) : a[q];
@@ -92,14 +96,21 @@ hipError_t launch_combine(const Plan &p) {
     const int vec = ybf16 ? 8 : 4;
     const int threads = ybf16 ? min(1024, ((p.d / vec + 63) / 64) * 64) : 256;
     dim3 grid(p.N, (p.d + threads * vec - 1) / (threads * vec)), block(threads);
-#define FGS_COMBINE(OB, YB) hipLaunchKernelGGL((combine_kernel<OB, YB>), grid, block, 0, p.stream, p.Y, p.tw, p.rop, \
-                                             p.out, p.N, p.d, p.k, acc)
+#define FGS_COMBINE2(OB, YB, KT) hipLaunchKernelGGL((combine_kernel<OB, YB, KT>), grid, block, 0, p.stream, p.Y, p.tw, \
+                                                  p.rop, p.out, p.N, p.d, p.k, acc)
+#define FGS_COMBINE(OB, YB)                                       \
+    do {                                                          \
+        if (p.k == 6) FGS_COMBINE2(OB, YB, 6);                    \
+        else if (p.k == 8) FGS_COMBINE2(OB, YB, 8);               \
+        else FGS_COMBINE2(OB, YB, 0);                             \
+    } while (0)
     if (p.xdt == MOE_DTYPE_BF16) {
         if (ybf16) FGS_COMBINE(true, true); else FGS_COMBINE(true, false);
     } else {
         if (ybf16) FGS_COMBINE(false, true); else FGS_COMBINE(false, false);
     }
 #undef FGS_COMBINE
+#undef FGS_COMBINE2
     return hipGetLastError();
 }
 

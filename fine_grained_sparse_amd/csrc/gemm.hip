@@ -56,7 +56,7 @@ constexpr int kBK = 64;         // K per stage
 constexpr int kLdsStride = 80;  // padded row length in LDS (elements): conflict-free 16-byte fragment reads
 
 // Tile geometry for WN column waves: 2 x WN waves (128 * WN threads), tile
-// 128 rows x 64*WN columns.  Expert GEMMs use WN = 4, the router WN = 2.
+// 128 rows x 64*WN columns (the GEMMs use WN = 4).
 template <int WN>
 struct Geo {
     static constexpr int kThreads = 128 * WN;
@@ -1549,70 +1549,80 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float *__restri
                                                            int32_t *__restrict__ flags, int E, int d) {
     const int e = blockIdx.x;
     uint16_t *row = w3 + (size_t)e * 3 * d;
+    const float4 *src = reinterpret_cast<const float4 *>(rw + (size_t)e * d);
     int any = 0;
-    for (int kx = threadIdx.x; kx < d; kx += blockDim.x) {
-        const float v = rw[(size_t)e * d + kx];
-        const uint32_t uh = __float_as_uint(v) & 0xFFFF0000u;
-        const float r1 = v - __uint_as_float(uh);
-        const uint32_t um = __float_as_uint(r1) & 0xFFFF0000u;
-        const float r2 = r1 - __uint_as_float(um);
-        const uint16_t m = (uint16_t)(um >> 16), l = (uint16_t)f32_to_bf16_rne(r2);
-        row[kx] = (uint16_t)(uh >> 16);
-        row[d + kx] = m;
-        row[2 * d + kx] = l;
-        any |= ((m | l) & 0x7FFF) != 0;   // a -0 term contributes nothing either
+    // four weights per thread and pass (d is a multiple of 64): one 16-byte
+    // load, three 8-byte stores
+    for (int q = threadIdx.x; q < d / 4; q += blockDim.x) {
+        const float4 v4 = src[q];
+        const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+        uint32_t hw[2] = {0, 0}, mw[2] = {0, 0}, lw[2] = {0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t uh = __float_as_uint(v[i]) & 0xFFFF0000u;
+            const float r1 = v[i] - __uint_as_float(uh);
+            const uint32_t um = __float_as_uint(r1) & 0xFFFF0000u;
+            const float r2 = r1 - __uint_as_float(um);
+            const uint32_t m = um >> 16, l = f32_to_bf16_rne(r2);
+            hw[i >> 1] |= (uh >> 16) << (16 * (i & 1));
+            mw[i >> 1] |= m << (16 * (i & 1));
+            lw[i >> 1] |= l << (16 * (i & 1));
+            any |= ((m | l) & 0x7FFF) != 0;   // a -0 term contributes nothing either
+        }
+        *reinterpret_cast<uint2 *>(row + 4 * q) = make_uint2(hw[0], hw[1]);
+        *reinterpret_cast<uint2 *>(row + d + 4 * q) = make_uint2(mw[0], mw[1]);
+        *reinterpret_cast<uint2 *>(row + 2 * d + 4 * q) = make_uint2(lw[0], lw[1]);
     }
     any = __syncthreads_or(any);
     if (threadIdx.x == 0) flags[e] = any;
 }
 
-// grid: (ceil(E / 128), ceil(N / 128), ks); block 256; LDS Geo<2>::kLds.
-// Slice z covers GEMM columns [z*3d/ks, (z+1)*3d/ks) and writes partial[z].
-__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__restrict__ x,
-                                                          const uint16_t *__restrict__ w3,
-                                                          const int32_t *__restrict__ flags, float *__restrict__ partial,
-                                                          int N, int d, int E) {
-    using G = Geo<2>;
-    extern __shared__ uint16_t lds[];
-    const int t0 = blockIdx.y * kBM, e0 = blockIdx.x * G::kBN;
-    // slices 0 .. ks/3-1 cover the hi term, then mid, then lo; a mid or lo
-    // slice whose experts all have zero terms there is skipped (its partial
-    // sums would be exactly zero; the top-k does not read them)
-    if ((int)blockIdx.z >= (int)gridDim.z / 3) {
-        const int e = e0 + (int)threadIdx.x;
-        const int any = __syncthreads_or(threadIdx.x < G::kBN && e < E ? flags[e] : 0);
+// The product runs on the direct-to-LDS tile: 128 tokens x 256 experts per
+// workgroup, x and W3 rows fetched straight into three LDS stages (the
+// register-staged 128 x 128 tile took 46 us at N = 8192 against 30 us).
+// grid: (ceil(E / 256), ceil(N / 128), ks); block 512; static LDS.
+// Slice z covers GEMM columns [z*3d/ks, (z+1)*3d/ks) (never two terms, so
+// its x columns are that range modulo d) and writes partial[z].
+__global__ __launch_bounds__(kThreads) void router_gemm_dma_kernel(const uint16_t *__restrict__ x,
+                                                                   const uint16_t *__restrict__ w3,
+                                                                   const int32_t *__restrict__ flags,
+                                                                   float *__restrict__ partial, int N, int d, int E) {
+    const int t0 = blockIdx.y * kBM, e0 = blockIdx.x * kBN;
+    const int tid = threadIdx.x;
+    if ((int)blockIdx.z >= (int)gridDim.z / 3) {   // mid or lo slice: skipped when all its experts' terms are zero
+        const int e = e0 + tid;
+        const int any = __syncthreads_or(tid < kBN && e < E ? flags[e] : 0);
         if (!any) return;
     }
     const int m = min(kBM, N - t0);
-    const int tid = threadIdx.x;
-    size_t a_off[G::kAPer], b_off[G::kBPer];
-    bool a_ok[G::kAPer];
-    const void *b_base[G::kBPer];
+    const int kslice = 3 * d / (int)gridDim.z;
+    const int kz = (int)blockIdx.z * kslice, ka = kz % d;
+    // lane i of DMA j of wave w fills tile row 8 (w n + j) + i / 8 at swizzled chunk i % 8
+    const int lane = tid & 63, w = tid >> 6, pos = lane & 7;
+    const uint16_t *a_src[kAPer], *b_src[kBPer];
 #pragma unroll
-    for (int j = 0; j < G::kAPer; ++j) {
-        const int r = (tid >> 3) + (G::kThreads / 8) * j;
-        a_ok[j] = r < m;
-        a_off[j] = (size_t)(t0 + (a_ok[j] ? r : 0)) * d;
+    for (int j = 0; j < kAPer; ++j) {
+        const int r = 8 * (w * kAPer + j) + (lane >> 3);
+        a_src[j] = x + (size_t)(t0 + (r < m ? r : 0)) * d + ka + ((pos ^ (r & 7)) << 3);
     }
 #pragma unroll
-    for (int j = 0; j < G::kBPer; ++j) {
-        const int r = (tid >> 3) + (G::kThreads / 8) * j;
-        b_base[j] = w3;
-        b_off[j] = (size_t)(e0 + r < E ? e0 + r : 0) * 3 * d;  // rows past E re-read row 0; never stored
+    for (int j = 0; j < kBPer; ++j) {
+        const int r = 8 * (w * kBPer + j) + (lane >> 3);
+        // rows past E re-read row 0; never stored
+        b_src[j] = w3 + (size_t)(e0 + r < E ? e0 + r : 0) * 3 * d + kz + ((pos ^ (r & 7)) << 3);
     }
     f32x4_t acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int kslice = 3 * d / (int)gridDim.z;
-    tile_mma<false, false, 2>(x, a_off, a_ok, b_base, b_off, (int)blockIdx.z * kslice, kslice, d, m, lds, acc);
-    float *logits = partial + (size_t)blockIdx.z * N * E;
+    tile_mma_dma(a_src, b_src, kslice, m, acc);
 
-    const int lane = tid & 63, wave = tid >> 6, wm = wave / 2, wn = wave % 2;
+    float *logits = partial + (size_t)blockIdx.z * N * E;
+    const int wave = tid >> 6, wm = wave / kWN, wn = wave % kWN;
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
-        const int e = e0 + b_row_of<2>(wn, ni) + (lane >> 4) * 4;
+        const int e = e0 + b_row_of(wn, ni) + (lane >> 4) * 4;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             const int r = wm * 64 + mi * 16 + (lane & 15);
@@ -1633,9 +1643,9 @@ hipError_t launch_router_gemm(const Plan &p, uint16_t *w3) {
     hipLaunchKernelGGL(router_split_kernel, dim3(p.E), dim3(256), 0, p.stream, p.rw, w3, p.rflags, p.E, p.d);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid((p.E + Geo<2>::kBN - 1) / Geo<2>::kBN, (p.N + kBM - 1) / kBM, p.ks);
-    hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(Geo<2>::kThreads), Geo<2>::kLds, p.stream,
-                       (const uint16_t *)p.x, w3, p.rflags, p.partial, p.N, p.d, p.E);
+    dim3 grid((p.E + kBN - 1) / kBN, (p.N + kBM - 1) / kBM, p.ks);
+    hipLaunchKernelGGL(router_gemm_dma_kernel, grid, dim3(kThreads), 0, p.stream, (const uint16_t *)p.x, w3,
+                       p.rflags, p.partial, p.N, p.d, p.E);
     return hipGetLastError();
 }
 
@@ -1656,11 +1666,8 @@ hipError_t gemm_kernels_init() {
     if ((e = allow_lds(gate_up_gemm_f8_kernel<false, false>)) != hipSuccess) return e;
     if ((e = allow_lds(down_gemm_f8_kernel<true, false>)) != hipSuccess) return e;
     if ((e = allow_lds(down_gemm_f8_kernel<false, false>)) != hipSuccess) return e;
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(router_gemm_kernel),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)Geo<2>::kLds)) != hipSuccess)
-        return e;
-    // the direct-to-LDS kernels (bf16 x with bf16 or per-channel FP8 weights)
-    // use static LDS only
+    // the direct-to-LDS kernels (bf16 x with bf16 or FP8 weights, FP8 x FP8
+    // within 24 K blocks, the router GEMM) use static LDS only
     return hipSuccess;
 }
 

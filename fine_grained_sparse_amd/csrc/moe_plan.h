@@ -85,14 +85,14 @@ constexpr int kRouterGemmN = 64;
 inline bool router_gemm(int N, int xdt) { return xdt == MOE_DTYPE_BF16 && N > kRouterGemmN; }
 // k-slices of the router GEMM: 3 c slices, c per split term (hi, mid, lo),
 // so that a slice never straddles two terms and the slices of all-zero terms
-// can be skipped; c divides the d/64 K stages of a term and is raised until
-// the hi term alone gives about 512 workgroups (ks <= 9).
+// can be skipped; c <= 4 divides the d/64 K stages of a term and is raised
+// while the hi term alone fills at most one 128 x 256 tile per CU (256).
 inline int router_gemm_ks(int N, int d, int E) {
-    const long wgs = (long)((N + 127) / 128) * ((E + 127) / 128);
+    const long wgs = (long)((N + 127) / 128) * ((E + 255) / 256);
     const int stages = d / 64;
     int c = 1;
-    for (int cand : {2, 3})
-        if (stages % cand == 0 && wgs * c < 512) c = cand;
+    for (int cand : {2, 3, 4})
+        if (stages % cand == 0 && wgs * cand <= 256) c = cand;
     return 3 * c;
 }
 inline RouterTiling router_tiling(int N, int d, int E) {

@@ -60,31 +60,36 @@ __global__ __launch_bounds__(256) void prenorm_kernel(const void *__restrict__ r
     }
 }
 
+// four values of Y as floats; Y is read exactly once: non-temporal loads
 template <bool YBF16>
 __device__ __forceinline__ float4 load_y4n(const void *Y, size_t elem) {
     if constexpr (YBF16) {
-        const uint2 v = *reinterpret_cast<const uint2 *>((const uint16_t *)Y + elem);
+        const uint2 v = ld_stream8((const uint16_t *)Y + elem);
         return make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
     } else {
-        return *reinterpret_cast<const float4 *>((const float *)Y + elem);
+        const uint4 v = ld_stream16((const float *)Y + elem);
+        return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
     }
 }
 
-// grid: N; block 256; dynamic LDS d floats (the token's layer output)
-template <bool XBF16, bool YBF16>
+// grid: N; block 256; dynamic LDS d floats (the token's layer output).
+// KT: the top-k (6 or 8) as a constant, or 0 for any k <= 8 (slots past k
+// then repeat slot k-1 and are not added)
+template <bool XBF16, bool YBF16, int KT>
 __global__ __launch_bounds__(256) void combine_block_kernel(const void *__restrict__ Y, const float *__restrict__ tw,
                                                             const int32_t *__restrict__ rop,
                                                             const float *__restrict__ g, float eps, void *resid,
-                                                            int N, int d, int k) {
+                                                            int N, int d, int k_arg) {
     extern __shared__ float yrow[];
     __shared__ float red[4];
+    constexpr int KS = KT ? KT : 8;   // slots loaded
+    const int k = KT ? KT : k_arg;
     const int t = blockIdx.x;
-    // the token's k <= 8 rows and weights: uniform addresses, so scalar loads
-    // (slots past k repeat slot k-1 and are not added)
-    int rs[8];
-    float ws[8];
+    // the token's rows and weights: uniform addresses, so scalar loads
+    int rs[KS];
+    float ws[KS];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < KS; ++j) {
         const int jj = j < k ? j : k - 1;
         rs[j] = rop[(size_t)t * k + jj];
         ws[j] = tw[(size_t)t * k + jj];
@@ -94,11 +99,11 @@ __global__ __launch_bounds__(256) void combine_block_kernel(const void *__restri
     for (int c = threadIdx.x * 4; c < d; c += 1024) {
         // every slot's row requested at once, added in slot order
         float4 a = load_y4n<YBF16>(Y, shared_row * d + c);
-        float4 y[8];
+        float4 y[KS];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) y[j] = load_y4n<YBF16>(Y, (size_t)rs[j] * d + c);
+        for (int j = 0; j < KS; ++j) y[j] = load_y4n<YBF16>(Y, (size_t)rs[j] * d + c);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {   // per-value selects, not branches: the loads stay ahead of every use
+        for (int j = 0; j < KS; ++j) {   // per-value selects, not branches: the loads stay ahead of every use
             const bool on = j < k;
             a.x = on ? fmaf(ws[j], y[j].x, a.x) : a.x;
             a.y = on ? fmaf(ws[j], y[j].y, a.y) : a.y;
@@ -131,14 +136,21 @@ hipError_t launch_prenorm(const Plan &p, const void *resid, const float *g, floa
 hipError_t launch_combine_block(const Plan &p) {
     const size_t lds = (size_t)p.d * sizeof(float);
     const bool ybf16 = !p.use_stream;
-#define FGS_CB(XB, YB) hipLaunchKernelGGL((combine_block_kernel<XB, YB>), dim3(p.N), dim3(256), lds, p.stream, \
-                                          p.Y, p.tw, p.rop, p.norm_post, p.eps, p.out, p.N, p.d, p.k)
+#define FGS_CB2(XB, YB, KT) hipLaunchKernelGGL((combine_block_kernel<XB, YB, KT>), dim3(p.N), dim3(256), lds, \
+                                               p.stream, p.Y, p.tw, p.rop, p.norm_post, p.eps, p.out, p.N, p.d, p.k)
+#define FGS_CB(XB, YB)                                 \
+    do {                                               \
+        if (p.k == 6) FGS_CB2(XB, YB, 6);              \
+        else if (p.k == 8) FGS_CB2(XB, YB, 8);         \
+        else FGS_CB2(XB, YB, 0);                       \
+    } while (0)
     if (p.xdt == MOE_DTYPE_BF16) {
         if (ybf16) FGS_CB(true, true); else FGS_CB(true, false);
     } else {
         if (ybf16) FGS_CB(false, true); else FGS_CB(false, false);
     }
 #undef FGS_CB
+#undef FGS_CB2
     return hipGetLastError();
 }
 

@@ -29,64 +29,24 @@ __device__ __forceinline__ float from_orderable(uint32_t o) {
     return __uint_as_float(u);
 }
 
-// FLAGS: partial sums from the router GEMM, whose mid/lo slices are skipped per rflags
-template <int VPL, bool FLAGS>
-__global__ __launch_bounds__(256) void topk_kernel(
-    const float *__restrict__ partial, int ks, const int32_t *__restrict__ rflags, const float *__restrict__ bias,
-    float *__restrict__ logits_out, int32_t *__restrict__ ids, float *__restrict__ tw,
-    float *__restrict__ gap, int N, int E, int k, bool renorm) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= N) return;
-
-    // Logits: slices added in order 0..ks-1 (ks <= 10).  Every load is issued
-    // up front from a valid address (experts past E read expert 0, slices past
-    // ks re-read slice ks-1) and masked afterwards, so the loads of all slices
-    // and experts are in flight together.
-    float h[VPL];
+// Selection and mixture weights of token t from its logits h[v] (lane l
+// holds experts l + 64 v) and the biases bv[v]; writes ids, tw, gap and the
+// optional logits of the token.
+template <int VPL>
+__device__ __forceinline__ void select_token(const float (&h)[VPL], const float (&bv)[VPL], int lane, int t, int E,
+                                             int k, bool renorm, float *__restrict__ logits_out,
+                                             int32_t *__restrict__ ids, float *__restrict__ tw,
+                                             float *__restrict__ gap) {
     uint64_t key[VPL];
-    const size_t slice = (size_t)N * E;
-    const float *row = partial + (size_t)t * E;
-    constexpr int kMaxSlices = 10;
-    constexpr bool kAllAtOnce = VPL * kMaxSlices <= 60;
-    // the biases go out first, from clamped indices, so no load waits behind another
-    // (with the router GEMM's split, rflags[e] == 0 says the slices of the mid
-    // and lo terms, the last two thirds, are all zero for expert e: not added)
-    float bv[VPL];
-    int fl[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
         const int e = lane + 64 * v;
-        bv[v] = bias[e < E ? e : 0];
-        fl[v] = FLAGS ? rflags[e < E ? e : 0] : 1;
-    }
-    const int hi_slices = FLAGS ? ks / 3 : ks;
-    float part[kAllAtOnce ? VPL : 1][kMaxSlices];
-    if constexpr (kAllAtOnce) {
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-            const int e = lane + 64 * v, ec = e < E ? e : 0;
-#pragma unroll
-            for (int s = 0; s < kMaxSlices; ++s) part[v][s] = row[(size_t)min(s, ks - 1) * slice + ec];
-        }
-    }
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-        const int e = lane + 64 * v, ec = e < E ? e : 0;
-        float p[kMaxSlices];
-#pragma unroll
-        for (int s = 0; s < kMaxSlices; ++s)
-            p[s] = kAllAtOnce ? part[kAllAtOnce ? v : 0][s] : row[(size_t)min(s, ks - 1) * slice + ec];
-        float acc = p[0];
-#pragma unroll
-        for (int s = 1; s < kMaxSlices; ++s) acc += (s < hi_slices || (FLAGS && s < ks && fl[v])) ? p[s] : 0.0f;
-        h[v] = acc;
         // the key is formed unconditionally (a select, no branch), so the bias
         // load cannot be sunk behind the partial sums
-        const float sc = acc + bv[v];
+        const float sc = h[v] + bv[v];
         const uint64_t kv = ((uint64_t)orderable(sc) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
         key[v] = e < E ? kv : 0;  // 0 is below every real key
-        if (e < E && logits_out) logits_out[(size_t)t * E + e] = acc;
+        if (e < E && logits_out) logits_out[(size_t)t * E + e] = h[v];
     }
 
     // k <= 8: fully unrolled rounds keep every array in registers
@@ -154,6 +114,104 @@ __global__ __launch_bounds__(256) void topk_kernel(
         tw[(size_t)t * k + lane] = renorm ? expf(hv - hmax) / zsum : sigmoidf_(hv);
     }
     if (gap && lane == 0) gap[t] = (k < E) ? sk - sk1 : __builtin_inff();
+}
+
+// FLAGS: partial sums from the router GEMM, whose mid/lo slices are skipped
+// per rflags.  (Two or four tokens per wave, the next token's partial sums
+// loaded while the current one is selected, measured slower: the selection
+// rounds, not the loads, set the pace.)
+template <int VPL, bool FLAGS>
+__global__ __launch_bounds__(256) void topk_kernel(
+    const float *__restrict__ partial, int ks, const int32_t *__restrict__ rflags, const float *__restrict__ bias,
+    float *__restrict__ logits_out, int32_t *__restrict__ ids, float *__restrict__ tw,
+    float *__restrict__ gap, int N, int E, int k, bool renorm) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= N) return;
+    const float *row = partial + (size_t)t * E;
+
+    const size_t slice = (size_t)N * E;
+    // the biases go out first, from clamped indices, so no load waits behind another
+    // (with the router GEMM's split, rflags[e] == 0 says the slices of the mid
+    // and lo terms, the last two thirds, are all zero for expert e: not added)
+    float bv[VPL];
+    int fl[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        const int e = lane + 64 * v;
+        bv[v] = bias[e < E ? e : 0];
+        fl[v] = FLAGS ? rflags[e < E ? e : 0] : 1;
+    }
+
+    if constexpr (!FLAGS) {
+        // Logits: slices added in order 0..ks-1 (ks <= 10).  Every load is
+        // issued up front from a valid address (experts past E read expert 0,
+        // slices past ks re-read slice ks-1) and masked afterwards, so the
+        // loads of all slices and experts are in flight together.
+        constexpr int kMaxSlices = 10;
+        constexpr bool kAllAtOnce = VPL * kMaxSlices <= 60;
+        float part[kAllAtOnce ? VPL : 1][kMaxSlices];
+        if constexpr (kAllAtOnce) {
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                const int e = lane + 64 * v, ec = e < E ? e : 0;
+#pragma unroll
+                for (int s = 0; s < kMaxSlices; ++s) part[v][s] = row[(size_t)min(s, ks - 1) * slice + ec];
+            }
+        }
+        float h[VPL];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const int e = lane + 64 * v, ec = e < E ? e : 0;
+            float p[kMaxSlices];
+#pragma unroll
+            for (int s = 0; s < kMaxSlices; ++s)
+                p[s] = kAllAtOnce ? part[kAllAtOnce ? v : 0][s] : row[(size_t)min(s, ks - 1) * slice + ec];
+            float acc = p[0];
+#pragma unroll
+            for (int s = 1; s < kMaxSlices; ++s) acc += s < ks ? p[s] : 0.0f;
+            h[v] = acc;
+        }
+        select_token<VPL>(h, bv, lane, t, E, k, renorm, logits_out, ids, tw, gap);
+    } else {
+        // hi-term slices (c = ks/3 <= 4) per token; the mid and lo slices (2c)
+        // are fetched in a second round, and only when some expert of this
+        // wave has nonzero terms there, so bf16-valued router weights cost
+        // one pass over c slices.  Slices are added in order 0..ks-1.
+        constexpr int kMaxHi = 4;
+        const int hi = ks / 3;
+        int need = 0;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) need |= (lane + 64 * v < E) && fl[v];
+        float part[VPL][kMaxHi];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const int e = lane + 64 * v, ec = e < E ? e : 0;
+#pragma unroll
+            for (int s = 0; s < kMaxHi; ++s) part[v][s] = s < hi ? row[(size_t)s * slice + ec] : 0.0f;
+        }
+        float h[VPL];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            float acc = part[v][0];
+#pragma unroll
+            for (int s = 1; s < kMaxHi; ++s) acc += s < hi ? part[v][s] : 0.0f;
+            h[v] = acc;
+        }
+        if (__any(need)) {
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                const int e = lane + 64 * v, ec = e < E ? e : 0;
+                float ml[2 * kMaxHi];
+#pragma unroll
+                for (int s = 0; s < 2 * kMaxHi; ++s)
+                    ml[s] = (hi + s < ks && fl[v]) ? row[(size_t)(hi + s) * slice + ec] : 0.0f;
+#pragma unroll
+                for (int s = 0; s < 2 * kMaxHi; ++s) h[v] += ml[s];
+            }
+        }
+        select_token<VPL>(h, bv, lane, t, E, k, renorm, logits_out, ids, tw, gap);
+    }
 }
 
 hipError_t launch_topk(const Plan &p) {

@@ -168,11 +168,12 @@ def test_shape_limits(cfg_name, over):
     _run_full(get_config(cfg_name, **over))
 
 
-@pytest.mark.parametrize("n", [300, 40])
+@pytest.mark.parametrize("n", [300, 40, 4096, 8192])
 def test_router_full_fp32_weights(n):
     """FP32 router weights that are not bf16 values (mid and lo split terms nonzero) for a scattered
     subset of experts: expert blocks with all, some and none of their experts flagged (the router
-    GEMM skips the zero-term slices only where a whole block has none), and the N <= 64 router."""
+    GEMM skips the zero-term slices only where a whole block has none), the N <= 64 router, and
+    the top-k's two- and four-token waves (N = 4096, 8192; 4 and 2 K slices per split term)."""
     cfg = get_config("toy", n_tokens=n, x_dtype="bf16", n_experts=384, d_ff=64, d_ff_shared=64)
     host = generate(cfg, seed=8)
     rw = host["router_w"].clone()
