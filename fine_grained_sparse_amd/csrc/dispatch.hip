@@ -62,7 +62,9 @@ __device__ int block_exclusive_scan_1024(int *v, int L, int *wsum) {
 }
 
 // After `cnt[0..E)` holds per-expert counts (LDS): offsets, tile list.
-// `scratch` >= 2*(E+1)+... ints of LDS.  Leaves offsets in off[0..E+2).
+// Leaves offsets in off[0..E+2).  PER_TILE: the tile list is written one
+// thread per tile (large batches), else one thread per group.
+template <bool PER_TILE>
 __device__ void offsets_and_tiles(const int *cnt, int *off, int *ntile, int *wsum, int N, int k, int E,
                                   int bm, int32_t *g_offsets, int32_t *g_exp_off, int32_t *tiles,
                                   int32_t *n_tiles) {
@@ -89,13 +91,29 @@ __device__ void offsets_and_tiles(const int *cnt, int *off, int *ntile, int *wsu
     }
     __syncthreads();
     int nt = block_exclusive_scan_1024(ntile, E + 1, wsum);
-    for (int q = tid; q <= E; q += blockDim.x) {
-        const int g = q == 0 ? E : q - 1;
-        const int m = off[g + 1] - off[g];
-        const int start = ntile[q];
-        for (int i = 0; i * bm < m; ++i) {
-            tiles[2 * (start + i)] = g;
-            tiles[2 * (start + i) + 1] = i * bm;
+    if constexpr (PER_TILE) {
+        // one thread per tile: its slot q is the last one whose first tile is
+        // at or before it (an empty slot shares its successor's start and
+        // loses the tie); no thread walks a long group alone
+        for (int s = tid; s < nt; s += blockDim.x) {
+            int lo = 0, hi = E;   // ntile[lo] <= s; find the largest such q
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (ntile[mid] <= s) lo = mid; else hi = mid - 1;
+            }
+            tiles[2 * s] = lo == 0 ? E : lo - 1;
+            tiles[2 * s + 1] = (s - ntile[lo]) * bm;
+        }
+    } else {
+        // one thread per group (small batches: one tile per group, no search)
+        for (int q = tid; q <= E; q += blockDim.x) {
+            const int g = q == 0 ? E : q - 1;
+            const int m = off[g + 1] - off[g];
+            const int start = ntile[q];
+            for (int i = 0; i * bm < m; ++i) {
+                tiles[2 * (start + i)] = g;
+                tiles[2 * (start + i) + 1] = i * bm;
+            }
         }
     }
     if (tid == 0) *n_tiles = nt;
@@ -159,7 +177,7 @@ __global__ __launch_bounds__(1024) void dispatch_fused_kernel(
             if (j < k) atomicAdd(&cnt[my[j]], 1);
     }
     __syncthreads();
-    offsets_and_tiles(cnt, off, ntile, wsum, N, k, E, bm, g_offsets, g_exp_off, tiles, n_tiles);
+    offsets_and_tiles<false>(cnt, off, ntile, wsum, N, k, E, bm, g_offsets, g_exp_off, tiles, n_tiles);
     __syncthreads();
     block_scatter(my, bits, off, 0, N, k, E, por, rop);
 }
@@ -205,11 +223,17 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t *blk, int n
         for (int i = tid; i < n; i += blockDim.x) stage[i] = src[i];
         __syncthreads();
         for (int e = tid; e < E; e += blockDim.x) {
+            // 16 blocks per step: all reads issued before the first write
             int run = cnt[e];
-            for (int b = 0; b < nb; ++b) {
-                const int c = stage[b * E + e];
-                stage[b * E + e] = run;
-                run += c;
+            for (int b = 0; b < nb; b += 16) {
+                int c[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) c[i] = b + i < nb ? stage[(b + i) * E + e] : 0;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (b + i < nb) stage[(b + i) * E + e] = run;
+                    run += c[i];
+                }
             }
             cnt[e] = run;
         }
@@ -217,7 +241,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t *blk, int n
         for (int i = tid; i < n; i += blockDim.x) blk[(size_t)b0 * E + i] = stage[i];
         __syncthreads();
     }
-    offsets_and_tiles(cnt, off, ntile, wsum, N, k, E, bm, g_offsets, g_exp_off, tiles, n_tiles);
+    offsets_and_tiles<true>(cnt, off, ntile, wsum, N, k, E, bm, g_offsets, g_exp_off, tiles, n_tiles);
 }
 
 // blk[b][e]: rows of expert e in the blocks before b (from the scan)
