@@ -185,7 +185,7 @@ int run_layer(const moe_desc *desc, const void *x, const float *router_w, const 
     int dev = 0;
     st = check_device(&dev);
     if (st != MOE_OK) return st;
-    if ((!L.stream || L.rgemm) && g_gemm_init[dev].load(std::memory_order_acquire) != 1) {
+    if (!L.stream && g_gemm_init[dev].load(std::memory_order_acquire) != 1) {   // the expert GEMMs' LDS limits
         // idempotent: concurrent first calls may both set the same attributes
         hipError_t e = gemm_kernels_init();
         if (e != hipSuccess) { g_last_hip_error = (int)e; return MOE_ERR_HIP; }

@@ -162,6 +162,7 @@ def test_block_act_quant():
     ("toy", dict(n_tokens=16, d_model=4160, n_experts=48, d_ff=128, d_ff_shared=128, x_dtype="bf16")),  # d past the stream path
     ("toy", dict(n_tokens=16, d_ff=640, d_ff_shared=512)),             # f past the stream path: GEMM at tiny m
     ("toy", dict(n_tokens=100, d_model=2560, n_experts=1024, top_k=8, x_dtype="bf16")),  # most experts, largest k
+    ("toy", dict(n_tokens=300, n_experts=202, top_k=7, x_dtype="bf16")),  # router GEMM: one ragged expert tile, E % 4 != 0
 ])
 def test_shape_limits(cfg_name, over):
     """Edges of the supported shapes and of the stream/GEMM path choice."""
