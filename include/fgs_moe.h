@@ -46,7 +46,9 @@
  *
  * Execution: all work is enqueued on `stream` (a hipStream_t; NULL = the
  * default stream) without host synchronisation; results are valid once the
- * stream reaches that point.  Device faults surface at the caller's next
+ * stream reaches that point.  `stream` must belong to the calling thread's
+ * current device (hipSetDevice), which is the device that is checked and
+ * configured.  Device faults surface at the caller's next
  * synchronisation.  Calls that share a workspace must be ordered on one
  * stream.  Calls can be captured in a HIP graph (no memset or host work is
  * enqueued); make the first call on each device outside a capture, since it
