@@ -236,17 +236,18 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
 // output rows per wave: 4 KB of weights per wave in both formats (4 bf16 rows
 // of 512, 8 E4M3 rows).  Measured at decode size, 2, 8 and 16 bf16 rows and
 // 4 or 16 FP8 rows are slower: fewer, larger waves leave more of the machine
-// idle behind each one's index loads and at the grid's tail.  Eight waves
-// per workgroup: the index loads are shared by twice the rows (decode N=32:
-// 62.8 against 64.1 us with four waves; sixteen waves 64.8 us).
-constexpr int kDnWaves = 8;
+// idle behind each one's index loads and at the grid's tail.  32 rows per
+// workgroup in both formats: eight bf16 waves (decode N=32: 62.8 against
+// 64.1 us with four waves, 64.8 with sixteen), four FP8 waves (eight: 37.7
+// against 37.2 us, with 1 x 128 activations 44.2 against 41.3).
+template <bool FP8> constexpr int dn_waves() { return FP8 ? 4 : 8; }
 template <bool FP8> constexpr int dn_rows_per_wave() { return FP8 ? 8 : 4; }
-template <bool FP8> constexpr int dn_rows_per_block() { return kDnWaves * dn_rows_per_wave<FP8>(); }
+template <bool FP8> constexpr int dn_rows_per_block() { return dn_waves<FP8>() * dn_rows_per_wave<FP8>(); }
 
-// grid: (d / dn_rows_per_block, tile list capacity); block 64 * kDnWaves.  Needs f, fs <= 512.
+// grid: (d / dn_rows_per_block, tile list capacity); block 64 * dn_waves.  Needs f, fs <= 512.
 // AQ: H is the E4M3 codes [rows][ldh] (as bytes) with scales hs [rows][ldh/128].
 template <int WM, bool AQ>
-__global__ __launch_bounds__(64 * kDnWaves) void down_stream_kernel(
+__global__ __launch_bounds__(64 * dn_waves<WM != kWBf16>()) void down_stream_kernel(
     const uint16_t *__restrict__ H, const float *__restrict__ hs, int ldh, const void *__restrict__ wd,
     const float *__restrict__ sd,
     const void *__restrict__ wsd, const float *__restrict__ ssd, const int32_t *__restrict__ tiles,
@@ -363,7 +364,8 @@ hipError_t launch_gate_up(const Plan &p) {
 
 hipError_t launch_down(const Plan &p) {
     const int rb = p.wdt == MOE_DTYPE_FP8_E4M3 ? dn_rows_per_block<true>() : dn_rows_per_block<false>();
-    dim3 grid(p.d / rb, p.max_tiles), block(64 * kDnWaves);
+    const int waves = p.wdt == MOE_DTYPE_FP8_E4M3 ? dn_waves<true>() : dn_waves<false>();
+    dim3 grid(p.d / rb, p.max_tiles), block(64 * waves);
     const long rows = (long)p.N * p.k + p.N;
     if (p.aq) {  // hidden activations in 1 x 128 groups (every row of H, routed and shared)
         hipError_t e = launch_quant_groups(p.hf, 0, p.ldh, rows, p.ldh, p.hq, p.ldh, p.hs, p.ldh / 128, p.stream);
