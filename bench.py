@@ -271,7 +271,7 @@ def main():
         if cfg.w_dtype != "fp8":
             return 0
         return 4 * n_in / (128 * 128) if cfg.scale_block else 4   # per 128x128 block, or per output channel
-    stream_path = N <= 64 and d <= 4096 and f <= 512 and fs <= 512
+    stream_path = N <= 192 and d <= 4096 and f <= 512 and fs <= 512   # the library's own rule
     kind = "stream" if stream_path else "gemm"
 
     # algorithmic bytes and flops per launch of the two expert kernels, for U

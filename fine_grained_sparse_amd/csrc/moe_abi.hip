@@ -81,7 +81,7 @@ Layout layout_for(const moe_desc *d) {
     L.nblk = (int)((N + 255) / 256);
     if (L.nblk < 1) L.nblk = 1;
     L.stream = stream_path(d->n_tokens, d->d_model, d->d_ff, d->d_ff_shared);
-    L.bm = L.stream ? (d->n_tokens > 0 ? d->n_tokens : 1) : kGemmBM;
+    L.bm = L.stream ? (d->n_tokens < 1 ? 1 : d->n_tokens < kStreamBM ? d->n_tokens : kStreamBM) : kGemmBM;
     L.max_tiles = max_tiles_for(d->n_tokens, d->top_k, d->n_experts, L.bm);
     L.ldh = d->d_ff > d->d_ff_shared ? d->d_ff : d->d_ff_shared;
     const size_t rows = N * k + N;

@@ -69,8 +69,14 @@ hipError_t gemm_kernels_init();  // once per process: raise the kernels' LDS lim
 hipError_t launch_quant_groups(const void *v, int v_bf16, int ldv, long rows, int cols, uint8_t *q, int ldq,
                                float *s, int lds, hipStream_t stream);
 
-// Decode-shaped expert kernels keep whole weight rows in registers.
-constexpr int kStreamMaxN = 64;
+// Decode-shaped expert kernels keep whole weight rows in registers and take
+// tiles of at most 64 rows (one token per lane).  Against the grouped GEMMs
+// (one MI355X, d = 2560, E = 384, top-6) they are faster up to about 192
+// tokens: bf16 weights at N = 65 / 128 / 192: 0.322 / 0.438 / 0.516 ms
+// against 0.387 / 0.503 / 0.534; at 224 both take 0.55; E4M3 weights at
+// N = 128: 0.293 against 0.359, at 192 both 0.373.
+constexpr int kStreamMaxN = 192;
+constexpr int kStreamBM = 64;
 inline bool stream_path(int N, int d, int f, int fs) {
     return N <= kStreamMaxN && d <= 4096 && f <= 512 && fs <= 512;
 }

@@ -42,26 +42,37 @@ def _run_full(cfg, seed=0, residual=False, renormalize=False, act_quant=False):
     return stats
 
 
-def test_toy():
-    _run_full(get_config("toy"))
+@pytest.mark.parametrize("n", [128, 300])
+def test_toy(n):
+    """The toy layer on the stream path (128 tokens, two 64-row tiles for the shared expert) and
+    on the grouped GEMMs (300 tokens)."""
+    _run_full(get_config("toy", n_tokens=n))
 
 
-@pytest.mark.parametrize("n", [1, 2, 7, 32, 64])
+@pytest.mark.parametrize("n", [1, 2, 7, 32, 64, 65, 130, 192])
 def test_decode_full_shape(n):
+    """Full-size layer on the stream path (above 64 tokens: several 64-row tiles per group)."""
     _run_full(get_config("decode", n_tokens=n))
 
 
-def test_decode_fp8_weights():
-    _run_full(get_config("decode", w_dtype="fp8", n_tokens=16))
+@pytest.mark.parametrize("n", [16, 129])
+def test_decode_fp8_weights(n):
+    _run_full(get_config("decode", w_dtype="fp8", n_tokens=n))
 
 
-@pytest.mark.parametrize("over", [
+_TOY_VARIANTS = [
     dict(top_k=1), dict(top_k=8), dict(n_experts=6, top_k=6), dict(n_experts=40),
     dict(d_model=192, d_ff=128, d_ff_shared=64), dict(x_dtype="bf16", w_dtype="fp8"),
     dict(n_tokens=1), dict(n_tokens=600), dict(n_tokens=257, n_experts=1024, top_k=8),
-])
-def test_toy_variants(over):
-    _run_full(get_config("toy", **over))
+]
+
+
+@pytest.mark.parametrize("over,n", [(v, None) for v in _TOY_VARIANTS] +
+                         [(v, 300) for v in _TOY_VARIANTS if "n_tokens" not in v])
+def test_toy_variants(over, n):
+    """Odd shapes and dtypes at the toy's own batch (stream path up to 192 tokens) and at 300
+    tokens (grouped GEMMs)."""
+    _run_full(get_config("toy", **(dict(over, n_tokens=n) if n else over)))
 
 
 def test_accumulate_into_residual():
@@ -81,8 +92,8 @@ def test_renormalized_gate(cfg_name, over):
     dict(n_tokens=16), dict(n_tokens=128), dict(n_tokens=600),
     dict(n_tokens=9, x_dtype="bf16", d_model=384, d_ff=256, d_ff_shared=128),
     dict(n_tokens=200, x_dtype="bf16", d_model=384, d_ff=256, d_ff_shared=128),
-    dict(n_tokens=150, x_dtype="bf16", d_model=3072, d_ff=256, d_ff_shared=128),   # 24 K blocks: direct-to-LDS tile
-    dict(n_tokens=150, x_dtype="bf16", d_model=3200, d_ff=256, d_ff_shared=128),   # 25 K blocks: register-staged tile
+    dict(n_tokens=250, x_dtype="bf16", d_model=3072, d_ff=256, d_ff_shared=128),   # 24 K blocks: direct-to-LDS tile
+    dict(n_tokens=250, x_dtype="bf16", d_model=3200, d_ff=256, d_ff_shared=128),   # 25 K blocks: register-staged tile
 ])
 def test_fp8_block_scales_toy(over):
     """FP8 weights with one scale per 128 x 128 block (MOE_FLAG_FP8_BLOCK128): stream and GEMM
@@ -130,8 +141,8 @@ def test_quantize_groups_bit_exact(dtype, rows, cols):
     dict(n_tokens=16), dict(n_tokens=128), dict(n_tokens=600), dict(n_tokens=16, scale_block=0),
     dict(n_tokens=200, scale_block=0), dict(n_tokens=9, d_model=384, d_ff=256, d_ff_shared=128),
     dict(n_tokens=200, d_model=384, d_ff=256, d_ff_shared=128),
-    dict(n_tokens=150, d_model=3072, d_ff=256, d_ff_shared=128),   # 24 K blocks: the direct-to-LDS tile's limit
-    dict(n_tokens=150, d_model=3200, d_ff=256, d_ff_shared=128),   # 25 K blocks: the register-staged tile
+    dict(n_tokens=250, d_model=3072, d_ff=256, d_ff_shared=128),   # 24 K blocks: the direct-to-LDS tile's limit
+    dict(n_tokens=250, d_model=3200, d_ff=256, d_ff_shared=128),   # 25 K blocks: the register-staged tile
 ])
 def test_fp8_act_quant_toy(over):
     """1 x 128 activation quantisation with FP8 x FP8 matmuls (MOE_FLAG_FP8_ACT_QUANT): stream and
@@ -141,7 +152,7 @@ def test_fp8_act_quant_toy(over):
     _run_full(get_config("toy", **base), act_quant=True)
 
 
-@pytest.mark.parametrize("name,n", [("fp8block", 32), ("fp8", 48)])
+@pytest.mark.parametrize("name,n", [("fp8block", 32), ("fp8", 48), ("fp8block", 150)])
 def test_decode_act_quant(name, n):
     _run_full(get_config(name, n_tokens=n), act_quant=True)
 
@@ -155,8 +166,9 @@ def test_block_act_quant():
 
 
 @pytest.mark.parametrize("cfg_name,over", [
-    ("decode", dict(n_tokens=64)),                                     # largest batch on the stream path
-    ("decode", dict(n_tokens=65)),                                     # first batch on the GEMM path
+    ("decode", dict(n_tokens=192)),                                    # largest batch on the stream path
+    ("decode", dict(n_tokens=193)),                                    # smallest batch on the grouped GEMMs
+    ("decode", dict(n_tokens=65)),                                     # two 64-row stream tiles for the shared expert
     ("toy", dict(n_tokens=40, n_experts=448, top_k=8)),                # small batch, 7 experts per lane in top-k
     ("toy", dict(n_tokens=8, d_model=4096, n_experts=64, d_ff=512, d_ff_shared=512, x_dtype="bf16")),  # widest stream rows
     ("toy", dict(n_tokens=16, d_model=4160, n_experts=48, d_ff=128, d_ff_shared=128, x_dtype="bf16")),  # d past the stream path
