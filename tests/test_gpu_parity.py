@@ -55,6 +55,14 @@ def test_decode_full_shape(n):
     _run_full(get_config("decode", n_tokens=n))
 
 
+@pytest.mark.parametrize("cfg_name,over", [("decode", dict(n_tokens=32)), ("decode", dict(n_tokens=96, w_dtype="fp8")),
+                                          ("toy", dict(n_tokens=300, x_dtype="bf16"))])
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_other_seeds(cfg_name, over, seed):
+    """Fresh inputs for the stream path (bf16 and E4M3 weights) and the grouped GEMMs."""
+    _run_full(get_config(cfg_name, **over), seed=seed)
+
+
 @pytest.mark.parametrize("n", [16, 129])
 def test_decode_fp8_weights(n):
     _run_full(get_config("decode", w_dtype="fp8", n_tokens=n))
