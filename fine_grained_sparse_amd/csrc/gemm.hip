@@ -93,7 +93,7 @@ static_assert(kGemmLdsDma <= 160 * 1024, "the direct-to-LDS stages must fit one 
 // the grid must hold that many workgroups.  Returns false for a workgroup
 // without an item.
 constexpr int kXcds = 8;
-constexpr int kXcdTiles = 4;
+constexpr int kXcdTiles = 2;   // blocks of 1, 4, 8 tile rows measured slower (Zipf 1.347 / 1.358 / 1.347 ms against 1.341)
 __device__ __forceinline__ bool xcd_item(int n_items, int &item) {
     const int L = blockIdx.y * gridDim.x + blockIdx.x;
     const int B = kXcdTiles * gridDim.x;
