@@ -155,6 +155,95 @@ __device__ void block_scatter(const int (&e)[8], uint32_t *bits, const int *base
         }
 }
 
+// ---- one-wave path (N <= 64, every group within one tile): a single wave,
+// lane t holding token t, so no step needs a workgroup barrier.  Per-expert
+// counts and 64-bit token masks come from LDS atomics; the offsets and the
+// tile list are wave-wide prefix sums over 16 experts per lane.
+
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+        const int o = __shfl_up(v, s, kWave);
+        if (lane >= s) v += o;
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(64) void dispatch_wave_kernel(
+    const int32_t *__restrict__ ids, int N, int k, int E, int32_t *g_offsets, int32_t *g_exp_off,
+    int32_t *tiles, int32_t *n_tiles, int32_t *por, int32_t *rop) {
+    __shared__ int cnt[1024];
+    __shared__ unsigned long long mask[1024];
+    __shared__ int off[1024];
+    const int lane = threadIdx.x;
+    const bool live = lane < N;
+    int my[8];
+    load_token_ids(ids, lane, k, live, my);
+    for (int e = lane; e < E; e += 64) { cnt[e] = 0; mask[e] = 0ull; }
+    __syncthreads();
+    if (live) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < k) {
+                atomicAdd(&cnt[my[j]], 1);
+                atomicOr(&mask[my[j]], 1ull << lane);
+            }
+    }
+    __syncthreads();
+    // lane l owns experts [C l, C l + C): exclusive offsets and tile slots
+    const int C = (E + 63) / 64;   // <= 16
+    int c[16], sum = 0, nonempty = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int e = C * lane + i;
+        c[i] = (i < C && e < E) ? cnt[e] : 0;
+        sum += c[i];
+        nonempty += c[i] > 0;
+    }
+    const int base = wave_inclusive_scan(sum) - sum;
+    const int tbase = wave_inclusive_scan(nonempty) - nonempty;   // routed tiles before this lane's experts
+    const int total = N * k;
+    int run = base, trun = 1 + tbase;   // tile 0 is the shared group
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int e = C * lane + i;
+        if (i < C && e < E) {
+            off[e] = run;
+            g_offsets[e] = run;
+            if (g_exp_off) g_exp_off[e] = run;
+            if (c[i] > 0) {
+                tiles[2 * trun] = e;
+                tiles[2 * trun + 1] = 0;
+                ++trun;
+            }
+            run += c[i];
+        }
+    }
+    if (lane == 63) *n_tiles = trun;   // the last lane's running count is the total
+    if (lane == 0) {
+        g_offsets[E] = total;
+        g_offsets[E + 1] = total + N;
+        if (g_exp_off) g_exp_off[E] = total;
+        tiles[0] = E;
+        tiles[1] = 0;
+    }
+    __syncthreads();
+    // rank of token t among expert e's tokens: the tokens below t in e's mask
+    if (live) {
+        const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j >= k) break;
+            const int e = my[j];
+            const int pos = off[e] + __popcll(mask[e] & below);
+            por[pos] = lane * k + j;
+            rop[(size_t)lane * k + j] = pos;
+        }
+    }
+}
+
 // ---- one-block path (N <= 256): everything in one workgroup of 1024 threads
 
 __global__ __launch_bounds__(1024) void dispatch_fused_kernel(
@@ -258,6 +347,11 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t *__
 }
 
 hipError_t launch_dispatch(const Plan &p) {
+    if (p.N <= 64 && p.bm >= p.N) {   // one wave; every group fits one tile
+        hipLaunchKernelGGL(dispatch_wave_kernel, dim3(1), dim3(64), 0, p.stream, p.ids, p.N, p.k, p.E, p.offsets,
+                           p.exp_off_out, p.tiles, p.n_tiles, p.por, p.rop);
+        return hipGetLastError();
+    }
     if (p.nblk == 1) {
         hipLaunchKernelGGL(dispatch_fused_kernel, dim3(1), dim3(1024), 0, p.stream, p.ids, p.N, p.k, p.E, p.bm,
                            p.offsets, p.exp_off_out, p.tiles, p.n_tiles, p.por, p.rop);
