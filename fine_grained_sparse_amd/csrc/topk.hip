@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
     float *__restrict__ logits_out, int32_t *__restrict__ ids, float *__restrict__ tw,
     float *__restrict__ gap, int N, int E, int k, bool renorm) {
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (t >= N) return;
     const float *row = partial + (size_t)t * E;
 
@@ -215,7 +215,11 @@ __global__ __launch_bounds__(256) void topk_kernel(
 }
 
 hipError_t launch_topk(const Plan &p) {
-    dim3 grid((p.N + 3) / 4), block(256);
+    // one token per wave; small batches put each wave in a workgroup of its own,
+    // so the selections spread over as many CUs (N = 32: 6.0 against 7.1 us
+    // with four waves per workgroup)
+    const int wpb = p.N <= 64 ? 1 : 4;
+    dim3 grid((p.N + wpb - 1) / wpb), block(64 * wpb);
     int vpl = (p.E + 63) / 64;
 #define FGS_TOPK2(V, F)                                                                             \
     hipLaunchKernelGGL((topk_kernel<V, F>), grid, block, 0, p.stream, p.partial, p.ks, p.rflags, p.rb, \
