@@ -55,18 +55,23 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4 &a, const uint4 &b, 
 // (l % 16) of B with the 8 consecutive k at 8*(l / 16); both operands use the
 // same k mapping, so the k order inside the instruction does not matter.
 // Result: lane l holds D[4*(l/16) + i][l % 16], i = 0..3.
-template <int MT, int NT>
+// KW > 1: a workgroup of KW waves per job, wave w taking the w-th of KW equal
+// parts of the k-slice; the parts' sums are added in wave order through LDS
+// (fewer bytes per wave in flight without more slices for the top-k to add).
+template <int MT, int NT, int KW = 1>
 __global__ __launch_bounds__(256) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ rw, float *__restrict__ partial,
     int N, int d, int E, int kslice, int n_tb, int n_eb, int n_jobs) {
     const int lane = threadIdx.x & 63;
-    const int job = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int kw = KW > 1 ? (int)(threadIdx.x >> 6) : 0;
+    const int job = KW > 1 ? (int)blockIdx.x : (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
     if (job >= n_jobs) return;
     const int tb = job % n_tb;
     const int rest = job / n_tb;
     const int eb = rest % n_eb;
     const int s = rest / n_eb;
-    const int t0 = tb * 16 * MT, e0 = eb * 16 * NT, k0 = s * kslice;
+    const int kpart = kslice / KW;
+    const int t0 = tb * 16 * MT, e0 = eb * 16 * NT, k0 = s * kslice + kw * kpart;
     const int r = lane & 15, kq = (lane >> 4) * 8;
 
     const uint16_t *xrow[MT];
@@ -93,7 +98,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
         for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll 8
-    for (int kk = 0; kk < kslice; kk += 32) {
+    for (int kk = 0; kk < kpart; kk += 32) {
         uint4 a[MT];
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
@@ -116,6 +121,26 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
         }
     }
 
+    if constexpr (KW > 1) {   // the whole workgroup has a job: n_jobs workgroups
+        __shared__ f32x4_t red[KW - 1][MT][NT][64];
+        if (kw > 0)
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) red[kw - 1][i][j][lane] = acc[i][j];
+        __syncthreads();
+        if (kw > 0) return;
+#pragma unroll
+        for (int w = 0; w < KW - 1; ++w)
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const f32x4_t o = red[w][i][j][lane];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[i][j][q] += o[q];
+                }
+    }
     float *dst = partial + (size_t)s * N * E;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -167,8 +192,12 @@ hipError_t launch_router(const Plan &p) {
     if (rt.mt == 2) {
         // one wave per workgroup: the few hundred jobs of a small batch spread
         // over as many CUs, each pulling its slice of W_r with its own loads
-        hipLaunchKernelGGL((router_mfma_kernel<2, 1>), dim3(n_jobs), dim3(64), 0, p.stream,
-                           x, p.rw, p.partial, p.N, p.d, p.E, p.kslice, n_tb, n_eb, n_jobs);
+        if (p.kslice % 64 == 0)   // two waves per job, each half of the k-slice
+            hipLaunchKernelGGL((router_mfma_kernel<2, 1, 2>), dim3(n_jobs), dim3(128), 0, p.stream,
+                               x, p.rw, p.partial, p.N, p.d, p.E, p.kslice, n_tb, n_eb, n_jobs);
+        else
+            hipLaunchKernelGGL((router_mfma_kernel<2, 1>), dim3(n_jobs), dim3(64), 0, p.stream,
+                               x, p.rw, p.partial, p.N, p.d, p.E, p.kslice, n_tb, n_eb, n_jobs);
     } else {
         dim3 grid((n_jobs + 3) / 4);
         hipLaunchKernelGGL((router_mfma_kernel<4, 4>), grid, dim3(256), 0, p.stream,
