@@ -192,7 +192,12 @@ hipError_t launch_router(const Plan &p) {
     if (rt.mt == 2) {
         // one wave per workgroup: the few hundred jobs of a small batch spread
         // over as many CUs, each pulling its slice of W_r with its own loads
-        if (p.kslice % 64 == 0)   // two waves per job, each half of the k-slice
+        // several waves per job, each a part of the k-slice of 32 or more k
+        // (N = 32, d = 2560: router 6.3 us with one wave, 5.1 with two, 4.8 with four)
+        if (p.kslice % 128 == 0)
+            hipLaunchKernelGGL((router_mfma_kernel<2, 1, 4>), dim3(n_jobs), dim3(256), 0, p.stream,
+                               x, p.rw, p.partial, p.N, p.d, p.E, p.kslice, n_tb, n_eb, n_jobs);
+        else if (p.kslice % 64 == 0)
             hipLaunchKernelGGL((router_mfma_kernel<2, 1, 2>), dim3(n_jobs), dim3(128), 0, p.stream,
                                x, p.rw, p.partial, p.N, p.d, p.E, p.kslice, n_tb, n_eb, n_jobs);
         else

@@ -183,6 +183,8 @@ def test_block_act_quant():
     ("toy", dict(n_tokens=16, d_ff=640, d_ff_shared=512)),             # f past the stream path: GEMM at tiny m
     ("toy", dict(n_tokens=100, d_model=2560, n_experts=1024, top_k=8, x_dtype="bf16")),  # most experts, largest k
     ("toy", dict(n_tokens=300, n_experts=202, top_k=7, x_dtype="bf16")),  # router GEMM: one ragged expert tile, E % 4 != 0
+    ("toy", dict(n_tokens=24, d_model=640, x_dtype="bf16")),            # small-batch router: two waves per k-slice
+    ("toy", dict(n_tokens=24, d_model=1280, x_dtype="bf16")),           # small-batch router: four waves per k-slice
 ])
 def test_shape_limits(cfg_name, over):
     """Edges of the supported shapes and of the stream/GEMM path choice."""
