@@ -52,7 +52,7 @@ class LayerConfig:
     d_ff_shared: int
     x_dtype: str          # "f32" | "bf16"  (the output has the same dtype)
     w_dtype: str          # "bf16" | "fp8"
-    bias_kind: str        # "normal" | "zipf"
+    bias_kind: str        # "normal" | "zipf" | "hot"
     bias_std: float = 0.1
     zipf_s: float = 1.1
     x_std: float = 1.0
@@ -87,6 +87,11 @@ CONFIGS: Dict[str, LayerConfig] = {
     # FP8 weights, router bias = log of a Zipf(1.1) popularity over experts
     "zipf": LayerConfig("zipf", n_tokens=16384, x_dtype="bf16", w_dtype="fp8",
                         bias_kind="zipf", zipf_s=1.1, **_FULL),
+    # compute-ceiling probe of the grouped GEMMs: a bias of +16 on experts
+    # 0..top_k-1 routes every token to them, so every row tile is full and the
+    # seven experts' weights are shared by all tiles (stay on chip)
+    "hot": LayerConfig("hot", n_tokens=16384, x_dtype="bf16", w_dtype="bf16",
+                       bias_kind="hot", bias_std=0.1, **_FULL),
 }
 
 
@@ -205,6 +210,10 @@ def generate(cfg: LayerConfig, seed: int = 0, device: str = "cpu",
 
     if cfg.bias_kind == "zipf":
         out["router_b"] = zipf_bias(E, cfg.zipf_s, seeds["zipf_perm"]).to(device)
+    elif cfg.bias_kind == "hot":
+        b = _randn((E,), cfg.bias_std, seeds["router_b"], device)
+        b[:cfg.top_k] += 16.0
+        out["router_b"] = b
     else:
         out["router_b"] = _randn((E,), cfg.bias_std, seeds["router_b"], device)
 

@@ -7,13 +7,23 @@ import torch
 
 from moe_inputs import generate, get_config
 from tests import parity as PA
+from tests import report
 
 pytestmark = pytest.mark.gpu
 
 
+_CASE = [""]
+
+
 def _say(*a):
-    print(*a, flush=True)
+    """Print progress; a case line and its result line also go to the run's summary."""
+    line = " ".join(str(v) for v in a)
+    print(line, flush=True)
     sys.stdout.flush()
+    if line.startswith("case"):
+        _CASE[0] = line
+    elif line.lstrip().startswith("->"):
+        report.add(f"{_CASE[0]}  {line.strip()}")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -327,17 +337,72 @@ def test_zero_tokens_is_noop():
 
 @pytest.mark.parametrize("name,aq", [("prefill", False), ("fp8", False), ("fp8block", False), ("zipf", False),
                                      ("fp8block", True), ("zipf", True)])
-def test_full_size_sampled(name, aq):
-    """Full-size workloads: routing and layout of every token, output of a sample."""
+def test_full_size(name, aq):
+    """Full-size workloads, every token: routing, dispatch layout and every output row against the
+    oracle.  These are the cases that run the grouped GEMMs over many row tiles per expert (Zipf:
+    about 120 tiles for the hottest expert, ragged last tiles) and the full-grid XCD work order."""
     cfg = get_config(name)
-    _say(f"case {name} N={cfg.n_tokens} w={cfg.w_dtype} bias={cfg.bias_kind} act_quant={aq} (sampled outputs)")
+    _say(f"case {name} N={cfg.n_tokens} w={cfg.w_dtype} bias={cfg.bias_kind} act_quant={aq} (every token)")
     host = generate(cfg, seed=0)
     g = PA.run_gpu(cfg, PA.to_device(host), act_quant=aq)
-    stats = PA.sampled_check(cfg, host, g, n_sample=24, act_quant=aq)
+    _say("  gpu done; oracle on every token")
+    stats = PA.full_check(cfg, host, g, act_quant=aq)
     counts = np.diff(g["expert_offsets"])
     stats["empty_experts"] = int((counts == 0).sum())
     stats["max_expert_rows"] = int(counts.max())
     _say(f"  -> {stats}")
+    assert stats["tokens"] == cfg.n_tokens
     if name == "zipf":
         # skewed routing: some experts receive no token, one receives most
         assert stats["empty_experts"] > 0 and stats["max_expert_rows"] > cfg.n_tokens // 2
+
+
+# Exact ties.  Expert ids of a tie group share one router row and one bias, so
+# their biased scores are bit-equal on both sides; the other experts are pushed
+# above (forced) or below the group so that the tie sits exactly at the k-th /
+# (k+1)-th place of every token (gap 0).  The lower id must win every time: no
+# near-tie exemption applies.
+_TIES = {
+    # four forced experts, three tied ones: the two lowest ids of the three are selected
+    "triple": dict(forced=[0, 100, 250, 300], tied=[7, 200, 383], tied_bias=[32.0, 32.0, 32.0], rest=None),
+    # five forced experts, a tied pair whose biases differ only in the sign of zero
+    "neg_zero_low": dict(forced=[3, 4, 5, 6, 7], tied=[50, 51], tied_bias=[-0.0, 0.0], rest=-64.0),
+    "neg_zero_high": dict(forced=[3, 4, 5, 6, 7], tied=[50, 51], tied_bias=[0.0, -0.0], rest=-64.0),
+    # the tied pair's router rows are zero: both scores are exactly zero
+    "zero_score": dict(forced=[10, 20, 30, 40, 380], tied=[60, 61], tied_bias=[0.0, -0.0], rest=-64.0, zero=True),
+}
+
+
+@pytest.mark.parametrize("n", [32, 300])
+@pytest.mark.parametrize("kind", list(_TIES))
+def test_exact_score_ties(kind, n):
+    """Bit-equal biased scores at the selection boundary go to the lower expert id (N <= 64 router
+    and top-k, and the router GEMM with multi-token top-k waves above 64 tokens)."""
+    spec = _TIES[kind]
+    cfg = get_config("decode", n_tokens=n)
+    host = generate(cfg, seed=13)
+    rw, rb = host["router_w"].clone(), host["router_b"].clone()
+    tied, forced = spec["tied"], spec["forced"]
+    if spec["rest"] is not None:
+        rb[:] = spec["rest"]
+    rb[forced] = 64.0
+    row = torch.zeros_like(rw[0]) if spec.get("zero") else rw[tied[0]].clone()
+    for e, b in zip(tied, spec["tied_bias"]):
+        rw[e] = row
+        rb[e] = b
+    host = dict(host, router_w=rw, router_b=rb)
+    _say(f"case ties {kind} N={n} forced={forced} tied={tied} bias={spec['tied_bias']}")
+    g = PA.run_gpu(cfg, PA.to_device(host))
+    # the premise: the tied logits are bit-identical on the GPU for every token
+    lg = g["logits"][:, tied]
+    assert np.all(lg.view(np.uint32) == lg[:, :1].view(np.uint32)), "tied experts' GPU logits differ"
+    k = cfg.top_k
+    n_pick = k - len(forced)
+    want = np.array(sorted(forced + tied[:n_pick]), dtype=np.int32)
+    # exemption off: every token selects the forced ids and the lowest tied ids
+    bad = np.nonzero(np.any(g["topk_ids"] != want[None, :], axis=1))[0]
+    assert bad.size == 0, f"{bad.size} tokens break the tie rule, first {bad[:5]}: {g['topk_ids'][bad[:3]]}"
+    assert np.all(g["gap"] == 0.0), "gap of an exact tie must be 0"
+    stats = PA.full_check(cfg, host, g)
+    assert stats["differing_ids"] == 0
+    _say(f"  -> {stats}")
