@@ -26,7 +26,8 @@ STAGES = ("router", "topk", "dispatch", "gate_up", "down", "combine")
 MOE_NUM_STAGES = len(STAGES)
 
 EXPORTED = ("moe_workspace_size", "moe_forward", "moe_status_string", "moe_last_hip_error",
-            "moe_block_workspace_size", "moe_block_forward", "moe_quantize_groups")
+            "moe_block_workspace_size", "moe_block_forward", "moe_quantize_groups", "moe_forward_noalloc")
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class MoeDesc(ctypes.Structure):
@@ -68,6 +69,10 @@ def lib() -> ctypes.CDLL:
                                   ctypes.POINTER(MoeWeights), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                   ctypes.POINTER(MoeAux), ctypes.c_void_p]
         L.moe_forward.restype = ctypes.c_int
+        L.moe_forward_noalloc.argtypes = [ctypes.POINTER(MoeDesc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.POINTER(MoeWeights), ctypes.c_void_p, ctypes.POINTER(MoeAux),
+                                          ctypes.c_void_p]
+        L.moe_forward_noalloc.restype = ctypes.c_int
         L.moe_block_workspace_size.argtypes = [ctypes.POINTER(MoeDesc)]
         L.moe_block_workspace_size.restype = ctypes.c_size_t
         L.moe_block_forward.argtypes = [ctypes.POINTER(MoeDesc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -137,6 +142,17 @@ def forward_raw(desc: MoeDesc, x: torch.Tensor, router_w: torch.Tensor, router_b
     return lib().moe_forward(ctypes.byref(desc), _ptr(x), _ptr(router_w), _ptr(router_b),
                              ctypes.byref(weights), _ptr(out), _ptr(workspace), workspace.numel(),
                              ctypes.byref(aux) if aux is not None else None, stream)
+
+
+def forward_noalloc_raw(desc: MoeDesc, x: torch.Tensor, router_w: torch.Tensor, router_b: torch.Tensor,
+                        weights: MoeWeights, out: torch.Tensor, aux: Optional[MoeAux] = None,
+                        stream: Optional[int] = None) -> int:
+    """Call moe_forward_noalloc (the library's own per-GPU scratch); returns the status code."""
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    return lib().moe_forward_noalloc(ctypes.byref(desc), _ptr(x), _ptr(router_w), _ptr(router_b),
+                                     ctypes.byref(weights), _ptr(out), ctypes.byref(aux) if aux is not None else None,
+                                     stream)
 
 
 class MoeLayer:

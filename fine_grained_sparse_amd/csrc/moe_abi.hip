@@ -2,8 +2,16 @@
 // The declarations and their documentation are in include/fgs_moe.h.
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "moe_plan.h"
+
+// Intermediates of moe_forward_noalloc: one copy of this array per GPU, in
+// the code object's static storage, held until the process ends.  On the
+// host the name is a stand-in object, not a device address: host code takes
+// the address from hipGetSymbolAddress, once per device (scratch_ptr below),
+// and passes that pointer on.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace fgs {
 namespace {
@@ -12,6 +20,28 @@ thread_local int g_last_hip_error = 0;
 std::atomic<int> g_arch_state[64];  // 0 unknown, 1 gfx950, 2 other
 
 std::atomic<int> g_gemm_init[64];   // per device: 0 not yet, 1 the GEMM kernels' LDS limits are raised
+
+std::atomic<void *> g_scratch_ptr[64];   // per device: the address of `scratch`, resolved on first use
+std::mutex g_scratch_mu;
+
+// Device address of this device's copy of `scratch` (dev must be current).
+int scratch_ptr(int dev, void **out) {
+    void *q = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!q) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        q = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!q) {
+            hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !q) {
+                g_last_hip_error = (int)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+                return MOE_ERR_HIP;
+            }
+            g_scratch_ptr[dev].store(q, std::memory_order_release);
+        }
+    }
+    *out = q;
+    return MOE_OK;
+}
 
 int check_device(int *dev_out = nullptr) {
     int dev = 0;
@@ -152,14 +182,16 @@ struct BlockArgs {
     float eps;
 };
 
+// static_scratch: the workspace is this device's `scratch` array (moe_forward_noalloc);
+// `workspace` is then ignored and workspace_bytes is the array's size
 int run_layer(const moe_desc *desc, const void *x, const float *router_w, const float *router_bias,
               const moe_weights *weights, void *out, void *workspace, size_t workspace_bytes, const moe_aux *aux,
-              void *stream, const BlockArgs *blk) {
+              void *stream, const BlockArgs *blk, bool static_scratch = false) {
     int st = check_desc(desc);
     if (st != MOE_OK) return st;
     if (blk && (desc->flags & MOE_FLAG_ACCUMULATE)) return MOE_ERR_ARG;
     if (desc->n_tokens == 0) return MOE_OK;
-    if (!x || !router_w || !router_bias || !weights || !out || !workspace) return MOE_ERR_ARG;
+    if (!x || !router_w || !router_bias || !weights || !out || (!workspace && !static_scratch)) return MOE_ERR_ARG;
     if (blk && (!blk->norm_pre || !blk->norm_post || !(blk->eps >= 0.0f))) return MOE_ERR_ARG;
     if (blk && desc->d_model > 16384) return MOE_ERR_UNSUPPORTED;  // the fused combine keeps a row in LDS
     const moe_weights &W = *weights;
@@ -173,7 +205,7 @@ int run_layer(const moe_desc *desc, const void *x, const float *router_w, const 
     for (const void *q : ptrs16)
         if (!aligned(q, 16)) return MOE_ERR_ARG;
     if (blk && (!aligned(blk->norm_pre, 16) || !aligned(blk->norm_post, 16))) return MOE_ERR_ARG;
-    if (!aligned(workspace, 256)) return MOE_ERR_ARG;
+    if (!static_scratch && !aligned(workspace, 256)) return MOE_ERR_ARG;
 
     const size_t xbytes = (size_t)desc->n_tokens * desc->d_model * (desc->x_dtype == MOE_DTYPE_F32 ? 4 : 2);
     if (!blk && overlaps(x, xbytes, out, xbytes)) {
@@ -185,6 +217,10 @@ int run_layer(const moe_desc *desc, const void *x, const float *router_w, const 
     int dev = 0;
     st = check_device(&dev);
     if (st != MOE_OK) return st;
+    if (static_scratch) {
+        st = scratch_ptr(dev, &workspace);
+        if (st != MOE_OK) return st;
+    }
     if (!L.stream && g_gemm_init[dev].load(std::memory_order_acquire) != 1) {   // the expert GEMMs' LDS limits
         // idempotent: concurrent first calls may both set the same attributes
         hipError_t e = gemm_kernels_init();
@@ -267,6 +303,12 @@ int moe_forward(const moe_desc *desc, const void *x, const float *router_w, cons
                 const moe_weights *weights, void *out, void *workspace, size_t workspace_bytes,
                 const moe_aux *aux, void *stream) {
     return run_layer(desc, x, router_w, router_bias, weights, out, workspace, workspace_bytes, aux, stream, nullptr);
+}
+
+int moe_forward_noalloc(const moe_desc *desc, const void *x, const float *router_w, const float *router_bias,
+                        const moe_weights *weights, void *out, const moe_aux *aux, void *stream) {
+    return run_layer(desc, x, router_w, router_bias, weights, out, nullptr, MOE_NOALLOC_SCRATCH_BYTES, aux, stream,
+                     nullptr, true);
 }
 
 size_t moe_block_workspace_size(const moe_desc *desc) {

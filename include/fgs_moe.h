@@ -41,8 +41,9 @@
  * Memory: every pointer is device memory owned by the caller.  The library
  * allocates nothing and frees nothing.  Its only mutable global state is set
  * once per device on the first call there: a cache of the device architecture
- * check and the raised LDS limit of the GEMM kernels; plus the thread-local
- * code of the last HIP error.
+ * check and the raised LDS limit of the GEMM kernels, and the address of the
+ * static scratch array behind moe_forward_noalloc; plus the thread-local code
+ * of the last HIP error.
  *
  * Execution: all work is enqueued on `stream` (a hipStream_t; NULL = the
  * default stream) without host synchronisation; results are valid once the
@@ -184,6 +185,28 @@ int moe_forward(const moe_desc *desc, const void *x, const float *router_w,
                 const float *router_bias, const moe_weights *weights, void *out,
                 void *workspace, size_t workspace_bytes, const moe_aux *aux,
                 void *stream);
+
+/* Bytes of the per-GPU device array behind moe_forward_noalloc: the full
+ * layer (d 2560, 384 experts, top-6, f 512) fits it up to 256 tokens in every
+ * weight format. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The intermediates live in a library-owned device
+ * array of MOE_NOALLOC_SCRATCH_BYTES per GPU (static storage of the code
+ * object, held until the process ends); no call allocates or frees memory.
+ * Arguments, semantics and errors as moe_forward, with the array as the
+ * workspace: a description whose moe_workspace_size() exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_WORKSPACE before anything is
+ * enqueued.  Every call on one GPU shares that GPU's array, which keeps the
+ * last call's contents (no part of it needs to start at zero): calls that can
+ * overlap on one GPU (several streams, or threads without ordering) race and
+ * give undefined results, so order them on one stream.  The first call on each
+ * device resolves the array's address; make it outside a graph capture. */
+int moe_forward_noalloc(const moe_desc *desc, const void *x, const float *router_w,
+                        const float *router_bias, const moe_weights *weights, void *out,
+                        const moe_aux *aux, void *stream);
 
 /* Workspace bytes moe_block_forward needs (0 on a bad description): the
  * moe_forward workspace plus room for the normalised input. */

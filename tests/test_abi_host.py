@@ -92,3 +92,22 @@ def test_argument_errors_before_device(lib):
     # zero tokens: a valid no-op even without buffers
     assert lib.moe_forward(ctypes.byref(_desc(n_tokens=0)), None, None, None, None, None, None, 0, None,
                            None) == B.MOE_OK
+
+
+def test_noalloc_argument_errors_before_device(lib):
+    """moe_forward_noalloc checks its arguments and the scratch size on the host, before any device call."""
+    weights = B.MoeWeights(*([16 * (i + 1) for i in range(3)] + [None] * 3 +
+                             [16 * (i + 5) for i in range(3)] + [None] * 3))
+
+    def call(desc, x=1 << 20, out=1 << 32):
+        return lib.moe_forward_noalloc(ctypes.byref(desc), x, 16, 16, ctypes.byref(weights), out, None, None)
+
+    assert call(_desc(top_k=0)) == B.MOE_ERR_ARG
+    assert call(_desc(), x=None) == B.MOE_ERR_ARG
+    assert call(_desc(), x=(1 << 20) + 8) == B.MOE_ERR_ARG
+    # the scratch array holds the full layer up to 256 tokens, not 320
+    assert B.workspace_size(_desc(n_tokens=256)) <= B.MOE_NOALLOC_SCRATCH_BYTES
+    assert B.workspace_size(_desc(n_tokens=320)) > B.MOE_NOALLOC_SCRATCH_BYTES
+    assert call(_desc(n_tokens=320)) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_forward_noalloc(ctypes.byref(_desc(n_tokens=0)), None, None, None, None, None, None,
+                                   None) == B.MOE_OK
