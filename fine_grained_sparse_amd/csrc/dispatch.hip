@@ -65,9 +65,12 @@ __device__ int block_exclusive_scan_1024(int *v, int L, int *wsum) {
 // Leaves offsets in off[0..E+2).  PER_TILE: the tile list is written one
 // thread per tile (large batches), else one thread per group.
 template <bool PER_TILE>
+__device__ void tile_list(const int *off, int *ntile, int *wsum, int E, int bm, int32_t *tiles, int32_t *n_tiles);
+
+template <bool PER_TILE>
 __device__ void offsets_and_tiles(const int *cnt, int *off, int *ntile, int *wsum, int N, int k, int E,
                                   int bm, int32_t *g_offsets, int32_t *g_exp_off, int32_t *tiles,
-                                  int32_t *n_tiles) {
+                                  int32_t *n_tiles, int32_t *tiles2 = nullptr, int32_t *n_tiles2 = nullptr) {
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += blockDim.x) off[e] = cnt[e];
     __syncthreads();
@@ -81,9 +84,21 @@ __device__ void offsets_and_tiles(const int *cnt, int *off, int *ntile, int *wsu
         g_offsets[e] = off[e];
         if (g_exp_off && e <= E) g_exp_off[e] = off[e];
     }
-    // tiles per group; the shared group (E, N rows, the most rows per expert
-    // at small N) is listed first so its workgroups start first.  Slot 0 of
-    // ntile[] is the shared group, slot 1 + e the routed expert e.
+    tile_list<PER_TILE>(off, ntile, wsum, E, bm, tiles, n_tiles);
+    // with 256-row gate/up tiles: the down product's 128-row list as well
+    if (tiles2) {
+        __syncthreads();
+        tile_list<PER_TILE>(off, ntile, wsum, E, bm / 2, tiles2, n_tiles2);
+    }
+}
+
+// The tile list of `bm` rows per tile: tiles per group; the shared group (E, N
+// rows, the most rows per expert at small N) is listed first so its
+// workgroups start first.  Slot 0 of ntile[] is the shared group, slot 1 + e
+// the routed expert e.
+template <bool PER_TILE>
+__device__ void tile_list(const int *off, int *ntile, int *wsum, int E, int bm, int32_t *tiles, int32_t *n_tiles) {
+    const int tid = threadIdx.x;
     for (int q = tid; q <= E; q += blockDim.x) {
         const int g = q == 0 ? E : q - 1;
         const int m = off[g + 1] - off[g];
@@ -117,6 +132,7 @@ __device__ void offsets_and_tiles(const int *cnt, int *off, int *ntile, int *wsu
         }
     }
     if (tid == 0) *n_tiles = nt;
+    __syncthreads();   // ntile[] is reused by a second list
 }
 
 // The k <= 8 expert ids of token t in registers: all loads issued at once
@@ -293,7 +309,8 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t *__res
 
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t *blk, int nblk, int N, int k, int E, int bm,
                                                              int32_t *g_offsets, int32_t *g_exp_off,
-                                                             int32_t *tiles, int32_t *n_tiles) {
+                                                             int32_t *tiles, int32_t *n_tiles, int32_t *tiles2,
+                                                             int32_t *n_tiles2) {
     __shared__ int cnt[1024];
     __shared__ int off[1026];
     __shared__ int ntile[1025];
@@ -330,7 +347,8 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t *blk, int n
         for (int i = tid; i < n; i += blockDim.x) blk[(size_t)b0 * E + i] = stage[i];
         __syncthreads();
     }
-    offsets_and_tiles<true>(cnt, off, ntile, wsum, N, k, E, bm, g_offsets, g_exp_off, tiles, n_tiles);
+    offsets_and_tiles<true>(cnt, off, ntile, wsum, N, k, E, bm, g_offsets, g_exp_off, tiles, n_tiles, tiles2,
+                            n_tiles2);
 }
 
 // blk[b][e]: rows of expert e in the blocks before b (from the scan)
@@ -361,7 +379,7 @@ hipError_t launch_dispatch(const Plan &p) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, p.stream, p.blk, p.nblk, p.N, p.k, p.E, p.bm,
-                       p.offsets, p.exp_off_out, p.tiles, p.n_tiles);
+                       p.offsets, p.exp_off_out, p.tiles, p.n_tiles, p.tiles2, p.n_tiles2);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(p.nblk), dim3(256), 0, p.stream, p.ids, p.blk, p.offsets, p.N,

@@ -741,6 +741,414 @@ __device__ __forceinline__ void tile_mma_dma_w8b(const uint16_t *const (&a_src)[
     if (kt + 2 < nk) step(kt + 2, L2, L1);
 }
 
+// ---------------------------------------------------------------- wide bf16 tile
+// 256 rows x 256 GEMM columns per workgroup for bf16 activations and weights
+// at large batches.  Per K stage the tile moves 64 KB of operands for 8.4
+// MFLOP, 1.5 times the flops per byte of the 128-row tile; the rate at which
+// one CU takes in operand bytes (a few tens of bytes per clock, whether they
+// come from HBM or from L2) is what bounds both tiles, so the wider tile does
+// more work per byte it takes in.  At prefill size (about 128-170 rows per
+// expert) a 256-row tile also covers an expert's rows in one tile, so each
+// weight slice is streamed once instead of once per 128 rows.
+//
+// 8 waves in 2 (rows) x 4 (columns), each wave 128 x 64 (8 x 4 sub-tiles of
+// MFMA 16x16x32 bf16).  LDS (160 KB, all of it): activation tiles in two
+// 32 KB buffers, weight tiles in three: the weights, read from HBM, are
+// fetched two stages ahead, the activations (mostly L2 hits) one stage
+// ahead.  Row layout and swizzle as in tile_mma_dma (128-byte rows, 16-byte
+// chunk c of row r at position c ^ (r & 7)).  DMAs take a wave-uniform base
+// in scalar registers (advanced by 128 bytes per stage) and a 32-bit
+// per-lane byte offset, so the eight DMA sources of a wave cost eight VGPRs.
+//
+// Stage kt reads activation buffer kt % 2 and weight buffer kt % 3, its
+// fragments read just before the MFMAs that use them (holding a whole half
+// stage of fragments on top of 128 accumulator registers does not fit a
+// wave's 256).  At the barrier that ends stage kt (every wave is done with
+// stage kt's buffers, and its own DMAs of stage kt+1 have landed) the
+// activations of stage kt+2 are fetched into buffer kt % 2 and the weights of
+// stage kt+3 into buffer kt % 3.  DMAs are issued in the order A(kt+1),
+// B(kt+2), A(kt+2), B(kt+3), ..., so "stage kt+1 landed" is vmcnt(4) (only
+// the weight DMAs of stage kt+2 remain, which keeps the memory pipe busy
+// across the barrier), or vmcnt(0) near the end.
+#ifndef FGS_WIDE_WMW
+#define FGS_WIDE_WMW 4
+#endif
+constexpr int kBMW = 256;                        // rows per wide tile
+constexpr int kWideBufB = kBMW * kDmaRowB;       // 32 KB: one operand tile of one stage
+// WMW waves along the rows (4 along the columns): 4 * WMW waves, each (256 / WMW) x 64
+template <int WMW> struct Wide {
+    static constexpr int kWaves = 4 * WMW;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kRowsPerWave = kBMW / WMW;
+    static constexpr int kSub = kRowsPerWave / 16;        // 16-row sub-tiles per wave
+    static constexpr int kDma = 32 / kWaves;              // DMAs per wave per operand and stage (1 KB each)
+};
+constexpr int kWideWMW = FGS_WIDE_WMW;
+static_assert(2 * kWideBufB + 3 * kWideBufB <= 160 * 1024, "the wide tile's buffers must fit one CU's LDS");
+
+// 16 bytes per lane from sbase + voff into LDS at `lds_dst` (wave-uniform) + 16 * lane
+__device__ __forceinline__ const uint8_t *uniform_ptr(const void *p);
+__device__ __forceinline__ void dma16s(const void *sbase_any, uint32_t voff, const void *lds_dst) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds_dst);
+    const uint8_t *sbase = uniform_ptr(sbase_any);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(dst)
+        : "memory");
+}
+
+// a pointer known to be the same in every lane, kept in scalar registers
+__device__ __forceinline__ const uint8_t *uniform_ptr(const void *p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint8_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// a_base/b_base[j]: wave-uniform bases of DMA j; a_off/b_off[j]: this lane's
+// byte offset (row and swizzled chunk of its LDS slot) at K = 0.
+typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
+// 16-byte LDS read at a 32-bit LDS byte address
+__device__ __forceinline__ uint4 lds_read16(uint32_t addr) {
+    const u32x4_t v = *reinterpret_cast<lds_u32x4_t *>((size_t)addr);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int WMW>
+__device__ __forceinline__ void tile_mma_wide(const uint8_t *a_base, const uint32_t (&a_off)[Wide<WMW>::kDma],
+                                              const uint8_t *const (&b_base)[Wide<WMW>::kDma],
+                                              const uint32_t (&b_off)[Wide<WMW>::kDma], int K, int m,
+                                              f32x4_t (&acc)[Wide<WMW>::kSub][4]) {
+    using WG = Wide<WMW>;
+    constexpr int kAPerW = WG::kDma, kBPerW = WG::kDma, kSub = WG::kSub, kRW = WG::kRowsPerWave;
+    // one LDS array: activation buffers at 0 and 32 KB, weight buffers at 64, 96 and 128 KB
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * kWideBufB];
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / kWN, wn = wave % kWN;
+    const int fr = lane & 15, fg = lane >> 4;
+    const int nk = K / kBK;
+    const uint32_t s0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;
+    auto fetch_a = [&](int kt, int buf) {
+        const uint8_t *sb = a_base + kt * (kBK * 2);
+#pragma unroll
+        for (int j = 0; j < kAPerW; ++j)
+            dma16s(sb, a_off[j], smem + buf * kWideBufB + (wave * kAPerW + j) * 1024);
+    };
+    auto fetch_b = [&](int kt, int buf) {
+#pragma unroll
+        for (int j = 0; j < kBPerW; ++j)
+            dma16s(b_base[j] + kt * (kBK * 2), b_off[j], smem + (2 + buf) * kWideBufB + (wave * kBPerW + j) * 1024);
+    };
+    // this lane's fragment byte offsets within a buffer, per 32-wide K half h: row
+    // (wave row base + lane % 16) or B row (wave column base + lane % 16) and the
+    // swizzled chunk 4 h + lane / 16 (the row's low three bits are those of lane % 16)
+    const int r_a = wm * kRW + fr, r_b = wn * 32 + fr;
+    const uint32_t la0 = s0 + r_a * kDmaRowB + (((0 + fg) ^ (fr & 7)) << 4);
+    const uint32_t la1 = s0 + r_a * kDmaRowB + (((4 + fg) ^ (fr & 7)) << 4);
+    const uint32_t lb0 = s0 + 2 * kWideBufB + r_b * kDmaRowB + (((0 + fg) ^ (fr & 7)) << 4);
+    const uint32_t lb1 = s0 + 2 * kWideBufB + r_b * kDmaRowB + (((4 + fg) ^ (fr & 7)) << 4);
+    // weight buffers lie past 64 KB, beyond the LDS read's 16-bit offset: one base
+    // register per buffer and half, the rest in the offset
+    const uint32_t lbb[3][2] = {{lb0, lb1}, {lb0 + kWideBufB, lb1 + kWideBufB},
+                                {lb0 + 2 * kWideBufB, lb1 + 2 * kWideBufB}};
+
+    // prologue: A(0) B(0) A(1) B(1) B(2); stage 0 landed once only A(1) B(1) B(2) may remain
+    fetch_a(0, 0);
+    fetch_b(0, 0);
+    if (nk > 1) { fetch_a(1, 1); fetch_b(1, 1); }
+    if (nk > 2) fetch_b(2, 2);
+    if (nk > 2) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(kAPerW + 2 * kBPerW));
+    else if (nk > 1) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(kAPerW + kBPerW));
+    else __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    auto run = [&](auto live_c) {
+        constexpr int LV = decltype(live_c)::value;   // live 16-row sub-tiles of this wave
+        // stage kt: activation buffer AB (kt % 2), weight buffer BB (kt % 3).
+        // Fragments are read as the MFMAs need them: the four weight fragments
+        // of a 32-wide K half, then one activation fragment per 16-row sub-tile
+        // (the next one requested before the current one's MFMAs)
+        auto stage = [&](int kt, auto ab_c, auto bb_c) {
+            constexpr int AB = decltype(ab_c)::value, BB = decltype(bb_c)::value;
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (LV > 0) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t la = (h ? la1 : la0) + AB * kWideBufB;
+                    const uint32_t lb = lbb[BB][h];
+                    uint4 bf[4];
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni)   // B rows wn*32 + 16 ni (ni < 2), 128 + wn*32 + 16 (ni - 2)
+                        bf[ni] = lds_read16(lb + (ni < 2 ? ni * 16 : 128 + (ni - 2) * 16) * kDmaRowB);
+                    uint4 a = lds_read16(la);
+#pragma unroll
+                    for (int mi = 0; mi < LV; ++mi) {
+                        const uint4 an = mi + 1 < LV ? lds_read16(la + (mi + 1) * 16 * kDmaRowB) : a;
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_bf16(bf[ni], a, acc[mi][ni]);
+                        a = an;
+                    }
+                    // the next half's reads stay behind this half's MFMAs (registers: four
+                    // waves per SIMD leave 128 a wave; the other waves hide the read latency)
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < nk) {
+                // own DMAs of stage kt+1 landed (the weights of stage kt+2 may remain), and
+                // every wave is done with buffers kt % 2 and kt % 3: refill them
+                if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(kBPerW));
+                else __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
+                lds_barrier();
+                if (kt + 2 < nk) fetch_a(kt + 2, AB);
+                if (kt + 3 < nk) fetch_b(kt + 3, BB);
+            }
+        };
+        int kt = 0;
+        for (; kt + 6 <= nk; kt += 6) {   // stage s: activations s % 2, weights s % 3
+            stage(kt, Live<0>{}, Live<0>{});
+            stage(kt + 1, Live<1>{}, Live<1>{});
+            stage(kt + 2, Live<0>{}, Live<2>{});
+            stage(kt + 3, Live<1>{}, Live<0>{});
+            stage(kt + 4, Live<0>{}, Live<1>{});
+            stage(kt + 5, Live<1>{}, Live<2>{});
+        }
+        if (kt < nk) stage(kt, Live<0>{}, Live<0>{});
+        if (kt + 1 < nk) stage(kt + 1, Live<1>{}, Live<1>{});
+        if (kt + 2 < nk) stage(kt + 2, Live<0>{}, Live<2>{});
+        if (kt + 3 < nk) stage(kt + 3, Live<1>{}, Live<0>{});
+        if (kt + 4 < nk) stage(kt + 4, Live<0>{}, Live<1>{});
+    };
+    // wave-uniform live count (8 sub-tiles per wave: rounded up to even; the extra
+    // sub-tile's rows are never stored)
+    const int live = min(kSub, max(0, (m - wm * kRW + 15) / 16));
+    if constexpr (kSub == 8) {
+        switch ((live + 1) & ~1) {
+            case 8: run(Live<8>{}); break;
+            case 6: run(Live<6>{}); break;
+            case 4: run(Live<4>{}); break;
+            case 2: run(Live<2>{}); break;
+            default: run(Live<0>{}); break;
+        }
+    } else {
+        switch (live) {
+            case 4: run(Live<4>{}); break;
+            case 3: run(Live<3>{}); break;
+            case 2: run(Live<2>{}); break;
+            case 1: run(Live<1>{}); break;
+            default: run(Live<0>{}); break;
+        }
+    }
+}
+
+// ---- the wide tile with E4M3 weights (one FP32 scale per output channel,
+// applied in the epilogue) and bf16 activations: 16 waves of 64 x 64.  A
+// stage holds 256 activation rows of 128 bytes (32 KB) and 256 weight rows of
+// 64 bytes (16 KB; chunk c of row r at position c ^ ((r >> 2) & 3), as in
+// tile_mma_dma_w8), three buffers of each (144 KB), both operands fetched two
+// stages ahead: at the barrier that ends stage kt (own DMAs of stage kt+1
+// landed; stage kt+2's may remain) stage kt+3 is fetched into buffers kt % 3.
+// A fragment read takes the 8 code bytes of its K range and widens them to
+// bf16 exactly.
+constexpr int kWideW8BufB = kBMW * kW8RowB;   // 16 KB
+typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) const u32x2v_t lds_u32x2_t;
+__device__ __forceinline__ uint2 lds_read8(uint32_t addr) {
+    const u32x2v_t v = *reinterpret_cast<lds_u32x2_t *>((size_t)addr);
+    return make_uint2(v.x, v.y);
+}
+
+template <int WMW>
+__device__ __forceinline__ void tile_mma_wide_w8(const uint8_t *a_base, const uint32_t (&a_off)[Wide<WMW>::kDma],
+                                                 const uint8_t *b_base, uint32_t b_off, int K, int m,
+                                                 f32x4_t (&acc)[Wide<WMW>::kSub][4]) {
+    using WG = Wide<WMW>;
+    constexpr int kAPerW = WG::kDma, kSub = WG::kSub, kRW = WG::kRowsPerWave;
+    static_assert(WG::kWaves == 16, "one weight DMA per wave and stage");
+    constexpr int G = kAPerW + 1;   // DMAs per wave and stage
+    // weight buffers at 0, 16 and 32 KB (their reads fit the 16-bit offset), activations at 48, 80, 112 KB
+    constexpr int kAOff = 3 * kWideW8BufB;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * kWideW8BufB + 3 * kWideBufB];
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / kWN, wn = wave % kWN;
+    const int fr = lane & 15, fg = lane >> 4;
+    const int nk = K / kBK;
+    const uint32_t s0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;
+    auto fetch = [&](int kt, int buf) {
+        const uint8_t *sa = a_base + kt * (kBK * 2);
+#pragma unroll
+        for (int j = 0; j < kAPerW; ++j)
+            dma16s(sa, a_off[j], smem + kAOff + buf * kWideBufB + (wave * kAPerW + j) * 1024);
+        dma16s(b_base + kt * kBK, b_off, smem + buf * kWideW8BufB + wave * 1024);
+    };
+    // this lane's fragment addresses per 32-wide K half h: activation row
+    // (wave row base + lane % 16), chunk 4 h + lane / 16; weight row (wave
+    // column base + lane % 16), code bytes 8 (4 h + lane / 16) .. + 7
+    const int r_a = wm * kRW + fr, r_b = wn * 32 + fr;
+    uint32_t la[3][2], lb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = 4 * h + fg;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) la[q][h] = s0 + kAOff + q * kWideBufB + r_a * kDmaRowB + ((c ^ (fr & 7)) << 4);
+        lb[h] = s0 + r_b * kW8RowB + ((((c >> 1) ^ (fr >> 2)) & 3) << 4) + ((c & 1) << 3);
+    }
+
+    fetch(0, 0);
+    if (nk > 1) fetch(1, 1);
+    if (nk > 2) fetch(2, 2);
+    if (nk > 2) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(2 * G));
+    else if (nk > 1) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(G));
+    else __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    auto run = [&](auto live_c) {
+        constexpr int LV = decltype(live_c)::value;
+        auto stage = [&](int kt, auto s_c) {
+            constexpr int S = decltype(s_c)::value;   // buffer kt % 3
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (LV > 0) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    uint4 bf[4];
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni)   // B rows wn*32 + 16 ni (ni < 2), 128 + wn*32 + 16 (ni - 2)
+                        bf[ni] = e4m3x8_to_bf16x8(
+                            lds_read8(lb[h] + S * kWideW8BufB + (ni < 2 ? ni * 16 : 128 + (ni - 2) * 16) * kW8RowB));
+                    uint4 a = lds_read16(la[S][h]);
+#pragma unroll
+                    for (int mi = 0; mi < LV; ++mi) {
+                        const uint4 an = mi + 1 < LV ? lds_read16(la[S][h] + (mi + 1) * 16 * kDmaRowB) : a;
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_bf16(bf[ni], a, acc[mi][ni]);
+                        a = an;
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < nk) {
+                if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(G));
+                else __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
+                lds_barrier();
+                if (kt + 3 < nk) fetch(kt + 3, S);
+            }
+        };
+        int kt = 0;
+        for (; kt + 3 <= nk; kt += 3) {   // stage s uses buffers s % 3
+            stage(kt, Live<0>{});
+            stage(kt + 1, Live<1>{});
+            stage(kt + 2, Live<2>{});
+        }
+        if (kt < nk) stage(kt, Live<0>{});
+        if (kt + 1 < nk) stage(kt + 1, Live<1>{});
+    };
+    const int live = min(kSub, max(0, (m - wm * kRW + 15) / 16));
+    switch (live) {
+        case 4: run(Live<4>{}); break;
+        case 3: run(Live<3>{}); break;
+        case 2: run(Live<2>{}); break;
+        case 1: run(Live<1>{}); break;
+        default: run(Live<0>{}); break;
+    }
+}
+
+// bf16 x with bf16 weights (W8 false) or E4M3 weights with per-channel scales (W8 true),
+// 256-row tiles.  grid: (ceil(max(f, fs) / 128), tile capacity); block 256 * WMW
+template <int WMW, bool W8>
+__global__ __launch_bounds__(Wide<WMW>::kThreads) void gate_up_gemm_wide_kernel(
+    const uint16_t *__restrict__ x, const void *__restrict__ wg, const void *__restrict__ wu,
+    const float *__restrict__ sg, const float *__restrict__ su, const void *__restrict__ wsg,
+    const void *__restrict__ wsu, const float *__restrict__ ssg, const float *__restrict__ ssu,
+    const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ por, uint16_t *__restrict__ H, int ldh, int d, int E, int k, int f, int fs) {
+    int item;
+    if (!xcd_item(*n_tiles * (int)gridDim.x, item)) return;
+    const int u = item / gridDim.x;
+    const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
+    const bool shared = g == E;
+    const int fg = shared ? fs : f;
+    constexpr int kHalf = kBN / 2;  // H columns per tile
+    const int c0 = (item % gridDim.x) * kHalf;
+    if (c0 >= fg) return;
+    const int gstart = offsets[g];
+    const int row0 = gstart + m0, m = min(kBMW, offsets[g + 1] - row0);
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), pos = lane & 7;
+    auto token_row = [&](int r) { return shared ? (row0 + r - gstart) : por[row0 + r] / k; };
+    using WG = Wide<WMW>;
+    constexpr int kAPerW = WG::kDma, kSub = WG::kSub, kRW = WG::kRowsPerWave;
+    constexpr int kBPerW = W8 ? 1 : WG::kDma;
+    constexpr int sw = W8 ? 1 : 2;   // bytes per weight
+    // lane i of activation DMA j of wave w fills tile row 8 (n w + j) + i / 8 at swizzled chunk position i % 8
+    uint32_t a_off[kAPerW], b_off[kBPerW];
+    const uint8_t *b_base[kBPerW];
+#pragma unroll
+    for (int j = 0; j < kAPerW; ++j) {
+        const int r = 8 * (w * kAPerW + j) + (lane >> 3);
+        const int t = token_row(r < m ? r : 0);   // rows past the group end read row 0 (never stored)
+        a_off[j] = (uint32_t)t * (uint32_t)(2 * d) + (uint32_t)((pos ^ (r & 7)) << 4);
+    }
+    // weight rows: tile rows [0, 128) are gate rows c0.., [128, 256) the matching up rows;
+    // the first half of the waves fetch gate rows, the rest up rows
+    const size_t wrow0 = shared ? 0 : (size_t)g * f;
+    const uint8_t *gate_m = uniform_ptr((const uint8_t *)(shared ? wsg : wg) + wrow0 * d * sw);
+    const uint8_t *up_m = uniform_ptr((const uint8_t *)(shared ? wsu : wu) + wrow0 * d * sw);
+#pragma unroll
+    for (int j = 0; j < kBPerW; ++j) {
+        // bf16: lane i of DMA j fills row 8 (n w + j) + i / 8, position i % 8 (chunk (i % 8) ^ (row & 7));
+        // E4M3: lane i of the wave's DMA fills row 16 w + i / 4, position i % 4 (chunk (i % 4) ^ ((row >> 2) & 3))
+        const int r = W8 ? 16 * w + (lane >> 2) : 8 * (w * kBPerW + j) + (lane >> 3);
+        const int c = c0 + (r & (kHalf - 1));
+        const int chunk = W8 ? (((lane & 3) ^ (r >> 2)) & 3) : (pos ^ (r & 7));
+        b_base[j] = w < WG::kWaves / 2 ? gate_m : up_m;
+        // columns past f_g (only when f_g is not a multiple of 128) re-read column c0; never stored
+        b_off[j] = (uint32_t)(c < fg ? c : c0) * (uint32_t)(sw * d) + (uint32_t)(chunk << 4);
+    }
+    f32x4_t acc[kSub][4];
+#pragma unroll
+    for (int i = 0; i < kSub; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (W8) tile_mma_wide_w8<WMW>(uniform_ptr(x), a_off, b_base[0], b_off[0], d, m, acc);
+    else tile_mma_wide<WMW>(uniform_ptr(x), a_off, b_base, b_off, d, m, acc);
+
+    // epilogue: acc[mi][ni][q] is row wm*kRW + mi*16 + lane%16, GEMM column
+    // b_row_of(wn, ni) + 4*(lane/16) + q; gate tile ni and up tile ni+2 share
+    // (row, H column), so each lane writes 4 consecutive H values
+    const int wm = w >> 2, wn = w & 3;
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+        const int col = c0 + wn * 32 + ni * 16 + (lane >> 4) * 4;
+        if (col >= fg) continue;  // f_g is a multiple of 64: all four in range or all out
+        float gs[4] = {1.f, 1.f, 1.f, 1.f}, us[4] = {1.f, 1.f, 1.f, 1.f};
+        if (W8) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                gs[q] = shared ? ssg[col + q] : sg[wrow0 + col + q];
+                us[q] = shared ? ssu[col + q] : su[wrow0 + col + q];
+            }
+        }
+#pragma unroll
+        for (int mi = 0; mi < kSub; ++mi) {
+            const int r = wm * kRW + mi * 16 + (lane & 15);
+            if (r < m) {
+                float hv[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) hv[q] = silu(acc[mi][ni][q] * gs[q]) * (acc[mi][ni + 2][q] * us[q]);
+                *reinterpret_cast<uint2 *>(H + (size_t)(row0 + r) * ldh + col) =
+                    make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+            }
+        }
+    }
+}
+
 // grid: (ceil(max(f, fs) / 128), tile capacity); block 512; LDS kGemmLds
 // (bf16 x and weights: none; the direct-to-LDS tile uses kGemmLdsDma of static LDS)
 template <int WM, bool XF32>
@@ -1686,6 +2094,16 @@ hipError_t launch_gate_up_gemm(const Plan &p) {
     // spare tile rows: the XCD-aware order needs n + 8 * kXcdTiles * gx launch slots
     const int gx = (fmax + kBN / 2 - 1) / (kBN / 2);
     dim3 grid(gx, p.max_tiles + kXcds * kXcdTiles), block(kThreads);
+    if (p.bm == kGemmBMWide) {   // bf16 activations, bf16 or per-channel E4M3 weights, 256-row tiles (gemm_bm)
+#define FGS_GUW(W8)                                                                                            \
+    hipLaunchKernelGGL((gate_up_gemm_wide_kernel<kWideWMW, W8>), grid, dim3(Wide<kWideWMW>::kThreads), 0, p.stream, \
+                       (const uint16_t *)p.x, p.W.w_gate, p.W.w_up, p.W.s_gate, p.W.s_up, p.W.ws_gate, p.W.ws_up,   \
+                       p.W.ss_gate, p.W.ss_up, p.tiles, p.n_tiles, p.offsets, p.por, p.H, p.ldh, p.d, p.E, p.k, p.f, \
+                       p.fs)
+        if (p.wdt == MOE_DTYPE_FP8_E4M3) FGS_GUW(true); else FGS_GUW(false);
+#undef FGS_GUW
+        return hipGetLastError();
+    }
     if (p.aq) {
         hipError_t e = launch_quant_groups(p.x, 1, p.d, p.N, p.d, p.xq, p.d, p.xs, p.d / 128, p.stream);
         if (e != hipSuccess) return e;
@@ -1721,6 +2139,13 @@ hipError_t launch_down_gemm(const Plan &p) {
     const int gx = (p.d + kBN - 1) / kBN;
     dim3 grid(gx, p.max_tiles + kXcds * kXcdTiles), block(kThreads);
     uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y);
+    // the down product (K = f, 8 stages at f = 512) keeps 128-row tiles: with wide
+    // gate/up tiles the dispatch writes it a list of its own (a 256-row down tile was
+    // slower at prefill size, 341 against 320 us: short K loop, idle row waves; taking
+    // each wide entry as two 128-row items cost 15-23 us against the plain list)
+    const int32_t *tiles = p.bm == kGemmBMWide ? p.tiles2 : p.tiles;
+    const int32_t *n_tiles = p.bm == kGemmBMWide ? p.n_tiles2 : p.n_tiles;
+    grid.y = (p.bm == kGemmBMWide ? p.max_tiles2 : p.max_tiles) + kXcds * kXcdTiles;
     if (p.aq) {
 #define FGS_DNF(B, D)                                                                                          \
     hipLaunchKernelGGL((down_gemm_f8_kernel<B, D>), grid, block, D ? 0 : kGemmLds, p.stream, p.hq, p.hs, p.ldh,     \
@@ -1736,7 +2161,7 @@ hipError_t launch_down_gemm(const Plan &p) {
     hipLaunchKernelGGL((down_gemm_kernel<WM>), grid, block,                                                       \
                        (WM == kWBf16 || WM == kWFp8Row || WM == kWFp8BlkDma) ? 0 : kGemmLds, p.stream, p.H,             \
                        p.ldh, p.W.w_down, p.W.s_down,                                                                \
-                       p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs)
+                       p.W.ws_down, p.W.ss_down, tiles, n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs)
     if (p.wdt != MOE_DTYPE_FP8_E4M3) FGS_DNG(kWBf16);
     else if (p.flags & MOE_FLAG_FP8_BLOCK128) {
         if (w8b_dma(p)) FGS_DNG(kWFp8BlkDma);

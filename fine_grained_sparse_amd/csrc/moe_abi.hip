@@ -85,8 +85,9 @@ int check_desc(const moe_desc *d) {
 }
 
 struct Layout {
-    size_t partial, ids, tw, blk, offsets, tiles, n_tiles, por, rop, H, Y, w3, rflags, xq, xs, hq, hs, hf, total;
-    int ks, kslice, nblk, max_tiles, bm, ldh;
+    size_t partial, ids, tw, blk, offsets, tiles, n_tiles, tiles2, n_tiles2, por, rop, H, Y, w3, rflags, xq, xs, hq,
+        hs, hf, total;
+    int ks, kslice, nblk, max_tiles, max_tiles2, bm, ldh;
     bool stream, rgemm, aq;
 };
 
@@ -111,8 +112,11 @@ Layout layout_for(const moe_desc *d) {
     L.nblk = (int)((N + 255) / 256);
     if (L.nblk < 1) L.nblk = 1;
     L.stream = stream_path(d->n_tokens, d->d_model, d->d_ff, d->d_ff_shared);
-    L.bm = L.stream ? (d->n_tokens < 1 ? 1 : d->n_tokens < kStreamBM ? d->n_tokens : kStreamBM) : kGemmBM;
+    L.bm = L.stream ? (d->n_tokens < 1 ? 1 : d->n_tokens < kStreamBM ? d->n_tokens : kStreamBM)
+                    : gemm_bm(d->n_tokens, d->d_model, d->top_k, d->d_ff, d->d_ff_shared, d->x_dtype, d->w_dtype,
+                              d->flags);
     L.max_tiles = max_tiles_for(d->n_tokens, d->top_k, d->n_experts, L.bm);
+    L.max_tiles2 = L.bm == kGemmBMWide ? max_tiles_for(d->n_tokens, d->top_k, d->n_experts, kGemmBM) : 0;
     L.ldh = d->d_ff > d->d_ff_shared ? d->d_ff : d->d_ff_shared;
     const size_t rows = N * k + N;
     size_t cur = 0;
@@ -123,6 +127,8 @@ Layout layout_for(const moe_desc *d) {
     L.offsets = take(cur, (E + 2) * 4);
     L.tiles = take(cur, (size_t)L.max_tiles * 2 * 4);
     L.n_tiles = take(cur, 4);
+    L.tiles2 = take(cur, (size_t)L.max_tiles2 * 2 * 4);
+    L.n_tiles2 = take(cur, L.max_tiles2 ? 4 : 0);
     L.por = take(cur, N * k * 4);
     L.rop = take(cur, N * k * 4);
     L.H = take(cur, rows * L.ldh * 2);
@@ -245,6 +251,9 @@ int run_layer(const moe_desc *desc, const void *x, const float *router_w, const 
     p.exp_off_out = aux ? aux->expert_offsets : nullptr;
     p.tiles = (int32_t *)(ws + L.tiles); p.n_tiles = (int32_t *)(ws + L.n_tiles);
     p.max_tiles = L.max_tiles; p.bm = L.bm;
+    p.tiles2 = L.max_tiles2 ? (int32_t *)(ws + L.tiles2) : nullptr;
+    p.n_tiles2 = L.max_tiles2 ? (int32_t *)(ws + L.n_tiles2) : nullptr;
+    p.max_tiles2 = L.max_tiles2;
     p.por = (aux && aux->pair_of_row) ? aux->pair_of_row : (int32_t *)(ws + L.por);
     p.rop = (aux && aux->row_of_pair) ? aux->row_of_pair : (int32_t *)(ws + L.rop);
     p.H = (uint16_t *)(ws + L.H); p.ldh = L.ldh;

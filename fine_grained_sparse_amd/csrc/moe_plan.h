@@ -33,6 +33,9 @@ struct Plan {
     int32_t *tiles;      // [max_tiles] packed (group << 16... see dispatch) entries
     int32_t *n_tiles;    // [1]
     int max_tiles;
+    int32_t *tiles2;     // with wide gate/up tiles (bm 256): the down product's 128-row list, else nullptr
+    int32_t *n_tiles2;
+    int max_tiles2;
     int bm;              // rows per tile of the expert kernels
     int32_t *por, *rop;  // [N*k]
     uint16_t *H;         // [N*k + N][ldh] bfloat16 SwiGLU activations
@@ -81,6 +84,25 @@ inline bool stream_path(int N, int d, int f, int fs) {
     return N <= kStreamMaxN && d <= 4096 && f <= 512 && fs <= 512;
 }
 constexpr int kGemmBM = 128;  // rows per tile of the grouped GEMMs
+// bf16 activations with bf16 or per-channel E4M3 weights at large batches take
+// 256-row tiles for gate/up (the wide tile: more flops per operand byte a CU
+// takes in); the down product takes each such entry as two 128-row items.  Their DMAs use
+// 32-bit byte offsets, so x and H must stay below 4 GB.
+constexpr int kGemmBMWide = 256;
+#ifndef FGS_WIDE_MIN_N
+#define FGS_WIDE_MIN_N 8192
+#endif
+constexpr int kWideMinN = FGS_WIDE_MIN_N;
+// only the multi-block dispatch (more than 256 tokens) writes the down product's own list
+static_assert(kWideMinN > 256, "wide tiles need the multi-block dispatch");
+inline int gemm_bm(int N, int d, int k, int f, int fs, int xdt, int wdt, uint32_t flags) {
+    const long ldh = f > fs ? f : fs;
+    const bool fits32 = (long)N * d * 2 < (1L << 32) && ((long)N * k + N) * ldh * 2 < (1L << 32);
+    const bool wide_w = wdt == MOE_DTYPE_BF16 || (wdt == MOE_DTYPE_FP8_E4M3 && !(flags & MOE_FLAG_FP8_BLOCK128));
+    if (xdt == MOE_DTYPE_BF16 && wide_w && !(flags & MOE_FLAG_FP8_ACT_QUANT) && N >= kWideMinN && fits32)
+        return kGemmBMWide;
+    return kGemmBM;
+}
 
 // Router tiling: wave tile of (16*MT tokens) x (16*NT experts); the k range is
 // cut into ks slices so that small batches still spread over many waves.

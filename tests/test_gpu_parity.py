@@ -201,6 +201,26 @@ def test_shape_limits(cfg_name, over):
     _run_full(get_config(cfg_name, **over))
 
 
+_WIDE = dict(x_dtype="bf16")
+
+
+@pytest.mark.parametrize("cfg_name,over", [
+    ("decode", dict(n_tokens=8200)),                                   # ragged last tiles, bf16 weights
+    ("decode", dict(n_tokens=8192, w_dtype="fp8")),                    # E4M3 weights, per-channel scales
+    # f not a multiple of 128 (a half-empty column block), K of 3 stages, about 3000 rows per expert
+    ("toy", dict(_WIDE, n_tokens=8192, n_experts=16, d_model=192, d_ff=192, d_ff_shared=64)),
+    ("toy", dict(_WIDE, n_tokens=8192, n_experts=16, d_model=192, d_ff=192, d_ff_shared=64, w_dtype="fp8")),
+    # short K (d = 128: 2 stages), f = 64, the most experts, the largest k
+    ("toy", dict(_WIDE, n_tokens=8300, n_experts=512, top_k=8, d_model=128, d_ff=64, d_ff_shared=128)),
+    ("toy", dict(_WIDE, n_tokens=8192, n_experts=64, d_model=64, d_ff=64, d_ff_shared=64, w_dtype="fp8")),  # 1 stage
+])
+def test_wide_tile(cfg_name, over):
+    """Large batches with bf16 activations run the 256-row gate/up tiles (bf16 or per-channel E4M3
+    weights) and take each entry as two 128-row items in the down product: odd widths, ragged and
+    multi-tile experts, short K."""
+    _run_full(get_config(cfg_name, **over))
+
+
 @pytest.mark.parametrize("n", [300, 40, 4096, 8192])
 def test_router_full_fp32_weights(n):
     """FP32 router weights that are not bf16 values (mid and lo split terms nonzero) for a scattered
