@@ -17,6 +17,7 @@
 // The scan also writes the tile list of the expert kernels: one entry
 // (group, first row within the group) per `bm` rows of every non-empty group,
 // shared group first, then routed experts in id order.
+#include "dispatch_small.h"
 #include "moe_common.h"
 #include "moe_plan.h"
 
@@ -135,14 +136,6 @@ __device__ void tile_list(const int *off, int *ntile, int *wsum, int E, int bm, 
     __syncthreads();   // ntile[] is reused by a second list
 }
 
-// The k <= 8 expert ids of token t in registers: all loads issued at once
-// (slots past k repeat slot k-1; a thread without a token reads token 0).
-__device__ __forceinline__ void load_token_ids(const int32_t *ids, int t, int k, bool live, int (&e)[8]) {
-    const int32_t *p = ids + (size_t)(live ? t : 0) * k;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = p[j < k ? j : k - 1];
-}
-
 // Rank of every pair of one block inside its expert, then the scatter.
 // `e` holds the ids of this thread's token (block b, token b*kBT + tid).
 __device__ void block_scatter(const int (&e)[8], uint32_t *bits, const int *base, int b, int N, int k, int E,
@@ -171,93 +164,12 @@ __device__ void block_scatter(const int (&e)[8], uint32_t *bits, const int *base
         }
 }
 
-// ---- one-wave path (N <= 64, every group within one tile): a single wave,
-// lane t holding token t, so no step needs a workgroup barrier.  Per-expert
-// counts and 64-bit token masks come from LDS atomics; the offsets and the
-// tile list are wave-wide prefix sums over 16 experts per lane.
-
-// inclusive prefix sum over the 64 lanes
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-        const int o = __shfl_up(v, s, kWave);
-        if (lane >= s) v += o;
-    }
-    return v;
-}
+// ---- one-wave path (N <= 64, every group within one tile): dispatch_small.h
 
 __global__ __launch_bounds__(64) void dispatch_wave_kernel(
     const int32_t *__restrict__ ids, int N, int k, int E, int32_t *g_offsets, int32_t *g_exp_off,
     int32_t *tiles, int32_t *n_tiles, int32_t *por, int32_t *rop) {
-    __shared__ int cnt[1024];
-    __shared__ unsigned long long mask[1024];
-    __shared__ int off[1024];
-    const int lane = threadIdx.x;
-    const bool live = lane < N;
-    int my[8];
-    load_token_ids(ids, lane, k, live, my);
-    for (int e = lane; e < E; e += 64) { cnt[e] = 0; mask[e] = 0ull; }
-    __syncthreads();
-    if (live) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (j < k) {
-                atomicAdd(&cnt[my[j]], 1);
-                atomicOr(&mask[my[j]], 1ull << lane);
-            }
-    }
-    __syncthreads();
-    // lane l owns experts [C l, C l + C): exclusive offsets and tile slots
-    const int C = (E + 63) / 64;   // <= 16
-    int c[16], sum = 0, nonempty = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int e = C * lane + i;
-        c[i] = (i < C && e < E) ? cnt[e] : 0;
-        sum += c[i];
-        nonempty += c[i] > 0;
-    }
-    const int base = wave_inclusive_scan(sum) - sum;
-    const int tbase = wave_inclusive_scan(nonempty) - nonempty;   // routed tiles before this lane's experts
-    const int total = N * k;
-    int run = base, trun = 1 + tbase;   // tile 0 is the shared group
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int e = C * lane + i;
-        if (i < C && e < E) {
-            off[e] = run;
-            g_offsets[e] = run;
-            if (g_exp_off) g_exp_off[e] = run;
-            if (c[i] > 0) {
-                tiles[2 * trun] = e;
-                tiles[2 * trun + 1] = 0;
-                ++trun;
-            }
-            run += c[i];
-        }
-    }
-    if (lane == 63) *n_tiles = trun;   // the last lane's running count is the total
-    if (lane == 0) {
-        g_offsets[E] = total;
-        g_offsets[E + 1] = total + N;
-        if (g_exp_off) g_exp_off[E] = total;
-        tiles[0] = E;
-        tiles[1] = 0;
-    }
-    __syncthreads();
-    // rank of token t among expert e's tokens: the tokens below t in e's mask
-    if (live) {
-        const unsigned long long below = (1ull << lane) - 1ull;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (j >= k) break;
-            const int e = my[j];
-            const int pos = off[e] + __popcll(mask[e] & below);
-            por[pos] = lane * k + j;
-            rop[(size_t)lane * k + j] = pos;
-        }
-    }
+    dispatch_small(ids, N, k, E, g_offsets, g_exp_off, tiles, n_tiles, por, rop);
 }
 
 // ---- one-block path (N <= 256): everything in one workgroup of 1024 threads
@@ -364,7 +276,63 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t *__
     block_scatter(my, bits, base, blockIdx.x, N, k, E, por, rop);   // its first barrier publishes base
 }
 
+// ---- scan and scatter in one launch (after dispatch_hist_kernel).  Every
+// block reads all blocks' counts (nblk x E values, coalesced over the
+// experts), forms the expert totals and its own per-expert prefix, scans the
+// totals into the group offsets and scatters its tokens; block 0 also writes
+// the offsets and the tile lists.  This trades the single-workgroup scan
+// kernel and one launch for nblk x E reads per block, which is cheap up to
+// kFusedScanMaxBlk blocks.
+#ifndef FGS_DISPATCH_FUSED_SCAN
+#define FGS_DISPATCH_FUSED_SCAN 0
+#endif
+constexpr int kFusedScanMaxBlk = 64;   // N <= 16384 tokens
+__global__ __launch_bounds__(1024) void dispatch_scan_scatter_kernel(
+    const int32_t *__restrict__ ids, const int32_t *__restrict__ blk, int nblk, int N, int k, int E, int bm,
+    int32_t *g_offsets, int32_t *g_exp_off, int32_t *tiles, int32_t *n_tiles, int32_t *tiles2, int32_t *n_tiles2,
+    int32_t *por, int32_t *rop) {
+    __shared__ int cnt[1024];
+    __shared__ int pre[1024];
+    __shared__ int off[1026];
+    __shared__ int ntile[1025];
+    __shared__ int wsum[17];
+    __shared__ uint32_t bits[1024 * kBTW];
+    const int tid = threadIdx.x, b = blockIdx.x;
+    const int t = b * kBT + tid;
+    int my[8];
+    load_token_ids(ids, t, k, tid < kBT && t < N, my);
+    // expert e: total over all blocks and the rows in blocks before b, 16 loads in flight
+    for (int e = tid; e < E; e += blockDim.x) {
+        int tot = 0, before = 0;
+        for (int b0 = 0; b0 < nblk; b0 += 16) {
+            int c[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c[i] = b0 + i < nblk ? blk[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                tot += c[i];
+                before += b0 + i < b ? c[i] : 0;
+            }
+        }
+        cnt[e] = tot;
+        pre[e] = before;
+    }
+    __syncthreads();
+    if (b == 0) {
+        offsets_and_tiles<true>(cnt, off, ntile, wsum, N, k, E, bm, g_offsets, g_exp_off, tiles, n_tiles, tiles2,
+                                n_tiles2);
+    } else {
+        for (int e = tid; e < E; e += blockDim.x) off[e] = cnt[e];
+        __syncthreads();
+        block_exclusive_scan_1024(off, E, wsum);
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) pre[e] += off[e];
+    block_scatter(my, bits, pre, b, N, k, E, por, rop);   // its first barrier publishes pre
+}
+
 hipError_t launch_dispatch(const Plan &p) {
+    if (p.fused_route) return hipSuccess;   // done by the fused top-k kernel
     if (p.N <= 64 && p.bm >= p.N) {   // one wave; every group fits one tile
         hipLaunchKernelGGL(dispatch_wave_kernel, dim3(1), dim3(64), 0, p.stream, p.ids, p.N, p.k, p.E, p.offsets,
                            p.exp_off_out, p.tiles, p.n_tiles, p.por, p.rop);
@@ -378,6 +346,14 @@ hipError_t launch_dispatch(const Plan &p) {
     hipLaunchKernelGGL(dispatch_hist_kernel, dim3(p.nblk), dim3(256), 0, p.stream, p.ids, p.N, p.k, p.E, p.blk);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+#if FGS_DISPATCH_FUSED_SCAN
+    if (p.nblk <= kFusedScanMaxBlk) {
+        hipLaunchKernelGGL(dispatch_scan_scatter_kernel, dim3(p.nblk), dim3(1024), 0, p.stream, p.ids, p.blk, p.nblk,
+                           p.N, p.k, p.E, p.bm, p.offsets, p.exp_off_out, p.tiles, p.n_tiles, p.tiles2, p.n_tiles2,
+                           p.por, p.rop);
+        return hipGetLastError();
+    }
+#endif
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, p.stream, p.blk, p.nblk, p.N, p.k, p.E, p.bm,
                        p.offsets, p.exp_off_out, p.tiles, p.n_tiles, p.tiles2, p.n_tiles2);
     err = hipGetLastError();

@@ -261,6 +261,7 @@ int run_layer(const moe_desc *desc, const void *x, const float *router_w, const 
     p.w3 = (uint16_t *)(ws + L.w3);
     p.rflags = L.rgemm ? (int32_t *)(ws + L.rflags) : nullptr;
     p.use_stream = L.stream;
+    p.fused_route = L.stream && fused_route_ok(p.N, p.xdt);
     p.stream = (hipStream_t)stream;
     p.aq = L.aq;
     if (L.aq) {

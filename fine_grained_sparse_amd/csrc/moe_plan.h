@@ -53,6 +53,7 @@ struct Plan {
     float *hs;           // [N*k + N][ldh/128] their group scales
     float *hf;           // [N*k + N][ldh] FP32 hidden activations (stream path, before quantisation)
     bool use_stream;     // decode-shaped expert path; otherwise the grouped GEMMs
+    bool fused_route;    // top-k and dispatch in one kernel (fused_route_ok)
     hipStream_t stream;
 };
 
@@ -111,6 +112,19 @@ struct RouterTiling { int mt, nt, ks; };
 // (one k-slice, W_r split into three bf16 terms along K).
 constexpr int kRouterGemmN = 64;
 inline bool router_gemm(int N, int xdt) { return xdt == MOE_DTYPE_BF16 && N > kRouterGemmN; }
+
+// Batches of at most kFusedRouteN tokens run top-k and dispatch as one kernel
+// (router_mfma partial sums; on the stream path every group is one tile).
+// One MI355X, d = 2560, E = 384, top-6: 29.8 against 32.1 us per layer step at
+// N = 1, 37.7 against 39.4 at N = 2, equal at N = 4 (the selections of more
+// tokens on one CU then cost what the launch saves).
+#ifndef FGS_FUSED_ROUTE_N
+#define FGS_FUSED_ROUTE_N 4
+#endif
+constexpr int kFusedRouteN = FGS_FUSED_ROUTE_N;   // 0 switches the fusion off
+static_assert(kFusedRouteN >= 0 && kFusedRouteN <= 7, "one workgroup of at most 7 waves");
+constexpr int kFusedRouteCap = kFusedRouteN > 0 ? kFusedRouteN : 1;   // array and workgroup bounds
+inline bool fused_route_ok(int N, int xdt) { return N >= 1 && N <= kFusedRouteN && !router_gemm(N, xdt); }
 // k-slices of the router GEMM: 3 c slices, c per split term (hi, mid, lo),
 // so that a slice never straddles two terms and the slices of all-zero terms
 // can be skipped; c <= 4 divides the d/64 K stages of a term and is raised

@@ -14,6 +14,7 @@
 // id, so equal scores go to the lower id and the result is independent of the
 // reduction order.  A (k+1)-th round, run only when the gap is requested,
 // yields the selection gap.
+#include "dispatch_small.h"
 #include "moe_common.h"
 #include "moe_plan.h"
 
@@ -36,7 +37,7 @@ template <int VPL>
 __device__ __forceinline__ void select_token(const float (&h)[VPL], const float (&bv)[VPL], int lane, int t, int E,
                                              int k, bool renorm, float *__restrict__ logits_out,
                                              int32_t *__restrict__ ids, float *__restrict__ tw,
-                                             float *__restrict__ gap) {
+                                             float *__restrict__ gap, int32_t *ids_lds = nullptr) {
     uint64_t key[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
@@ -111,9 +112,42 @@ __device__ __forceinline__ void select_token(const float (&h)[VPL], const float 
         for (int j = 0; j < 8; ++j)
             if (j == lane) { e = sel[j]; hv = selh[j]; }
         ids[(size_t)t * k + lane] = e;
+        if (ids_lds) ids_lds[t * k + lane] = e;
         tw[(size_t)t * k + lane] = renorm ? expf(hv - hmax) / zsum : sigmoidf_(hv);
     }
     if (gap && lane == 0) gap[t] = (k < E) ? sk - sk1 : __builtin_inff();
+}
+
+// Logits of one token from the router's k-slice partial sums (no split-term
+// flags): slices added in order 0..ks-1 (ks <= 10).  Every load is issued up
+// front from a valid address (experts past E read expert 0, slices past ks
+// re-read slice ks-1) and masked afterwards, so the loads of all slices and
+// experts are in flight together.
+template <int VPL>
+__device__ __forceinline__ void sum_slices(const float *row, size_t slice, int ks, int lane, int E, float (&h)[VPL]) {
+    constexpr int kMaxSlices = 10;
+    constexpr bool kAllAtOnce = VPL * kMaxSlices <= 60;
+    float part[kAllAtOnce ? VPL : 1][kMaxSlices];
+    if constexpr (kAllAtOnce) {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const int e = lane + 64 * v, ec = e < E ? e : 0;
+#pragma unroll
+            for (int s = 0; s < kMaxSlices; ++s) part[v][s] = row[(size_t)min(s, ks - 1) * slice + ec];
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        const int e = lane + 64 * v, ec = e < E ? e : 0;
+        float p[kMaxSlices];
+#pragma unroll
+        for (int s = 0; s < kMaxSlices; ++s)
+            p[s] = kAllAtOnce ? part[kAllAtOnce ? v : 0][s] : row[(size_t)min(s, ks - 1) * slice + ec];
+        float acc = p[0];
+#pragma unroll
+        for (int s = 1; s < kMaxSlices; ++s) acc += s < ks ? p[s] : 0.0f;
+        h[v] = acc;
+    }
 }
 
 // FLAGS: partial sums from the router GEMM, whose mid/lo slices are skipped
@@ -144,34 +178,8 @@ __global__ __launch_bounds__(256) void topk_kernel(
     }
 
     if constexpr (!FLAGS) {
-        // Logits: slices added in order 0..ks-1 (ks <= 10).  Every load is
-        // issued up front from a valid address (experts past E read expert 0,
-        // slices past ks re-read slice ks-1) and masked afterwards, so the
-        // loads of all slices and experts are in flight together.
-        constexpr int kMaxSlices = 10;
-        constexpr bool kAllAtOnce = VPL * kMaxSlices <= 60;
-        float part[kAllAtOnce ? VPL : 1][kMaxSlices];
-        if constexpr (kAllAtOnce) {
-#pragma unroll
-            for (int v = 0; v < VPL; ++v) {
-                const int e = lane + 64 * v, ec = e < E ? e : 0;
-#pragma unroll
-                for (int s = 0; s < kMaxSlices; ++s) part[v][s] = row[(size_t)min(s, ks - 1) * slice + ec];
-            }
-        }
         float h[VPL];
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-            const int e = lane + 64 * v, ec = e < E ? e : 0;
-            float p[kMaxSlices];
-#pragma unroll
-            for (int s = 0; s < kMaxSlices; ++s)
-                p[s] = kAllAtOnce ? part[kAllAtOnce ? v : 0][s] : row[(size_t)min(s, ks - 1) * slice + ec];
-            float acc = p[0];
-#pragma unroll
-            for (int s = 1; s < kMaxSlices; ++s) acc += s < ks ? p[s] : 0.0f;
-            h[v] = acc;
-        }
+        sum_slices<VPL>(row, slice, ks, lane, E, h);
         select_token<VPL>(h, bv, lane, t, E, k, renorm, logits_out, ids, tw, gap);
     } else {
         // hi-term slices (c = ks/3 <= 4) per token; the mid and lo slices (2c)
@@ -214,6 +222,33 @@ __global__ __launch_bounds__(256) void topk_kernel(
     }
 }
 
+// Top-k and dispatch in one launch for batches of at most kFusedRouteN tokens
+// (router_mfma partial sums, no split-term flags): wave t selects token t's
+// experts as topk_kernel does and keeps its ids in LDS; after a barrier the
+// first wave lays out the dispatch (dispatch_small).  One launch less in the
+// small-batch chain; the selections of a few tokens fit one CU.
+template <int VPL>
+__global__ __launch_bounds__(64 * kFusedRouteCap) void topk_dispatch_kernel(
+    const float *__restrict__ partial, int ks, const float *__restrict__ bias, float *__restrict__ logits_out,
+    int32_t *__restrict__ ids, float *__restrict__ tw, float *__restrict__ gap, int N, int E, int k, bool renorm,
+    int32_t *g_offsets, int32_t *g_exp_off, int32_t *tiles, int32_t *n_tiles, int32_t *por, int32_t *rop) {
+    __shared__ int32_t sids[kFusedRouteCap * 8];
+    const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+    if (t < N) {
+        float bv[VPL];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const int e = lane + 64 * v;
+            bv[v] = bias[e < E ? e : 0];
+        }
+        float h[VPL];
+        sum_slices<VPL>(partial + (size_t)t * E, (size_t)N * E, ks, lane, E, h);
+        select_token<VPL>(h, bv, lane, t, E, k, renorm, logits_out, ids, tw, gap, sids);
+    }
+    __syncthreads();
+    dispatch_small(sids, N, k, E, g_offsets, g_exp_off, tiles, n_tiles, por, rop);
+}
+
 hipError_t launch_topk(const Plan &p) {
     // one token per wave; small batches put each wave in a workgroup of its own,
     // so the selections spread over as many CUs (N = 32: 6.0 against 7.1 us
@@ -221,6 +256,20 @@ hipError_t launch_topk(const Plan &p) {
     const int wpb = p.N <= 64 ? 1 : 4;
     dim3 grid((p.N + wpb - 1) / wpb), block(64 * wpb);
     int vpl = (p.E + 63) / 64;
+    if (p.fused_route) {   // top-k and dispatch in one workgroup of N waves
+#define FGS_TOPKD(V)                                                                                          \
+    hipLaunchKernelGGL((topk_dispatch_kernel<V>), dim3(1), dim3(64 * p.N), 0, p.stream, p.partial, p.ks, p.rb,   \
+                       p.logits, p.ids, p.tw, p.gap, p.N, p.E, p.k, (p.flags & MOE_FLAG_RENORMALIZE) != 0,        \
+                       p.offsets, p.exp_off_out, p.tiles, p.n_tiles, p.por, p.rop)
+        if (vpl <= 1) FGS_TOPKD(1);
+        else if (vpl <= 2) FGS_TOPKD(2);
+        else if (vpl <= 4) FGS_TOPKD(4);
+        else if (vpl <= 6) FGS_TOPKD(6);
+        else if (vpl <= 8) FGS_TOPKD(8);
+        else FGS_TOPKD(16);
+#undef FGS_TOPKD
+        return hipGetLastError();
+    }
 #define FGS_TOPK2(V, F)                                                                             \
     hipLaunchKernelGGL((topk_kernel<V, F>), grid, block, 0, p.stream, p.partial, p.ks, p.rflags, p.rb, \
                        p.logits, p.ids, p.tw, p.gap, p.N, p.E, p.k, (p.flags & MOE_FLAG_RENORMALIZE) != 0)

@@ -201,6 +201,18 @@ def test_shape_limits(cfg_name, over):
     _run_full(get_config(cfg_name, **over))
 
 
+@pytest.mark.parametrize("cfg_name,over,kw", [
+    ("decode", dict(n_tokens=3), dict(renormalize=True)),
+    ("decode", dict(n_tokens=4, w_dtype="fp8"), {}),
+    ("fp8block", dict(n_tokens=2), dict(act_quant=True)),
+    ("toy", dict(n_tokens=4, n_experts=1024, top_k=8), {}),           # 16 experts per lane, the largest k
+    ("toy", dict(n_tokens=1, x_dtype="bf16"), dict(residual=True)),
+])
+def test_fused_route(cfg_name, over, kw):
+    """Batches of at most four tokens run top-k and dispatch as one kernel."""
+    _run_full(get_config(cfg_name, **over), **kw)
+
+
 _WIDE = dict(x_dtype="bf16")
 
 
@@ -216,8 +228,28 @@ _WIDE = dict(x_dtype="bf16")
 ])
 def test_wide_tile(cfg_name, over):
     """Large batches with bf16 activations run the 256-row gate/up tiles (bf16 or per-channel E4M3
-    weights) and take each entry as two 128-row items in the down product: odd widths, ragged and
+    weights) while the down product walks a 128-row list of its own: odd widths, ragged and
     multi-tile experts, short K."""
+    _run_full(get_config(cfg_name, **over))
+
+
+@pytest.mark.parametrize("cfg_name,over", [
+    ("toy", dict(n_tokens=300, d_model=256, d_ff=192, d_ff_shared=256)),             # one column block, f != f_s
+    ("toy", dict(n_tokens=600, n_experts=64, top_k=8, d_model=512, d_ff=256, d_ff_shared=192)),
+    ("toy", dict(n_tokens=600, n_experts=64, top_k=8, d_model=512, d_ff=256, d_ff_shared=192, w_dtype="fp8")),
+    ("toy", dict(n_tokens=6000, n_experts=32, top_k=4, d_model=1024, d_ff=192, d_ff_shared=320)),  # ~4 items per CU
+    ("toy", dict(n_tokens=3000, n_experts=32, top_k=4, d_model=768, d_ff=128, d_ff_shared=320, w_dtype="fp8")),
+    ("toy", dict(n_tokens=300)),                                        # K of one stage: the ring runs items ahead
+    ("toy", dict(n_tokens=300, w_dtype="fp8", x_dtype="bf16")),
+    ("toy", dict(_WIDE, n_tokens=8192, n_experts=8, top_k=2, d_model=256, d_ff=256, d_ff_shared=192)),  # wide gate/up
+    ("decode", dict(n_tokens=193)),                                    # ~13 items per CU, most of 1-8 rows
+    ("decode", dict(n_tokens=250, w_dtype="fp8")),
+])
+def test_persistent_down(cfg_name, over):
+    """bf16 or per-channel E4M3 weights with d a multiple of 256 run the persistent down product,
+    whose DMA ring crosses item boundaries: items of different K (shared expert), K shorter than
+    the ring, one or several column blocks, few and many items per workgroup, nearly empty row
+    tiles."""
     _run_full(get_config(cfg_name, **over))
 
 
@@ -250,7 +282,7 @@ def test_128_experts(n):
 
 @pytest.mark.parametrize("cfg_name,over,renorm", [
     ("toy", {}, False), ("toy", dict(x_dtype="bf16", n_tokens=300), False), ("decode", {}, False),
-    ("decode", dict(n_tokens=100, w_dtype="fp8"), True),
+    ("decode", dict(n_tokens=100, w_dtype="fp8"), True), ("decode", dict(n_tokens=3), False),
 ])
 def test_block_sandwich_norm(cfg_name, over, renorm):
     """moe_block_forward: pre-RMSNorm, the layer, post-RMSNorm + residual fused in the combine."""
@@ -270,7 +302,7 @@ def test_deterministic():
 
 
 @pytest.mark.parametrize("cfg_name,over,aq", [("decode", dict(n_tokens=32), False), ("toy", dict(n_tokens=300), False),
-                                             ("fp8block", dict(n_tokens=200), True)])
+                                             ("fp8block", dict(n_tokens=200), True), ("decode", dict(n_tokens=2), False)])
 def test_graph_replay_matches_eager(cfg_name, over, aq):
     """moe_forward captured in a HIP graph: every replay equals the eager result bit for bit,
     with eager work on the same buffers between replays."""
