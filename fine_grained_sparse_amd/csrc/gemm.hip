@@ -46,6 +46,8 @@
 //                 fetched straight into LDS (K up to 24 blocks of 128).
 // A 128 x 256 stage of 128 bytes per row moves 48 KB for 4.2 MFLOP (bf16) or
 // 8.4 MFLOP (FP8).
+#include <atomic>
+
 #include "moe_common.h"
 #include "moe_plan.h"
 
@@ -1406,6 +1408,245 @@ __global__ __launch_bounds__(kThreads) void down_gemm_kernel(
     }
 }
 
+// ---- persistent down product: bf16 H with bf16 weights (W8 false) or E4M3
+// weights with per-channel scales (W8 true), d a multiple of 256 (whole
+// column blocks).  The grid is one workgroup per CU; a workgroup
+// walks the work items of its launch index in the XCD-aware order (its index
+// modulo 8 fixes its XCD), and the DMA ring of tile_mma_dma (NB = 3 buffers
+// of 48 KB) or tile_mma_dma_w8 (NB = 4 of 32 KB) runs on across item
+// boundaries: the last NB stages of an item fetch the first NB of the next,
+// so an item never waits for a workgroup launch or for its first operands.
+// Stage s of the workgroup's sequence uses buffer s % NB, and at its barrier
+// stage s + NB is fetched into that buffer.  An item's last stage waits for
+// the next item's first stage, passes the barrier, finishes its MFMAs and
+// stores its outputs before it fetches stage s + NB; the stores are then
+// older than that fetch, and every later wait, which leaves only fetched
+// stages in flight, also covers them (with NB = 4 the first wait of the next
+// item also completes the stage fetched just before the stores).  Items
+// shorter than NB stages are fine: the fetch cursor then runs more than one
+// item ahead, and every wait counts only stages actually fetched.
+#ifndef FGS_DOWN_PERSIST
+#define FGS_DOWN_PERSIST 1
+#endif
+__device__ __forceinline__ int xcd_map(int slot, int B) {   // launch slot -> work item, as xcd_item
+    const int c = slot % kXcds, s = slot / kXcds;
+    return ((s / B) * kXcds + c) * B + s % B;
+}
+
+template <bool W8>
+__global__ __launch_bounds__(kThreads) void down_gemm_persist_kernel(
+    const uint16_t *__restrict__ H, int ldh, const uint8_t *__restrict__ wd, const float *__restrict__ sd,
+    const uint8_t *__restrict__ wsd, const float *__restrict__ ssd, const int32_t *__restrict__ tiles,
+    const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets, uint16_t *__restrict__ Y, int d, int E,
+    int f, int fs) {
+    static_assert(kAPer == 2 && kBPer == 4, "two activation DMAs per wave and stage");
+    constexpr int NB = W8 ? 4 : 3;                          // ring buffers = fetch distance in stages
+    constexpr int kStage = W8 ? kW8StageB : kDmaStageB;     // bytes per stage
+    constexpr int kBDma = W8 ? 2 : kBPer;                   // weight DMAs per wave and stage
+    constexpr int G = kAPer + kBDma;                        // DMAs per wave and stage
+    constexpr int kWs = W8 ? 1 : 2;                         // bytes per weight
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * kStage];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / kWN, wn = wave % kWN, fr = lane & 15, fg = lane >> 4;
+    const int gx = d / kBN, B = kXcdTiles * gx;
+    const int n_items = *n_tiles * gx;
+    const int G_wg = gridDim.x;
+
+    // fetch cursor: the item whose stages are fetched next, its next stage and buffer
+    int fq = 0, fkt = 0, fnk = 0, fbuf = 0;
+    bool fvalid = false;
+    // DMA sources: a wave-uniform base (H, the item's weight matrix) and this
+    // lane's 32-bit byte offset at K = 0 (H below 4 GiB: checked by the launcher)
+    uint32_t a_off[kAPer], b_off[kBDma];
+    const uint8_t *b_base = wd;
+    auto load_fetch_item = [&]() {
+        const int item = xcd_map(blockIdx.x + fq * G_wg, B);
+        fvalid = item < n_items;
+        if (!fvalid) return;
+        const int u = item / gx;
+        const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
+        const bool shared = g == E;
+        const int K = shared ? fs : f;
+        const int o0 = (item % gx) * kBN;
+        const int row0 = offsets[g] + m0, m = min(kBM, offsets[g + 1] - row0);
+        b_base = shared ? wsd : wd + (size_t)g * d * K * kWs;
+        fnk = K / kBK;
+#pragma unroll
+        for (int j = 0; j < kAPer; ++j) {
+            const int r = 8 * (wave * kAPer + j) + (lane >> 3);
+            a_off[j] = ((uint32_t)(row0 + (r < m ? r : 0)) * (uint32_t)ldh + (((lane & 7) ^ (r & 7)) << 3)) * 2u;
+        }
+#pragma unroll
+        for (int j = 0; j < kBDma; ++j) {
+            if constexpr (W8) {   // 16 rows of 64 code bytes per DMA, chunk (lane % 4) ^ ((r / 4) % 4)
+                const int r = 16 * (wave * 2 + j) + (lane >> 2);
+                b_off[j] = (uint32_t)(o0 + r) * (uint32_t)K + ((((lane & 3) ^ (r >> 2)) & 3) << 4);
+            } else {              // 8 rows of 128 bytes per DMA, chunk (lane % 8) ^ (r % 8)
+                const int r = 8 * (wave * kBPer + j) + (lane >> 3);
+                b_off[j] = ((uint32_t)(o0 + r) * (uint32_t)K + (((lane & 7) ^ (r & 7)) << 3)) * 2u;
+            }
+        }
+    };
+    int gf = 0;   // stages fetched so far
+    auto fetch_next = [&]() {
+        if (!fvalid) return;
+        uint8_t *buf = smem + fbuf * kStage;
+        const uint16_t *sa = H + fkt * kBK;
+        const uint8_t *sb = b_base + fkt * kBK * kWs;
+#pragma unroll
+        for (int j = 0; j < kAPer; ++j) dma16s(sa, a_off[j], buf + (wave * kAPer + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < kBDma; ++j) dma16s(sb, b_off[j], buf + kBM * kDmaRowB + (wave * kBDma + j) * 1024);
+        fbuf = fbuf == NB - 1 ? 0 : fbuf + 1;
+        ++gf;
+        if (++fkt == fnk) {
+            fkt = 0;
+            ++fq;
+            load_fetch_item();
+        }
+    };
+    // until at most `later` stages of this wave's DMAs are in flight
+    auto wait_stages = [&](int later) {
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(2 * G));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(G));
+        else __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
+    };
+    // this lane's fragment addresses in buffer 0 per 32-wide K half h: A row
+    // wm*64 + lane%16, B row wn*32 + lane%16, K chunk 4 h + lane/16 (the other
+    // rows of the wave differ by multiples of 16 rows: constant offsets)
+    const uint32_t s0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;
+    uint32_t la[2], lb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = 4 * h + fg;
+        la[h] = s0 + (wm * 64 + fr) * kDmaRowB + ((c ^ (fr & 7)) << 4);
+        if constexpr (W8)
+            lb[h] = s0 + kBM * kDmaRowB + (wn * 32 + fr) * kW8RowB + ((((c >> 1) ^ (fr >> 2)) & 3) << 4) + ((c & 1) << 3);
+        else
+            lb[h] = s0 + kBM * kDmaRowB + (wn * 32 + fr) * kDmaRowB + ((c ^ (fr & 7)) << 4);
+    }
+    constexpr int kBRowB = W8 ? kW8RowB : kDmaRowB;
+
+    load_fetch_item();
+    if (!fvalid) return;
+#pragma unroll
+    for (int i = 0; i < NB - 1; ++i) fetch_next();
+    wait_stages(gf - 1);   // stage 0 landed
+    lds_barrier();
+    fetch_next();
+    __builtin_amdgcn_sched_barrier(0);
+
+    int gs = 0;   // stage being computed
+    for (int q = 0;; ++q) {
+        const int item = xcd_map(blockIdx.x + q * G_wg, B);
+        if (item >= n_items) break;
+        const int u = item / gx;
+        const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
+        const bool shared = g == E;
+        const int nk = (shared ? fs : f) / kBK;
+        const int o0 = (item % gx) * kBN;
+        const int row0 = offsets[g] + m0, m = min(kBM, offsets[g + 1] - row0);
+
+        auto run = [&](auto live_c) {
+            constexpr int LV = decltype(live_c)::value;
+            constexpr int R = LV > 0 ? 4 + LV : 0;
+            f32x4_t acc[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            auto read_half = [&](uint32_t bo, int h, uint4 (&af)[4], uint4 (&bf)[4]) {
+                if constexpr (LV > 0) {
+                    const uint32_t pa = la[h] + bo, pb = lb[h] + bo;
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) {
+                        const uint32_t rb = (ni < 2 ? ni * 16 : kBN / 2 + (ni - 2) * 16) * kBRowB;
+                        if constexpr (W8) bf[ni] = e4m3x8_to_bf16x8(lds_read8(pb + rb));
+                        else bf[ni] = lds_read16(pb + rb);
+                    }
+#pragma unroll
+                    for (int mi = 0; mi < LV; ++mi) af[mi] = lds_read16(pa + mi * 16 * kDmaRowB);
+                }
+            };
+            auto mma_half = [&](const uint4 (&af)[4], const uint4 (&bf)[4]) {
+#pragma unroll
+                for (int mi = 0; mi < LV; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_bf16(bf[ni], af[mi], acc[mi][ni]);
+            };
+            // this wave's DMAs of stage gs + 1 landed; the later fetched stages stay in flight
+            auto wait_next = [&]() { wait_stages(gf - gs - 2); };
+            uint4 fa0[4], fb0[4], fa1[4], fb1[4];
+            int cb = gs % NB;
+            read_half(cb * kStage, 0, fa0, fb0);
+            // every stage but the item's last: stage gs + NB goes into buffer cb
+#pragma nounroll
+            for (int kt = 0; kt + 1 < nk; ++kt) {
+                const int nb = cb == NB - 1 ? 0 : cb + 1;
+                __builtin_amdgcn_sched_barrier(0);
+                read_half(cb * kStage, 1, fa1, fb1);
+                mma_half(fa0, fb0);
+                interleave_mfma_reads<R, 4 * LV>();
+                __builtin_amdgcn_sched_barrier(0);
+                wait_next();
+                lds_barrier();
+                fetch_next();
+                __builtin_amdgcn_sched_barrier(0);
+                read_half(nb * kStage, 0, fa0, fb0);
+                mma_half(fa1, fb1);
+                interleave_mfma_reads<R, 4 * LV>();
+                __builtin_amdgcn_sched_barrier(0);
+                ++gs;
+                cb = nb;
+            }
+            // the last stage: wait for the next item's first stage (if any), finish,
+            // store, then fetch stage gs + NB
+            __builtin_amdgcn_sched_barrier(0);
+            read_half(cb * kStage, 1, fa1, fb1);
+            mma_half(fa0, fb0);
+            __builtin_amdgcn_sched_barrier(0);
+            const bool more = gf > gs + 1;
+            if (more) {
+                wait_next();
+                lds_barrier();
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mma_half(fa1, fb1);
+            __builtin_amdgcn_sched_barrier(0);
+            uint16_t *yb = Y + (size_t)row0 * d + o0;
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                const int o = b_row_of(wn, ni) + (lane >> 4) * 4;
+                float sc[4] = {1.f, 1.f, 1.f, 1.f};
+                if constexpr (W8) {
+                    const float *sp = shared ? ssd + o0 + o : sd + (size_t)g * d + o0 + o;
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) sc[qq] = sp[qq];
+                }
+#pragma unroll
+                for (int mi = 0; mi < LV; ++mi) {
+                    const int r = wm * 64 + mi * 16 + (lane & 15);
+                    if (r < m)
+                        *reinterpret_cast<uint2 *>(yb + (uint32_t)(r * d + o)) =
+                            make_uint2(pack_bf16x2(acc[mi][ni][0] * sc[0], acc[mi][ni][1] * sc[1]),
+                                       pack_bf16x2(acc[mi][ni][2] * sc[2], acc[mi][ni][3] * sc[3]));
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) fetch_next();
+            ++gs;
+        };
+        const int live = min(4, max(0, (m - wm * 64 + 15) / 16));
+        switch (live) {
+            case 4: run(Live<4>{}); break;
+            case 3: run(Live<3>{}); break;
+            case 2: run(Live<2>{}); break;
+            case 1: run(Live<1>{}); break;
+            default: run(Live<0>{}); break;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- FP8 x FP8
 // 1 x 128 activation quantisation ("Inside Kolibri 1", section "The FP8 path
 // is explicitly mixed precision"): A holds E4M3 codes of activations with one
@@ -2135,6 +2376,25 @@ hipError_t launch_gate_up_gemm(const Plan &p) {
     return hipGetLastError();
 }
 
+// compute units of the current device, rounded down to whole XCD groups (cached per device)
+static hipError_t cu_count(int *out) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        v = v / kXcds * kXcds;
+        if (v < kXcds) v = kXcds;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    *out = v;
+    return hipSuccess;
+}
+
 hipError_t launch_down_gemm(const Plan &p) {
     const int gx = (p.d + kBN - 1) / kBN;
     dim3 grid(gx, p.max_tiles + kXcds * kXcdTiles), block(kThreads);
@@ -2157,6 +2417,28 @@ hipError_t launch_down_gemm(const Plan &p) {
 #undef FGS_DNF
         return hipGetLastError();
     }
+#if FGS_DOWN_PERSIST
+    // the persistent kernel: bf16 or per-channel E4M3 weights, whole 256-column
+    // blocks, 32-bit offsets into H and into one expert's matrix
+    const long h_bytes = ((long)p.N * p.k + p.N) * p.ldh * 2;
+    const bool w8 = p.wdt == MOE_DTYPE_FP8_E4M3 && !(p.flags & MOE_FLAG_FP8_BLOCK128);
+    if ((p.wdt == MOE_DTYPE_BF16 || w8) && p.d % kBN == 0 && p.f % kBK == 0 && p.fs % kBK == 0 &&
+        h_bytes < (1L << 32) &&
+        (long)p.d * (p.f > p.fs ? p.f : p.fs) * 2 < (1L << 32)) {
+        int cus = 0;
+        hipError_t e = cu_count(&cus);
+        if (e != hipSuccess) return e;
+        if (w8)
+            hipLaunchKernelGGL(down_gemm_persist_kernel<true>, dim3(cus), block, 0, p.stream, p.H, p.ldh,
+                               (const uint8_t *)p.W.w_down, p.W.s_down, (const uint8_t *)p.W.ws_down, p.W.ss_down,
+                               tiles, n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs);
+        else
+            hipLaunchKernelGGL(down_gemm_persist_kernel<false>, dim3(cus), block, 0, p.stream, p.H, p.ldh,
+                               (const uint8_t *)p.W.w_down, p.W.s_down, (const uint8_t *)p.W.ws_down, p.W.ss_down,
+                               tiles, n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs);
+        return hipGetLastError();
+    }
+#endif
 #define FGS_DNG(WM)                                                                                       \
     hipLaunchKernelGGL((down_gemm_kernel<WM>), grid, block,                                                       \
                        (WM == kWBf16 || WM == kWFp8Row || WM == kWFp8BlkDma) ? 0 : kGemmLds, p.stream, p.H,             \
