@@ -77,6 +77,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--vendor-reference", action="store_true",
+                    help="only time the vendor BLAS (torch.bmm, bf16) on uniform batched GEMMs shaped like the "
+                         "expert GEMMs (a reference for the grouped GEMMs, not part of the layer)")
     return ap.parse_args()
 
 
@@ -108,16 +111,63 @@ class Hip:
 
 
 def copy_probe():
+    """Three plain 1 GiB device copies (torch's copy kernel): the counter calibration run, and a
+    reference for the HBM rate a plain streaming kernel reaches (bytes read + written per second)."""
     import torch
     nbytes = 1 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     src.fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    for _ in range(3):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    for i in range(3):
         dst.copy_(src)
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_probe_bytes": nbytes, "launches": 3}), flush=True)
+    us = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(3)]
+    best = min(us)
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": 3, "us": [round(u, 1) for u in us],
+                      "best_read_plus_write_GBps": round(2 * nbytes / best / 1e3, 1)}), flush=True)
+
+
+def vendor_reference():
+    """torch.bmm (rocBLAS / hipBLASLt) in bf16 on uniform batched GEMMs with the expert GEMMs' shapes:
+    384 experts x 128 rows (the prefill chunk's average rows per expert) for gate/up (2560 -> 1024) and
+    down (512 -> 2560), the same with 7 experts x 14043 rows (the all-hot probe: every token on six
+    experts plus the shared one), and one 8192^3 product.  Operands are contiguous."""
+    import torch
+    res = {}
+
+    def timed(name, A, B, reps):
+        for _ in range(3):
+            C = torch.bmm(A, B)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            C = torch.bmm(A, B)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / reps
+        b, m, kk = A.shape
+        n = B.shape[2]
+        flops = 2.0 * b * m * n * kk
+        res[name] = {"us": round(dt * 1e6, 1), "tflops": round(flops / dt / 1e12, 1),
+                     "mfma_frac_bf16": round(flops / dt / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+                     "weight_tbps": round(B.numel() * 2 / dt / 1e12, 2)}
+        log(f"vendor reference {name}: {res[name]}")
+        del C
+
+    g = torch.Generator(device="cuda").manual_seed(5)
+    for name, b, m, kk, n in (("prefill_gate_up", 384, 128, 2560, 1024), ("prefill_down", 384, 128, 512, 2560),
+                              ("hot_gate_up", 7, 14043, 2560, 1024), ("hot_down", 7, 14043, 512, 2560)):
+        A = torch.randn(b, m, kk, device="cuda", generator=g).to(torch.bfloat16)
+        B = (torch.randn(b, kk, n, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        timed(name, A, B, 20)
+        del A, B
+        torch.cuda.empty_cache()
+    A = torch.randn(1, 8192, 8192, device="cuda", generator=g).to(torch.bfloat16)
+    timed("square_8192", A, A.clone(), 10)
+    print(json.dumps({"vendor_reference": res, "what": vendor_reference.__doc__.split(".")[0]}), flush=True)
 
 
 # source files that define each expert kernel (with the device helpers it uses)
@@ -410,6 +460,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.vendor_reference:
+        vendor_reference()
         return
 
     from moe_inputs import get_config
