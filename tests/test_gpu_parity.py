@@ -195,6 +195,8 @@ def test_block_act_quant():
     ("toy", dict(n_tokens=300, n_experts=202, top_k=7, x_dtype="bf16")),  # router GEMM: one ragged expert tile, E % 4 != 0
     ("toy", dict(n_tokens=24, d_model=640, x_dtype="bf16")),            # small-batch router: two waves per k-slice
     ("toy", dict(n_tokens=24, d_model=1280, x_dtype="bf16")),           # small-batch router: four waves per k-slice
+    ("toy", dict(n_tokens=16640)),                                      # 65 dispatch blocks: separate scan launch
+    ("toy", dict(n_tokens=20000, x_dtype="bf16", d_model=128, d_ff=64, d_ff_shared=64)),  # the same with wide tiles
 ])
 def test_shape_limits(cfg_name, over):
     """Edges of the supported shapes and of the stream/GEMM path choice."""
