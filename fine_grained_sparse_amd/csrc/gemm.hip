@@ -46,6 +46,13 @@
 //                 fetched straight into LDS (K up to 24 blocks of 128).
 // A 128 x 256 stage of 128 bytes per row moves 48 KB for 4.2 MFLOP (bf16) or
 // 8.4 MFLOP (FP8).
+//
+// From 8192 tokens with bf16 activations the gate/up product takes 256 x 256
+// tiles of 16 waves (gate_up_gemm_wide_kernel).  The down product (K = f, only
+// eight 64-wide stages per item) with bf16 or per-channel E4M3 weights runs
+// persistent kernels whose DMA rings cross item boundaries:
+// down_gemm_persist_kernel on 128 x 256 items and, with the wide gate/up
+// tiles, down_gemm_wide_persist_kernel on 256 x 256 items.
 #include <atomic>
 
 #include "moe_common.h"
@@ -1428,6 +1435,32 @@ __global__ __launch_bounds__(kThreads) void down_gemm_kernel(
 #ifndef FGS_DOWN_PERSIST
 #define FGS_DOWN_PERSIST 1
 #endif
+#ifndef FGS_DOWN_WIDE
+#define FGS_DOWN_WIDE 1
+#endif
+// Epilogue helpers of the persistent down kernels.  Inside their item loop a
+// vector, flat or spilled memory access would make the compiler wait for
+// every direct-to-LDS fetch in flight (its wait counts cannot see the
+// fetches).  So the per-channel scales of an item are fetched into LDS with
+// its first weight stage (one more DMA of wave 0, ahead of the stage's own)
+// and read from there, and the output goes through a global (not flat)
+// store whose address is a scalar base plus one lane offset.
+typedef __attribute__((address_space(1))) uint8_t gbyte_t;
+// four values of a lane, scaled and rounded to bf16, to blk (wave-uniform) + lane_off bytes
+__device__ __forceinline__ void store_bf16x4(const uint16_t *blk, uint32_t lane_off, const f32x4_t &v,
+                                             const float (&sc)[4]) {
+    gbyte_t *b = (gbyte_t *)uniform_ptr(blk);
+    *reinterpret_cast<__attribute__((address_space(1))) u32x2v_t *>(b + lane_off) =
+        u32x2v_t{pack_bf16x2(v[0] * sc[0], v[1] * sc[1]), pack_bf16x2(v[2] * sc[2], v[3] * sc[3])};
+}
+// the 4 scales of a lane's columns 4 (lane/16) .. +3 of the 16-wide column fragment at
+// column c of the item, from the item's scale slot in LDS (256 floats)
+__device__ __forceinline__ void slot_scales(uint32_t slot, int c, int lane, float (&sc)[4]) {
+    const uint4 v = lds_read16(slot + (uint32_t)(c + (lane >> 4) * 4) * 4u);
+    sc[0] = __uint_as_float(v.x); sc[1] = __uint_as_float(v.y);
+    sc[2] = __uint_as_float(v.z); sc[3] = __uint_as_float(v.w);
+}
+
 __device__ __forceinline__ int xcd_map(int slot, int B) {   // launch slot -> work item, as xcd_item
     const int c = slot % kXcds, s = slot / kXcds;
     return ((s / B) * kXcds + c) * B + s % B;
@@ -1445,7 +1478,9 @@ __global__ __launch_bounds__(kThreads) void down_gemm_persist_kernel(
     constexpr int kBDma = W8 ? 2 : kBPer;                   // weight DMAs per wave and stage
     constexpr int G = kAPer + kBDma;                        // DMAs per wave and stage
     constexpr int kWs = W8 ? 1 : 2;                         // bytes per weight
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * kStage];
+    // E4M3: 8 slots of 256 column scales after the ring (the cursor runs at most NB items ahead)
+    constexpr int kSlots = W8 ? 8 : 0;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * kStage + kSlots * 1024];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / kWN, wn = wave % kWN, fr = lane & 15, fg = lane >> 4;
     const int gx = d / kBN, B = kXcdTiles * gx;
@@ -1459,6 +1494,7 @@ __global__ __launch_bounds__(kThreads) void down_gemm_persist_kernel(
     // lane's 32-bit byte offset at K = 0 (H below 4 GiB: checked by the launcher)
     uint32_t a_off[kAPer], b_off[kBDma];
     const uint8_t *b_base = wd;
+    const float *s_base = sd;   // the fetch item's 256 column scales (E4M3)
     auto load_fetch_item = [&]() {
         const int item = xcd_map(blockIdx.x + fq * G_wg, B);
         fvalid = item < n_items;
@@ -1470,6 +1506,7 @@ __global__ __launch_bounds__(kThreads) void down_gemm_persist_kernel(
         const int o0 = (item % gx) * kBN;
         const int row0 = offsets[g] + m0, m = min(kBM, offsets[g + 1] - row0);
         b_base = shared ? wsd : wd + (size_t)g * d * K * kWs;
+        if constexpr (W8) s_base = shared ? ssd + o0 : sd + (size_t)g * d + o0;
         fnk = K / kBK;
 #pragma unroll
         for (int j = 0; j < kAPer; ++j) {
@@ -1491,6 +1528,8 @@ __global__ __launch_bounds__(kThreads) void down_gemm_persist_kernel(
     auto fetch_next = [&]() {
         if (!fvalid) return;
         uint8_t *buf = smem + fbuf * kStage;
+        if constexpr (W8)
+            if (fkt == 0 && wave == 0) dma16s(s_base, lane * 16, smem + NB * kStage + (fq & (kSlots - 1)) * 1024);
         const uint16_t *sa = H + fkt * kBK;
         const uint8_t *sb = b_base + fkt * kBK * kWs;
 #pragma unroll
@@ -1613,28 +1652,298 @@ __global__ __launch_bounds__(kThreads) void down_gemm_persist_kernel(
             __builtin_amdgcn_sched_barrier(0);
             mma_half(fa1, fb1);
             __builtin_amdgcn_sched_barrier(0);
-            uint16_t *yb = Y + (size_t)row0 * d + o0;
+            // lane: row wm*64 + mi*16 + lane%16, columns o0 + b_row_of(wn, ni) + 4 (lane/16) .. +3
+            const uint32_t lane_off = ((uint32_t)(lane & 15) * (uint32_t)d + (uint32_t)(lane >> 4) * 4u) * 2u;
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni) {
-                const int o = b_row_of(wn, ni) + (lane >> 4) * 4;
+                const int c0 = o0 + b_row_of(wn, ni);
                 float sc[4] = {1.f, 1.f, 1.f, 1.f};
-                if constexpr (W8) {
-                    const float *sp = shared ? ssd + o0 + o : sd + (size_t)g * d + o0 + o;
-#pragma unroll
-                    for (int qq = 0; qq < 4; ++qq) sc[qq] = sp[qq];
-                }
+                if constexpr (W8) slot_scales(s0 + NB * kStage + (q & (kSlots - 1)) * 1024, b_row_of(wn, ni), lane, sc);
 #pragma unroll
                 for (int mi = 0; mi < LV; ++mi) {
-                    const int r = wm * 64 + mi * 16 + (lane & 15);
-                    if (r < m)
-                        *reinterpret_cast<uint2 *>(yb + (uint32_t)(r * d + o)) =
-                            make_uint2(pack_bf16x2(acc[mi][ni][0] * sc[0], acc[mi][ni][1] * sc[1]),
-                                       pack_bf16x2(acc[mi][ni][2] * sc[2], acc[mi][ni][3] * sc[3]));
+                    const int rb = wm * 64 + mi * 16;
+                    if (rb + (lane & 15) < m) store_bf16x4(Y + (size_t)(row0 + rb) * d + c0, lane_off, acc[mi][ni], sc);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
             if (more) fetch_next();
             ++gs;
+        };
+        const int live = min(4, max(0, (m - wm * 64 + 15) / 16));
+        switch (live) {
+            case 4: run(Live<4>{}); break;
+            case 3: run(Live<3>{}); break;
+            case 2: run(Live<2>{}); break;
+            case 1: run(Live<1>{}); break;
+            default: run(Live<0>{}); break;
+        }
+    }
+}
+
+// ---- persistent wide down product: 256 x 256 items (the wide gate/up's
+// 256-row tile list), 16 waves of 64 x 64, bf16 H with bf16 weights (W8
+// false) or E4M3 weights with per-channel scales (W8 true), d a multiple of
+// 256.  One workgroup per CU walks its XCD's items as down_gemm_persist_kernel
+// does, with the wide tile's two rings: NA activation buffers and NB weight
+// buffers of one stage each (bf16: 2 and 3 of 32 KB; E4M3: 3 of 32 KB and 3
+// of 16 KB).  At the barrier that ends stage s the activations of stage s + NA
+// and the weights of stage s + NB are fetched into the buffers stage s used,
+// by two cursors that cross item boundaries on their own.  The wave waits
+// before that barrier leave only the newest fetch group in flight; an item's
+// stores are issued after the barrier of its last stage and before that
+// stage's fetches, so the next wait covers them and no prefetch is waited
+// for early.  A quarter fewer operand bytes per flop than the 128 x 256 item
+// and one weight slice per expert and column block where an expert has at
+// most 256 rows.
+template <bool W8>
+__global__ __launch_bounds__(1024) void down_gemm_wide_persist_kernel(
+    const uint16_t *__restrict__ H, int ldh, const uint8_t *__restrict__ wd, const float *__restrict__ sd,
+    const uint8_t *__restrict__ wsd, const float *__restrict__ ssd, const int32_t *__restrict__ tiles,
+    const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets, uint16_t *__restrict__ Y, int d, int E,
+    int f, int fs) {
+    using WG = Wide<4>;
+    static_assert(WG::kWaves == 16 && WG::kDma == 2, "16 waves, two 1 KB DMAs per wave and operand stage");
+    constexpr int kAPerW = WG::kDma;               // 256 rows x 128 bytes = 32 DMAs of 1 KB
+    constexpr int kBPerW = W8 ? 1 : WG::kDma;      // 256 rows x 128 (bf16) or 64 (E4M3) bytes
+    constexpr int kWs = W8 ? 1 : 2;                // bytes per weight
+    constexpr int kBRowB = W8 ? kW8RowB : kDmaRowB;
+    constexpr int NA = W8 ? 3 : 2, NB = 3;
+    constexpr int kABuf = kWideBufB, kBBuf = W8 ? kWideW8BufB : kWideBufB;
+    constexpr int kBOff = 0, kAOff = NB * kBBuf;   // weight ring first, then the activation ring
+    // E4M3: 4 slots of 256 column scales after the rings (the weight cursor runs at most NB items ahead)
+    constexpr int kSOff = kAOff + NA * kABuf, kSlotB = W8 ? 4 * 1024 : 0;
+    static_assert(NB * kBBuf + NA * kABuf + kSlotB <= 160 * 1024, "the rings must fit one CU's LDS");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * kBBuf + NA * kABuf + kSlotB];
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = w / kWN, wn = w % kWN, fr = lane & 15, fg = lane >> 4;
+    const int gx = d / kBN, B = kXcdTiles * gx;
+    const int n_items = *n_tiles * gx;
+    const int G_wg = gridDim.x;
+
+    // activation cursor: next stage to fetch (item slot qa, stage kta of nka)
+    int qa = 0, kta = 0, nka = 0, fab = 0, gfa = 0;
+    bool va = false;
+    uint32_t a_off[kAPerW];
+    // rows past the group end read row 0 of the tile (never stored)
+    auto set_a_off = [&](int row0, int m) {
+#pragma unroll
+        for (int j = 0; j < kAPerW; ++j) {
+            const int r = 8 * (w * kAPerW + j) + (lane >> 3);
+            a_off[j] = ((uint32_t)(row0 + (r < m ? r : 0)) * (uint32_t)ldh + (((lane & 7) ^ (r & 7)) << 3)) * 2u;
+        }
+    };
+    auto load_a = [&]() {
+        const int item = xcd_map(blockIdx.x + qa * G_wg, B);
+        va = item < n_items;
+        if (!va) return;
+        const int u = item / gx;
+        const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
+        nka = (g == E ? fs : f) / kBK;
+        const int row0 = offsets[g] + m0;
+        set_a_off(row0, min(kBMW, offsets[g + 1] - row0));
+    };
+    // A DMAs of the stage `kt` into ring buffer `buf`
+    auto dma_a = [&](int kt, int buf) {
+        const uint16_t *sa = H + kt * kBK;
+#pragma unroll
+        for (int j = 0; j < kAPerW; ++j) dma16s(sa, a_off[j], smem + kAOff + buf * kABuf + (w * kAPerW + j) * 1024);
+    };
+    auto fetch_a = [&]() {   // bf16 only
+        if (!va) return;
+        dma_a(kta, fab);
+        fab = fab == NA - 1 ? 0 : fab + 1;
+        ++gfa;
+        if (++kta == nka) { kta = 0; ++qa; load_a(); }
+    };
+    // weight cursor
+    int qb = 0, ktb = 0, nkb = 0, fbb = 0, gfb = 0;
+    bool vb = false;
+    uint32_t b_off[kBPerW];
+    const uint8_t *b_base = wd;
+    const float *s_base = sd;   // the weight cursor item's 256 column scales (E4M3)
+    auto load_b = [&]() {
+        const int item = xcd_map(blockIdx.x + qb * G_wg, B);
+        vb = item < n_items;
+        if (!vb) return;
+        const int u = item / gx;
+        const int g = tiles[2 * u];
+        const bool shared = g == E;
+        const int K = shared ? fs : f;
+        nkb = K / kBK;
+        const int o0 = (item % gx) * kBN;
+        b_base = shared ? wsd : wd + (size_t)g * d * K * kWs;
+        if constexpr (W8) {   // this cursor fetches the activations too
+            const int row0 = offsets[g] + tiles[2 * u + 1];
+            set_a_off(row0, min(kBMW, offsets[g + 1] - row0));
+        }
+        if constexpr (W8) s_base = shared ? ssd + o0 : sd + (size_t)g * d + o0;
+#pragma unroll
+        for (int j = 0; j < kBPerW; ++j) {
+            if constexpr (W8) {   // 16 rows of 64 code bytes per DMA, chunk (lane % 4) ^ ((r / 4) % 4)
+                const int r = 16 * w + (lane >> 2);
+                b_off[j] = (uint32_t)(o0 + r) * (uint32_t)K + ((((lane & 3) ^ (r >> 2)) & 3) << 4);
+            } else {              // 8 rows of 128 bytes per DMA, chunk (lane % 8) ^ (r % 8)
+                const int r = 8 * (w * kBPerW + j) + (lane >> 3);
+                b_off[j] = ((uint32_t)(o0 + r) * (uint32_t)K + (((lane & 7) ^ (r & 7)) << 3)) * 2u;
+            }
+        }
+    };
+    auto fetch_b = [&]() {
+        if (!vb) return;
+        const uint8_t *sb = b_base + ktb * kBK * kWs;
+        if constexpr (W8) dma_a(ktb, fbb);
+#pragma unroll
+        for (int j = 0; j < kBPerW; ++j) dma16s(sb, b_off[j], smem + kBOff + fbb * kBBuf + (w * kBPerW + j) * 1024);
+        fbb = fbb == NB - 1 ? 0 : fbb + 1;
+        ++gfb;
+        if (++ktb == nkb) { ktb = 0; ++qb; load_b(); }
+    };
+    // one fetch group: an item's column scales when the weight cursor starts it
+    // (first, so a wait that leaves the group's operand DMAs in flight covers it),
+    // then the activation and the weight stage
+    auto fetch_group = [&](bool a) {
+        if constexpr (W8)
+            if (vb && ktb == 0 && w == 0) dma16s(s_base, lane * 16, smem + kSOff + (qb & 3) * 1024);
+        if (!W8 && a) fetch_a();
+        fetch_b();
+    };
+    // fetched stages (both operands): the activation cursor trails with bf16
+    auto fetched = [&]() { return W8 ? gfb : gfa; };
+
+    // this lane's fragment addresses in buffer 0 per 32-wide K half h: activation
+    // row wm*64 + lane%16, weight row wn*32 + lane%16, K chunk 4 h + lane/16
+    const uint32_t s0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;
+    uint32_t la[2], lb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = 4 * h + fg;
+        la[h] = s0 + kAOff + (wm * 64 + fr) * kDmaRowB + ((c ^ (fr & 7)) << 4);
+        if constexpr (W8)
+            lb[h] = s0 + kBOff + (wn * 32 + fr) * kW8RowB + ((((c >> 1) ^ (fr >> 2)) & 3) << 4) + ((c & 1) << 3);
+        else
+            lb[h] = s0 + kBOff + (wn * 32 + fr) * kDmaRowB + ((c ^ (fr & 7)) << 4);
+    }
+
+    if constexpr (!W8) load_a();
+    load_b();
+    if (!vb) return;
+    // prologue, in the steady state's issue order: activations of stages 0 .. NA-1,
+    // weights of stages 0 .. NB-1; all of it lands before the first stage
+#pragma unroll
+    for (int i = 0; i < NB; ++i) fetch_group(i < NA);
+    __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    int gs = 0;   // stage being computed
+    for (int q = 0;; ++q) {
+        const int item = xcd_map(blockIdx.x + q * G_wg, B);
+        if (item >= n_items) break;
+        const int u = item / gx;
+        const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
+        const bool shared = g == E;
+        const int nk = (shared ? fs : f) / kBK;
+        const int o0 = (item % gx) * kBN;
+        const int row0 = offsets[g] + m0, m = min(kBMW, offsets[g + 1] - row0);
+
+        auto run = [&](auto live_c) {
+            constexpr int LV = decltype(live_c)::value;
+            f32x4_t acc[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            int ca = gs % NA, cbw = gs % NB;
+            // the products of one stage from activation buffer ca and weight buffer cbw
+            auto compute = [&]() {
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (LV > 0) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t pa = la[h] + ca * kABuf, pb = lb[h] + cbw * kBBuf;
+                        uint4 bf[4];
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni) {
+                            const uint32_t rb = (ni < 2 ? ni * 16 : kBN / 2 + (ni - 2) * 16) * kBRowB;
+                            if constexpr (W8) bf[ni] = e4m3x8_to_bf16x8(lds_read8(pb + rb));
+                            else bf[ni] = lds_read16(pb + rb);
+                        }
+                        if constexpr (W8) {   // one activation fragment at a time: 128 registers a wave
+#pragma unroll
+                            for (int mi = 0; mi < LV; ++mi) {
+                                const uint4 a = lds_read16(pa + mi * 16 * kDmaRowB);
+#pragma unroll
+                                for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_bf16(bf[ni], a, acc[mi][ni]);
+                            }
+                        } else {              // the next fragment requested before this one's MFMAs
+                            uint4 a = lds_read16(pa);
+#pragma unroll
+                            for (int mi = 0; mi < LV; ++mi) {
+                                const uint4 an = mi + 1 < LV ? lds_read16(pa + (mi + 1) * 16 * kDmaRowB) : a;
+#pragma unroll
+                                for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_bf16(bf[ni], a, acc[mi][ni]);
+                                a = an;
+                            }
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            // this wave's DMAs of stage gs + 1 landed; only the newest fetch group
+            // (weights of gs + 2 with bf16, both operands of gs + 2 with E4M3) may remain
+            auto wait_next = [&]() {
+                if constexpr (W8) {
+                    if (gfb >= gs + 3) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(kAPerW + kBPerW));
+                    else __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
+                } else {
+                    if (gfb >= gs + 3) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(kBPerW));
+                    else __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
+                }
+            };
+            auto advance = [&]() {
+                ++gs;
+                ca = ca == NA - 1 ? 0 : ca + 1;
+                cbw = cbw == NB - 1 ? 0 : cbw + 1;
+            };
+            // every stage but the item's last (stage gs + 1 is this item's)
+#pragma nounroll
+            for (int kt = 0; kt + 1 < nk; ++kt) {
+                compute();
+                wait_next();
+                lds_barrier();
+                fetch_group(true);   // activations of stage gs + NA into buffer ca, weights of gs + NB into cbw
+                __builtin_amdgcn_sched_barrier(0);
+                advance();
+            }
+            // the last stage: products, then (if a later stage exists) its wait and
+            // barrier, the stores, and only then the fetches of this barrier
+            compute();
+            const bool more = fetched() > gs + 1;
+            if (more) {
+                wait_next();
+                lds_barrier();
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // lane: row wm*64 + mi*16 + lane%16, columns o0 + b_row_of(wn, ni) + 4 (lane/16) .. +3
+            // (the lane index recomputed here rather than kept live through the K loop)
+            const int ln = (int)__lane_id();
+            const uint32_t lane_off = ((uint32_t)(ln & 15) * (uint32_t)d + (uint32_t)(ln >> 4) * 4u) * 2u;
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                const int c0 = o0 + b_row_of(wn, ni);
+                float sc[4] = {1.f, 1.f, 1.f, 1.f};
+                if constexpr (W8) slot_scales(s0 + kSOff + (q & 3) * 1024, b_row_of(wn, ni), ln, sc);
+#pragma unroll
+                for (int mi = 0; mi < LV; ++mi) {
+                    const int rb = wm * 64 + mi * 16;
+                    if (rb + (ln & 15) < m) store_bf16x4(Y + (size_t)(row0 + rb) * d + c0, lane_off, acc[mi][ni], sc);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) fetch_group(true);
+            __builtin_amdgcn_sched_barrier(0);
+            advance();
         };
         const int live = min(4, max(0, (m - wm * 64 + 15) / 16));
         switch (live) {
@@ -2428,6 +2737,23 @@ hipError_t launch_down_gemm(const Plan &p) {
         int cus = 0;
         hipError_t e = cu_count(&cus);
         if (e != hipSuccess) return e;
+#if FGS_DOWN_WIDE
+        // 256 x 256 items (the gate/up's 256-row tile list) where the routed experts
+        // average at least 256 rows; one MI355X, d = 2560, E = 384, top-6: all-hot
+        // probe down 433 -> 403 us, Zipf 458 -> 443, but prefill (about 150 rows per
+        // expert) 315 -> 319, so it keeps the 128-row items
+        if (p.bm == kGemmBMWide && (long)p.N * p.k >= 256L * p.E) {
+            if (w8)
+                hipLaunchKernelGGL(down_gemm_wide_persist_kernel<true>, dim3(cus), dim3(1024), 0, p.stream, p.H,
+                                   p.ldh, (const uint8_t *)p.W.w_down, p.W.s_down, (const uint8_t *)p.W.ws_down,
+                                   p.W.ss_down, p.tiles, p.n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs);
+            else
+                hipLaunchKernelGGL(down_gemm_wide_persist_kernel<false>, dim3(cus), dim3(1024), 0, p.stream, p.H,
+                                   p.ldh, (const uint8_t *)p.W.w_down, p.W.s_down, (const uint8_t *)p.W.ws_down,
+                                   p.W.ss_down, p.tiles, p.n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs);
+            return hipGetLastError();
+        }
+#endif
         if (w8)
             hipLaunchKernelGGL(down_gemm_persist_kernel<true>, dim3(cus), block, 0, p.stream, p.H, p.ldh,
                                (const uint8_t *)p.W.w_down, p.W.s_down, (const uint8_t *)p.W.ws_down, p.W.ss_down,

@@ -243,15 +243,21 @@ def test_wide_tile(cfg_name, over):
     ("toy", dict(n_tokens=3000, n_experts=32, top_k=4, d_model=768, d_ff=128, d_ff_shared=320, w_dtype="fp8")),
     ("toy", dict(n_tokens=300)),                                        # K of one stage: the ring runs items ahead
     ("toy", dict(n_tokens=300, w_dtype="fp8", x_dtype="bf16")),
-    ("toy", dict(_WIDE, n_tokens=8192, n_experts=8, top_k=2, d_model=256, d_ff=256, d_ff_shared=192)),  # wide gate/up
     ("decode", dict(n_tokens=193)),                                    # ~13 items per CU, most of 1-8 rows
     ("decode", dict(n_tokens=250, w_dtype="fp8")),
+    # from 8192 tokens with bf16 activations: 256 x 256 items (16 waves)
+    ("toy", dict(_WIDE, n_tokens=8192, n_experts=8, top_k=2, d_model=256, d_ff=256, d_ff_shared=192)),
+    ("toy", dict(_WIDE, n_tokens=8192, n_experts=8, top_k=2, d_model=256, d_ff=256, d_ff_shared=192, w_dtype="fp8")),
+    ("toy", dict(_WIDE, n_tokens=8300, n_experts=24, top_k=3, d_model=512, d_ff=64, d_ff_shared=128)),   # K of 1-2 stages
+    ("toy", dict(_WIDE, n_tokens=8300, n_experts=24, top_k=3, d_model=512, d_ff=64, d_ff_shared=128, w_dtype="fp8")),
+    ("toy", dict(_WIDE, n_tokens=9000, n_experts=256, top_k=8, d_model=768, d_ff=128, d_ff_shared=256)),  # ~280 rows per expert
 ])
 def test_persistent_down(cfg_name, over):
-    """bf16 or per-channel E4M3 weights with d a multiple of 256 run the persistent down product,
-    whose DMA ring crosses item boundaries: items of different K (shared expert), K shorter than
-    the ring, one or several column blocks, few and many items per workgroup, nearly empty row
-    tiles."""
+    """bf16 or per-channel E4M3 weights with d a multiple of 256 run the persistent down products,
+    whose DMA rings cross item boundaries: 128 x 256 items below 8192 tokens, 256 x 256 items
+    (with the wide gate/up tiles) from there; items of different K (shared expert), K shorter than
+    the rings, one or several column blocks, few and many items per workgroup, nearly empty row
+    tiles, per-channel scales staged per item."""
     _run_full(get_config(cfg_name, **over))
 
 
