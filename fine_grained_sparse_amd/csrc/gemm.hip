@@ -811,6 +811,21 @@ __device__ __forceinline__ void dma16s(const void *sbase_any, uint32_t voff, con
         : "memory");
 }
 
+// 4 bytes per lane from sbase + voff into LDS at `lds_dst` (wave-uniform) + 4 * lane
+__device__ __forceinline__ void dma4s(const void *sbase_any, uint32_t voff, const void *lds_dst) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds_dst);
+    const uint8_t *sbase = uniform_ptr(sbase_any);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dword %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(dst)
+        : "memory");
+}
+
 // a pointer known to be the same in every lane, kept in scalar registers
 __device__ __forceinline__ const uint8_t *uniform_ptr(const void *p) {
     const uint64_t v = (uint64_t)(uintptr_t)p;
@@ -822,6 +837,10 @@ __device__ __forceinline__ const uint8_t *uniform_ptr(const void *p) {
 // a_base/b_base[j]: wave-uniform bases of DMA j; a_off/b_off[j]: this lane's
 // byte offset (row and swizzled chunk of its LDS slot) at K = 0.
 typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
+// 4-byte LDS read at a 32-bit LDS byte address
+__device__ __forceinline__ float lds_read_f32(uint32_t addr) {
+    return *reinterpret_cast<__attribute__((address_space(3))) const float *>((size_t)addr);
+}
 // 16-byte LDS read at a 32-bit LDS byte address
 __device__ __forceinline__ uint4 lds_read16(uint32_t addr) {
     const u32x4_t v = *reinterpret_cast<lds_u32x4_t *>((size_t)addr);
@@ -1466,19 +1485,21 @@ __device__ __forceinline__ int xcd_map(int slot, int B) {   // launch slot -> wo
     return ((s / B) * kXcds + c) * B + s % B;
 }
 
-template <bool W8>
+template <bool W8, bool BLK>
 __global__ __launch_bounds__(kThreads) void down_gemm_persist_kernel(
     const uint16_t *__restrict__ H, int ldh, const uint8_t *__restrict__ wd, const float *__restrict__ sd,
     const uint8_t *__restrict__ wsd, const float *__restrict__ ssd, const int32_t *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets, uint16_t *__restrict__ Y, int d, int E,
     int f, int fs) {
     static_assert(kAPer == 2 && kBPer == 4, "two activation DMAs per wave and stage");
+    static_assert(W8 || !BLK, "block scales come with E4M3 weights");
     constexpr int NB = W8 ? 4 : 3;                          // ring buffers = fetch distance in stages
     constexpr int kStage = W8 ? kW8StageB : kDmaStageB;     // bytes per stage
     constexpr int kBDma = W8 ? 2 : kBPer;                   // weight DMAs per wave and stage
     constexpr int G = kAPer + kBDma;                        // DMAs per wave and stage
     constexpr int kWs = W8 ? 1 : 2;                         // bytes per weight
-    // E4M3: 8 slots of 256 column scales after the ring (the cursor runs at most NB items ahead)
+    // E4M3: 8 slots after the ring (the cursor runs at most NB items ahead) for an item's 256
+    // column scales, or with block scales its two output blocks' K-block scales (2 f/128 values)
     constexpr int kSlots = W8 ? 8 : 0;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * kStage + kSlots * 1024];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1494,7 +1515,8 @@ __global__ __launch_bounds__(kThreads) void down_gemm_persist_kernel(
     // lane's 32-bit byte offset at K = 0 (H below 4 GiB: checked by the launcher)
     uint32_t a_off[kAPer], b_off[kBDma];
     const uint8_t *b_base = wd;
-    const float *s_base = sd;   // the fetch item's 256 column scales (E4M3)
+    const float *s_base = sd;   // the fetch item's scales (E4M3)
+    int s_cnt = 0;              // block scales: values in the slot
     auto load_fetch_item = [&]() {
         const int item = xcd_map(blockIdx.x + fq * G_wg, B);
         fvalid = item < n_items;
@@ -1506,7 +1528,13 @@ __global__ __launch_bounds__(kThreads) void down_gemm_persist_kernel(
         const int o0 = (item % gx) * kBN;
         const int row0 = offsets[g] + m0, m = min(kBM, offsets[g + 1] - row0);
         b_base = shared ? wsd : wd + (size_t)g * d * K * kWs;
-        if constexpr (W8) s_base = shared ? ssd + o0 : sd + (size_t)g * d + o0;
+        if constexpr (BLK) {   // [E][d/128][K/128]: output blocks o0/128 and o0/128 + 1 are adjacent
+            const int nob = d / 128, nkbk = K / 128;
+            s_base = (shared ? ssd : sd + (size_t)g * nob * nkbk) + (size_t)(o0 / 128) * nkbk;
+            s_cnt = 2 * nkbk;
+        } else if constexpr (W8) {
+            s_base = shared ? ssd + o0 : sd + (size_t)g * d + o0;
+        }
         fnk = K / kBK;
 #pragma unroll
         for (int j = 0; j < kAPer; ++j) {
@@ -1528,8 +1556,12 @@ __global__ __launch_bounds__(kThreads) void down_gemm_persist_kernel(
     auto fetch_next = [&]() {
         if (!fvalid) return;
         uint8_t *buf = smem + fbuf * kStage;
-        if constexpr (W8)
+        if constexpr (BLK) {
+            if (fkt == 0 && wave == 0)   // lanes past the count re-read value 0 (never used)
+                dma4s(s_base, lane < s_cnt ? lane * 4 : 0, smem + NB * kStage + (fq & (kSlots - 1)) * 1024);
+        } else if constexpr (W8) {
             if (fkt == 0 && wave == 0) dma16s(s_base, lane * 16, smem + NB * kStage + (fq & (kSlots - 1)) * 1024);
+        }
         const uint16_t *sa = H + fkt * kBK;
         const uint8_t *sb = b_base + fkt * kBK * kWs;
 #pragma unroll
@@ -1594,6 +1626,82 @@ __global__ __launch_bounds__(kThreads) void down_gemm_persist_kernel(
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if constexpr (BLK) {
+                // 128 x 128 block scales: every 64-wide stage's products of a 16-row
+                // sub-tile are formed in fresh accumulators and folded into the sum
+                // times the scale of its K block (kt / 2) and output block (column
+                // fragments 0-1: the item's first 128 columns, 2-3: the next 128), as
+                // tile_mma_dma_w8b does.  All of a stage's fragments are read before
+                // the barrier that frees its buffer.
+                const uint32_t slot = s0 + NB * kStage + (q & (kSlots - 1)) * 1024;
+                const int nkbk = nk / 2;
+                int cb = gs % NB;
+#pragma nounroll
+                for (int kt = 0; kt < nk; ++kt) {
+                    const int nb = cb == NB - 1 ? 0 : cb + 1;
+                    uint4 bfr[2][4], afr[4][2];
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (LV > 0) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const uint32_t pa = la[h] + cb * kStage, pb = lb[h] + cb * kStage;
+#pragma unroll
+                            for (int ni = 0; ni < 4; ++ni)
+                                bfr[h][ni] = e4m3x8_to_bf16x8(
+                                    lds_read8(pb + (ni < 2 ? ni * 16 : kBN / 2 + (ni - 2) * 16) * kW8RowB));
+#pragma unroll
+                            for (int mi = 0; mi < LV; ++mi) afr[mi][h] = lds_read16(pa + mi * 16 * kDmaRowB);
+                        }
+                    }
+                    const float slo = lds_read_f32(slot + (uint32_t)(kt >> 1) * 4u);
+                    const float shi = lds_read_f32(slot + (uint32_t)(nkbk + (kt >> 1)) * 4u);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const bool last = kt + 1 == nk;
+                    const bool more = gf > gs + 1;
+                    if (more) {
+                        wait_stages(gf - gs - 2);
+                        lds_barrier();
+                    }
+                    if (!last) fetch_next();   // stage gs + NB into buffer cb
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int mi = 0; mi < LV; ++mi) {
+                        f32x4_t pr[4];
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni)
+                            pr[ni] = mfma_bf16(bfr[1][ni], afr[mi][1],
+                                               mfma_bf16(bfr[0][ni], afr[mi][0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni) {
+                            const float c = ni < 2 ? slo : shi;
+#pragma unroll
+                            for (int qq = 0; qq < 4; ++qq) acc[mi][ni][qq] = fmaf(pr[ni][qq], c, acc[mi][ni][qq]);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (last) {
+                        const uint32_t lane_off =
+                            ((uint32_t)(lane & 15) * (uint32_t)d + (uint32_t)(lane >> 4) * 4u) * 2u;
+                        const float one[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni) {
+                            const int c0 = o0 + b_row_of(wn, ni);
+#pragma unroll
+                            for (int mi = 0; mi < LV; ++mi) {
+                                const int rb = wm * 64 + mi * 16;
+                                if (rb + (lane & 15) < m)
+                                    store_bf16x4(Y + (size_t)(row0 + rb) * d + c0, lane_off, acc[mi][ni], one);
+                            }
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (more) fetch_next();
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    ++gs;
+                    cb = nb;
+                }
+                return;
+            }
             auto read_half = [&](uint32_t bo, int h, uint4 (&af)[4], uint4 (&bf)[4]) {
                 if constexpr (LV > 0) {
                     const uint32_t pa = la[h] + bo, pb = lb[h] + bo;
@@ -2731,6 +2839,18 @@ hipError_t launch_down_gemm(const Plan &p) {
     // blocks, 32-bit offsets into H and into one expert's matrix
     const long h_bytes = ((long)p.N * p.k + p.N) * p.ldh * 2;
     const bool w8 = p.wdt == MOE_DTYPE_FP8_E4M3 && !(p.flags & MOE_FLAG_FP8_BLOCK128);
+    // 128 x 128 block scales: both output blocks' K-block scales of an item in one 64-lane DMA
+    const bool w8b = p.wdt == MOE_DTYPE_FP8_E4M3 && (p.flags & MOE_FLAG_FP8_BLOCK128) && p.f <= 4096 &&
+                     p.fs <= 4096 && p.d % kBN == 0 && h_bytes < (1L << 32);
+    if (w8b) {
+        int cus = 0;
+        hipError_t e = cu_count(&cus);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((down_gemm_persist_kernel<true, true>), dim3(cus), block, 0, p.stream, p.H, p.ldh,
+                           (const uint8_t *)p.W.w_down, p.W.s_down, (const uint8_t *)p.W.ws_down, p.W.ss_down,
+                           tiles, n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs);
+        return hipGetLastError();
+    }
     if ((p.wdt == MOE_DTYPE_BF16 || w8) && p.d % kBN == 0 && p.f % kBK == 0 && p.fs % kBK == 0 &&
         h_bytes < (1L << 32) &&
         (long)p.d * (p.f > p.fs ? p.f : p.fs) * 2 < (1L << 32)) {
@@ -2755,11 +2875,11 @@ hipError_t launch_down_gemm(const Plan &p) {
         }
 #endif
         if (w8)
-            hipLaunchKernelGGL(down_gemm_persist_kernel<true>, dim3(cus), block, 0, p.stream, p.H, p.ldh,
+            hipLaunchKernelGGL((down_gemm_persist_kernel<true, false>), dim3(cus), block, 0, p.stream, p.H, p.ldh,
                                (const uint8_t *)p.W.w_down, p.W.s_down, (const uint8_t *)p.W.ws_down, p.W.ss_down,
                                tiles, n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs);
         else
-            hipLaunchKernelGGL(down_gemm_persist_kernel<false>, dim3(cus), block, 0, p.stream, p.H, p.ldh,
+            hipLaunchKernelGGL((down_gemm_persist_kernel<false, false>), dim3(cus), block, 0, p.stream, p.H, p.ldh,
                                (const uint8_t *)p.W.w_down, p.W.s_down, (const uint8_t *)p.W.ws_down, p.W.ss_down,
                                tiles, n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs);
         return hipGetLastError();

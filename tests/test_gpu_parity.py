@@ -251,6 +251,12 @@ def test_wide_tile(cfg_name, over):
     ("toy", dict(_WIDE, n_tokens=8300, n_experts=24, top_k=3, d_model=512, d_ff=64, d_ff_shared=128)),   # K of 1-2 stages
     ("toy", dict(_WIDE, n_tokens=8300, n_experts=24, top_k=3, d_model=512, d_ff=64, d_ff_shared=128, w_dtype="fp8")),
     ("toy", dict(_WIDE, n_tokens=9000, n_experts=256, top_k=8, d_model=768, d_ff=128, d_ff_shared=256)),  # ~280 rows per expert
+    # E4M3 weights with 128 x 128 block scales: every stage folded with its K block's scale
+    ("toy", dict(n_tokens=300, w_dtype="fp8", scale_block=128, d_model=256, d_ff=128, d_ff_shared=256)),
+    ("toy", dict(n_tokens=600, w_dtype="fp8", scale_block=128, x_dtype="bf16", n_experts=64, top_k=8,
+                 d_model=768, d_ff=384, d_ff_shared=128)),
+    ("toy", dict(n_tokens=5000, w_dtype="fp8", scale_block=128, x_dtype="bf16", n_experts=24, top_k=4,
+                 d_model=512, d_ff=256, d_ff_shared=512)),
 ])
 def test_persistent_down(cfg_name, over):
     """bf16 or per-channel E4M3 weights with d a multiple of 256 run the persistent down products,
