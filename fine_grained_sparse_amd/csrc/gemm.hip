@@ -1626,82 +1626,6 @@ __global__ __launch_bounds__(kThreads) void down_gemm_persist_kernel(
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if constexpr (BLK) {
-                // 128 x 128 block scales: every 64-wide stage's products of a 16-row
-                // sub-tile are formed in fresh accumulators and folded into the sum
-                // times the scale of its K block (kt / 2) and output block (column
-                // fragments 0-1: the item's first 128 columns, 2-3: the next 128), as
-                // tile_mma_dma_w8b does.  All of a stage's fragments are read before
-                // the barrier that frees its buffer.
-                const uint32_t slot = s0 + NB * kStage + (q & (kSlots - 1)) * 1024;
-                const int nkbk = nk / 2;
-                int cb = gs % NB;
-#pragma nounroll
-                for (int kt = 0; kt < nk; ++kt) {
-                    const int nb = cb == NB - 1 ? 0 : cb + 1;
-                    uint4 bfr[2][4], afr[4][2];
-                    __builtin_amdgcn_sched_barrier(0);
-                    if constexpr (LV > 0) {
-#pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            const uint32_t pa = la[h] + cb * kStage, pb = lb[h] + cb * kStage;
-#pragma unroll
-                            for (int ni = 0; ni < 4; ++ni)
-                                bfr[h][ni] = e4m3x8_to_bf16x8(
-                                    lds_read8(pb + (ni < 2 ? ni * 16 : kBN / 2 + (ni - 2) * 16) * kW8RowB));
-#pragma unroll
-                            for (int mi = 0; mi < LV; ++mi) afr[mi][h] = lds_read16(pa + mi * 16 * kDmaRowB);
-                        }
-                    }
-                    const float slo = lds_read_f32(slot + (uint32_t)(kt >> 1) * 4u);
-                    const float shi = lds_read_f32(slot + (uint32_t)(nkbk + (kt >> 1)) * 4u);
-                    __builtin_amdgcn_sched_barrier(0);
-                    const bool last = kt + 1 == nk;
-                    const bool more = gf > gs + 1;
-                    if (more) {
-                        wait_stages(gf - gs - 2);
-                        lds_barrier();
-                    }
-                    if (!last) fetch_next();   // stage gs + NB into buffer cb
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int mi = 0; mi < LV; ++mi) {
-                        f32x4_t pr[4];
-#pragma unroll
-                        for (int ni = 0; ni < 4; ++ni)
-                            pr[ni] = mfma_bf16(bfr[1][ni], afr[mi][1],
-                                               mfma_bf16(bfr[0][ni], afr[mi][0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
-#pragma unroll
-                        for (int ni = 0; ni < 4; ++ni) {
-                            const float c = ni < 2 ? slo : shi;
-#pragma unroll
-                            for (int qq = 0; qq < 4; ++qq) acc[mi][ni][qq] = fmaf(pr[ni][qq], c, acc[mi][ni][qq]);
-                        }
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (last) {
-                        const uint32_t lane_off =
-                            ((uint32_t)(lane & 15) * (uint32_t)d + (uint32_t)(lane >> 4) * 4u) * 2u;
-                        const float one[4] = {1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-                        for (int ni = 0; ni < 4; ++ni) {
-                            const int c0 = o0 + b_row_of(wn, ni);
-#pragma unroll
-                            for (int mi = 0; mi < LV; ++mi) {
-                                const int rb = wm * 64 + mi * 16;
-                                if (rb + (lane & 15) < m)
-                                    store_bf16x4(Y + (size_t)(row0 + rb) * d + c0, lane_off, acc[mi][ni], one);
-                            }
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                        if (more) fetch_next();
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    ++gs;
-                    cb = nb;
-                }
-                return;
-            }
             auto read_half = [&](uint32_t bo, int h, uint4 (&af)[4], uint4 (&bf)[4]) {
                 if constexpr (LV > 0) {
                     const uint32_t pa = la[h] + bo, pb = lb[h] + bo;
@@ -1723,6 +1647,87 @@ __global__ __launch_bounds__(kThreads) void down_gemm_persist_kernel(
             };
             // this wave's DMAs of stage gs + 1 landed; the later fetched stages stay in flight
             auto wait_next = [&]() { wait_stages(gf - gs - 2); };
+            if constexpr (BLK) {
+                // 128 x 128 block scales: the products of every 64-wide stage (its two
+                // K halves, on the same double-buffered fragment schedule as below) go
+                // into fresh accumulators that are folded into the sum times the scale
+                // of the stage's K block (kt / 2) and output block (column fragments 0-1:
+                // the item's first 128 columns, 2-3: the next 128), as tile_mma_dma_w8b does
+                const uint32_t slot = s0 + NB * kStage + (q & (kSlots - 1)) * 1024;
+                const int nkbk = nk / 2;
+                f32x4_t pr[4][4];
+                auto mma_into = [&](const uint4 (&af)[4], const uint4 (&bf)[4], bool first) {
+#pragma unroll
+                    for (int mi = 0; mi < LV; ++mi)
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni)
+                            pr[mi][ni] = mfma_bf16(bf[ni], af[mi], first ? f32x4_t{0.f, 0.f, 0.f, 0.f} : pr[mi][ni]);
+                };
+                auto fold = [&](int kt) {
+                    const float slo = lds_read_f32(slot + (uint32_t)(kt >> 1) * 4u);
+                    const float shi = lds_read_f32(slot + (uint32_t)(nkbk + (kt >> 1)) * 4u);
+#pragma unroll
+                    for (int mi = 0; mi < LV; ++mi)
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni) {
+                            const float c = ni < 2 ? slo : shi;
+#pragma unroll
+                            for (int qq = 0; qq < 4; ++qq) acc[mi][ni][qq] = fmaf(pr[mi][ni][qq], c, acc[mi][ni][qq]);
+                        }
+                };
+                uint4 fa0[4], fb0[4], fa1[4], fb1[4];
+                int cb = gs % NB;
+                read_half(cb * kStage, 0, fa0, fb0);
+#pragma nounroll
+                for (int kt = 0; kt + 1 < nk; ++kt) {
+                    const int nb = cb == NB - 1 ? 0 : cb + 1;
+                    __builtin_amdgcn_sched_barrier(0);
+                    read_half(cb * kStage, 1, fa1, fb1);
+                    mma_into(fa0, fb0, true);
+                    interleave_mfma_reads<R, 4 * LV>();
+                    __builtin_amdgcn_sched_barrier(0);
+                    wait_next();
+                    lds_barrier();
+                    fetch_next();
+                    __builtin_amdgcn_sched_barrier(0);
+                    read_half(nb * kStage, 0, fa0, fb0);
+                    mma_into(fa1, fb1, false);
+                    interleave_mfma_reads<R, 4 * LV>();
+                    __builtin_amdgcn_sched_barrier(0);
+                    fold(kt);
+                    __builtin_amdgcn_sched_barrier(0);
+                    ++gs;
+                    cb = nb;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                read_half(cb * kStage, 1, fa1, fb1);
+                mma_into(fa0, fb0, true);
+                __builtin_amdgcn_sched_barrier(0);
+                const bool more = gf > gs + 1;
+                if (more) {
+                    wait_next();
+                    lds_barrier();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                mma_into(fa1, fb1, false);
+                fold(nk - 1);
+                __builtin_amdgcn_sched_barrier(0);
+                const uint32_t lane_off = ((uint32_t)(lane & 15) * (uint32_t)d + (uint32_t)(lane >> 4) * 4u) * 2u;
+                const float one[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    const int c0 = o0 + b_row_of(wn, ni);
+#pragma unroll
+                    for (int mi = 0; mi < LV; ++mi) {
+                        const int rb = wm * 64 + mi * 16;
+                        if (rb + (lane & 15) < m) store_bf16x4(Y + (size_t)(row0 + rb) * d + c0, lane_off, acc[mi][ni], one);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (more) fetch_next();
+                ++gs;
+                return;
+            }
             uint4 fa0[4], fb0[4], fa1[4], fb1[4];
             int cb = gs % NB;
             read_half(cb * kStage, 0, fa0, fb0);
