@@ -2748,6 +2748,246 @@ static bool w8b_dma(const Plan &p) {   // block-scaled FP8 weights, bf16 activat
     return p.d / 128 <= kF8DmaMaxKb && p.f / 128 <= kF8DmaMaxKb && p.fs / 128 <= kF8DmaMaxKb;
 }
 
+// ---- the wide FP8 x FP8 gate/up tile (1 x 128 activation quantisation, from
+// 8192 tokens): 256 x 256 items (256 rows; 128 gate columns and the matching
+// 128 up columns), 8 waves in 2 (rows) x 4 (columns), each 128 x 64 with 128
+// accumulator registers (two waves per SIMD), one 128-wide K block per
+// stage.  Per stage the activation codes (32 KB), the weight codes (32 KB)
+// and the 256 rows' activation scales of that K block arrive by DMA (one
+// dword DMA per wave: rows 32 w .. 32 w + 31), two stages of each in LDS;
+// with block scales the tile's gate and up K-block weight scales come once,
+// before the loop.  Every stage's products are formed per 16-row sub-tile
+// (one v_mfma_f32_16x16x128_f8f6f4 per 16 x 16 block) and folded into the
+// FP32 sums times (row's activation scale) x (column block's weight scale),
+// in the order tile_mma_dma_f8 uses, so H matches the 128-row kernel bit for
+// bit.  The SwiGLU epilogue quantises each row's 128 H values of the tile (the
+// row maximum crosses the 4 column waves through LDS).  Twice the flops per
+// operand byte of the 128 x 256 FP8 tile.
+constexpr int kF8WRows = 256;
+constexpr int kF8WOp = kF8WRows * 128;    // one operand tile of one stage (32 KB)
+constexpr int kF8WScl = 8 * 256;          // one stage's row scales: 64 slots per wave, 32 used
+template <bool BLKW>
+__global__ __launch_bounds__(512) void gate_up_gemm_f8_wide_kernel(
+    const uint8_t *__restrict__ xq, const float *__restrict__ xs, const void *__restrict__ wg,
+    const void *__restrict__ wu, const float *__restrict__ sg, const float *__restrict__ su,
+    const void *__restrict__ wsg, const void *__restrict__ wsu, const float *__restrict__ ssg,
+    const float *__restrict__ ssu, const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ por, uint8_t *__restrict__ hq,
+    float *__restrict__ hs, int ldh, int d, int E, int k, int f, int fs) {
+    // LDS: activations A0 A1, weights B0 B1, row scales S0 S1, the weight block scales
+    // (gate, then up: 256 bytes each, what one 64-lane dword DMA writes)
+    constexpr int kA = 0, kB = 2 * kF8WOp, kS = 4 * kF8WOp, kWsc = kS + 2 * kF8WScl;
+    constexpr int kAPerW = 4, kBPerW = 4;   // 1 KB DMAs per wave and operand stage
+    constexpr int G = kAPerW + kBPerW + 1;  // DMAs per wave and stage
+    // a 64-lane dword DMA writes 256 bytes: one row-scale region per wave, one block-scale region each
+    static_assert(kF8WScl == 8 * 256 && kWsc + 2 * 256 <= 160 * 1024, "DMA regions");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kWsc + 512];
+    int item;
+    if (!xcd_item(*n_tiles * (int)gridDim.x, item)) return;
+    const int u = item / gridDim.x;
+    const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
+    const bool shared = g == E;
+    const int fg = shared ? fs : f;
+    const int c0 = (item % gridDim.x) * 128;
+    if (c0 >= fg) return;
+    const int gstart = offsets[g];
+    const int row0 = gstart + m0, m = min(kF8WRows, offsets[g + 1] - row0);
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), pos = lane & 7;
+    const int wm = w >> 2, wn = w & 3;
+    const int fr = lane & 15, fq = lane >> 4;
+    const int nk = d / 128;
+    auto token_row = [&](int r) { return shared ? (row0 + r - gstart) : por[row0 + r] / k; };
+
+    // DMA sources (byte offsets at K = 0): rows past the group end read row 0 (never stored)
+    uint32_t a_off[kAPerW], b_off[kBPerW], s_off;
+#pragma unroll
+    for (int j = 0; j < kAPerW; ++j) {
+        const int r = 8 * (w * kAPerW + j) + (lane >> 3);
+        a_off[j] = (uint32_t)token_row(r < m ? r : 0) * (uint32_t)d + (uint32_t)((pos ^ (r & 7)) << 4);
+    }
+    const size_t wrow0 = shared ? 0 : (size_t)g * f;
+    // weight rows 0..127 are gate rows c0.., 128..255 the matching up rows: waves 0-3 fetch gate rows
+    const uint8_t *b_base = uniform_ptr((const uint8_t *)(w < 4 ? (shared ? wsg : wg) : (shared ? wsu : wu)) +
+                                        (wrow0 + c0) * (size_t)d);
+#pragma unroll
+    for (int j = 0; j < kBPerW; ++j) {
+        const int r = 8 * (w * kBPerW + j) + (lane >> 3);
+        b_off[j] = (uint32_t)(r & 127) * (uint32_t)d + (uint32_t)((pos ^ (r & 7)) << 4);
+    }
+    {
+        const int r = 32 * w + (lane & 31);
+        s_off = (uint32_t)token_row(r < m ? r : 0) * (uint32_t)nk * 4u;
+    }
+    const uint32_t s0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;
+    auto fetch = [&](int kt, int buf) __attribute__((always_inline)) {
+        const uint8_t *sa = xq + kt * 128, *sb = b_base + kt * 128;
+#pragma unroll
+        for (int j = 0; j < kAPerW; ++j) dma16s(sa, a_off[j], smem + kA + buf * kF8WOp + (w * kAPerW + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < kBPerW; ++j) dma16s(sb, b_off[j], smem + kB + buf * kF8WOp + (w * kBPerW + j) * 1024);
+        dma4s(xs + kt, s_off, smem + kS + buf * kF8WScl + w * 256);
+    };
+    if constexpr (BLKW) {   // the tile's K-block weight scales: gate (wave 0) and up (wave 1)
+        if (w < 2) {
+            const size_t sb = ((shared ? 0 : (size_t)g * (f / 128)) + c0 / 128) * (size_t)nk;
+            const float *src = (w == 0 ? (shared ? ssg : sg) : (shared ? ssu : su)) + sb;
+            dma4s(src, lane < nk ? lane * 4 : 0, smem + kWsc + w * 256);
+        }
+    }
+    fetch(0, 0);
+    if (nk > 1) fetch(1, 1);
+    if (nk > 1) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(G));
+    else __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // fragment addresses in buffer 0: activation row wm*128 + lane%16 (+16 mi), weight row
+    // b_row_of(wn, ni) + lane%16; a lane's 32 K bytes are chunks 2 (lane/16) and 2 (lane/16) + 1
+    uint32_t la[2], lb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int ch = 2 * fq + c;
+        la[c] = s0 + kA + (wm * 128 + fr) * 128 + ((ch ^ (fr & 7)) << 4);
+        lb[c] = s0 + kB + (wn * 32 + fr) * 128 + ((ch ^ (fr & 7)) << 4);
+    }
+    // this lane's row scale slot for sub-tile mi: row wm*128 + mi*16 + lane%16 -> (row / 32) * 64 + row % 32
+    const uint32_t ls = s0 + kS + (uint32_t)(((wm * 128 + fr) >> 5) * 64 + ((wm * 128 + fr) & 31)) * 4u;
+
+    f32x4_t acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto run = [&](auto live_c) __attribute__((always_inline)) {
+        constexpr int LV = decltype(live_c)::value;   // live 16-row sub-tiles (rounded up to even)
+        auto stage = [&](int kt, auto p_c) __attribute__((always_inline)) {
+            constexpr int P = decltype(p_c)::value;   // buffer kt % 2
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (LV > 0) {
+                uint4 bf[4][2];
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+                        bf[ni][c] = lds_read16(lb[c] + P * kF8WOp + (ni < 2 ? ni * 16 : 128 + (ni - 2) * 16) * 128);
+                const float wlo = BLKW ? lds_read_f32(s0 + kWsc + kt * 4) : 1.f;
+                const float whi = BLKW ? lds_read_f32(s0 + kWsc + 256 + kt * 4) : 1.f;
+                uint4 a0 = lds_read16(la[0] + P * kF8WOp), a1 = lds_read16(la[1] + P * kF8WOp);
+#pragma unroll
+                for (int mi = 0; mi < LV; ++mi) {
+                    // the next sub-tile's fragments requested before this one's MFMAs
+                    uint4 n0 = a0, n1 = a1;
+                    if (mi + 1 < LV) {
+                        n0 = lds_read16(la[0] + P * kF8WOp + (mi + 1) * 16 * 128);
+                        n1 = lds_read16(la[1] + P * kF8WOp + (mi + 1) * 16 * 128);
+                    }
+                    // sub-tile mi's rows are 16 consecutive rows: slot offset (mi*16 / 32) * 64 + (mi & 1) * 16
+                    const float sa = lds_read_f32(ls + P * kF8WScl + (uint32_t)((mi >> 1) * 64 + (mi & 1) * 16) * 4u);
+                    f32x4_t pr[4];
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) pr[ni] = mfma_f8(bf[ni][0], bf[ni][1], a0, a1);
+                    const float clo = sa * wlo, chi = sa * whi;
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) {
+                        const float c = ni < 2 ? clo : chi;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[mi][ni][q] = fmaf(pr[ni][q], c, acc[mi][ni][q]);
+                    }
+                    // the fold stays here: the empty statements take the sums as operands, so
+                    // the products need not be kept until the end of the stage (registers)
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) asm volatile("" : "+v"(acc[mi][ni]));
+                    a0 = n0;
+                    a1 = n1;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < nk) {
+                // own DMAs of stage kt+1 landed and every wave is done with buffer P: refill it
+                __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
+                lds_barrier();
+                if (kt + 2 < nk) fetch(kt + 2, P);
+            }
+        };
+        int kt = 0;
+        for (; kt + 2 <= nk; kt += 2) {
+            stage(kt, Live<0>{});
+            stage(kt + 1, Live<1>{});
+        }
+        if (kt < nk) stage(kt, Live<0>{});
+    };
+    const int live = min(8, max(0, (m - wm * 128 + 15) / 16));
+    switch ((live + 1) & ~1) {
+        case 8: run(Live<8>{}); break;
+        case 6: run(Live<6>{}); break;
+        case 4: run(Live<4>{}); break;
+        case 2: run(Live<2>{}); break;
+        default: run(Live<0>{}); break;
+    }
+
+    // SwiGLU into acc[mi][0..1]: row wm*128 + mi*16 + lane%16, H column c0 + wn*32 + ni*16 + 4 (lane/16) + q
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+        const int col = c0 + wn * 32 + ni * 16 + fq * 4;
+        float gs[4] = {1.f, 1.f, 1.f, 1.f}, us[4] = {1.f, 1.f, 1.f, 1.f};
+        if (!BLKW) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                gs[q] = shared ? ssg[col + q] : sg[wrow0 + col + q];
+                us[q] = shared ? ssu[col + q] : su[wrow0 + col + q];
+            }
+        }
+#pragma unroll
+        for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[mi][ni][q] = silu(acc[mi][ni][q] * gs[q]) * (acc[mi][ni + 2][q] * us[q]);
+    }
+    // row maxima over the tile's 128 H columns: this wave's 32, then across the 4 column
+    // waves through LDS (the first activation buffer, free once every wave is done)
+    float amax[8];
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) {
+        float mx = 0.f;
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) mx = fmaxf(mx, fabsf(acc[mi][ni][q]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        amax[mi] = mx;
+    }
+    lds_barrier();
+    float *red = reinterpret_cast<float *>(smem + kA);   // [256 rows][4 column waves]
+    if (lane < 16) {
+#pragma unroll
+        for (int mi = 0; mi < 8; ++mi) red[(wm * 128 + mi * 16 + lane) * 4 + wn] = amax[mi];
+    }
+    lds_barrier();
+    const int nhb = ldh / 128;
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) {
+        const int r = wm * 128 + mi * 16 + fr;
+        const float4 rm = *reinterpret_cast<const float4 *>(red + r * 4);
+        const float mx = fmaxf(fmaxf(rm.x, rm.y), fmaxf(rm.z, rm.w));
+        const float sc = mx > 0.f ? mx / 448.0f : 1.0f;
+        if (r < m) {
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+                const int col = c0 + wn * 32 + ni * 16 + fq * 4;
+                float v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = fminf(fmaxf(acc[mi][ni][q] / sc, -448.f), 448.f);
+                uint32_t wv = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+                wv = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], wv, true);
+                *reinterpret_cast<uint32_t *>(hq + (size_t)(row0 + r) * ldh + col) = wv;
+            }
+            if (wn == 0 && lane < 16) hs[(size_t)(row0 + r) * nhb + c0 / 128] = sc;
+        }
+    }
+}
+
 static bool f8_dma(const Plan &p) {
     return p.d / 128 <= kF8DmaMaxKb && p.f / 128 <= kF8DmaMaxKb && p.fs / 128 <= kF8DmaMaxKb;
 }
@@ -2757,6 +2997,17 @@ hipError_t launch_gate_up_gemm(const Plan &p) {
     // spare tile rows: the XCD-aware order needs n + 8 * kXcdTiles * gx launch slots
     const int gx = (fmax + kBN / 2 - 1) / (kBN / 2);
     dim3 grid(gx, p.max_tiles + kXcds * kXcdTiles), block(kThreads);
+    if (p.bm == kGemmBMWide && p.aq) {   // 1 x 128 activation quantisation, 256-row tiles (gemm_bm)
+        hipError_t e = launch_quant_groups(p.x, 1, p.d, p.N, p.d, p.xq, p.d, p.xs, p.d / 128, p.stream);
+        if (e != hipSuccess) return e;
+#define FGS_GUFW(B)                                                                                              \
+    hipLaunchKernelGGL((gate_up_gemm_f8_wide_kernel<B>), grid, dim3(512), 0, p.stream, p.xq, p.xs, p.W.w_gate,      \
+                       p.W.w_up, p.W.s_gate, p.W.s_up, p.W.ws_gate, p.W.ws_up, p.W.ss_gate, p.W.ss_up, p.tiles,      \
+                       p.n_tiles, p.offsets, p.por, p.hq, p.hs, p.ldh, p.d, p.E, p.k, p.f, p.fs)
+        if (p.flags & MOE_FLAG_FP8_BLOCK128) FGS_GUFW(true); else FGS_GUFW(false);
+#undef FGS_GUFW
+        return hipGetLastError();
+    }
     if (p.bm == kGemmBMWide) {   // bf16 activations, bf16 or per-channel E4M3 weights, 256-row tiles (gemm_bm)
 #define FGS_GUW(W8)                                                                                            \
     hipLaunchKernelGGL((gate_up_gemm_wide_kernel<kWideWMW, W8>), grid, dim3(Wide<kWideWMW>::kThreads), 0, p.stream, \
@@ -2831,7 +3082,7 @@ hipError_t launch_down_gemm(const Plan &p) {
     if (p.aq) {
 #define FGS_DNF(B, D)                                                                                          \
     hipLaunchKernelGGL((down_gemm_f8_kernel<B, D>), grid, block, D ? 0 : kGemmLds, p.stream, p.hq, p.hs, p.ldh,     \
-                       p.W.w_down, p.W.s_down, p.W.ws_down, p.W.ss_down, p.tiles, p.n_tiles, p.offsets, Y, p.d, p.E, \
+                       p.W.w_down, p.W.s_down, p.W.ws_down, p.W.ss_down, tiles, n_tiles, p.offsets, Y, p.d, p.E, \
                        p.f, p.fs)
         const bool blk = (p.flags & MOE_FLAG_FP8_BLOCK128) != 0;
         if (f8_dma(p)) { if (blk) FGS_DNF(true, true); else FGS_DNF(false, true); }

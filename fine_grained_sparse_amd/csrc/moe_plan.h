@@ -99,9 +99,15 @@ static_assert(kWideMinN > 256, "wide tiles need the multi-block dispatch");
 inline int gemm_bm(int N, int d, int k, int f, int fs, int xdt, int wdt, uint32_t flags) {
     const long ldh = f > fs ? f : fs;
     const bool fits32 = (long)N * d * 2 < (1L << 32) && ((long)N * k + N) * ldh * 2 < (1L << 32);
-    const bool wide_w = wdt == MOE_DTYPE_BF16 || (wdt == MOE_DTYPE_FP8_E4M3 && !(flags & MOE_FLAG_FP8_BLOCK128));
-    if (xdt == MOE_DTYPE_BF16 && wide_w && !(flags & MOE_FLAG_FP8_ACT_QUANT) && N >= kWideMinN && fits32)
-        return kGemmBMWide;
+    // bf16 or per-channel E4M3 weights with bf16 activations; or, with 1 x 128 activation
+    // quantisation, E4M3 weights of either scale layout and K up to 24 blocks of 128
+    const bool aq = (flags & MOE_FLAG_FP8_ACT_QUANT) != 0;
+#ifndef FGS_WIDE_F8
+#define FGS_WIDE_F8 1
+#endif
+    const bool wide_w = aq ? FGS_WIDE_F8 && wdt == MOE_DTYPE_FP8_E4M3 && d / 128 <= 24
+                           : wdt == MOE_DTYPE_BF16 || (wdt == MOE_DTYPE_FP8_E4M3 && !(flags & MOE_FLAG_FP8_BLOCK128));
+    if (xdt == MOE_DTYPE_BF16 && wide_w && N >= kWideMinN && fits32) return kGemmBMWide;
     return kGemmBM;
 }
 

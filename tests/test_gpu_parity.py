@@ -161,10 +161,17 @@ def test_quantize_groups_bit_exact(dtype, rows, cols):
     dict(n_tokens=200, d_model=384, d_ff=256, d_ff_shared=128),
     dict(n_tokens=250, d_model=3072, d_ff=256, d_ff_shared=128),   # 24 K blocks: the direct-to-LDS tile's limit
     dict(n_tokens=250, d_model=3200, d_ff=256, d_ff_shared=128),   # 25 K blocks: the register-staged tile
+    # from 8192 tokens: the 256 x 256 FP8 x FP8 gate/up tile (8 waves of 128 x 64)
+    dict(n_tokens=8192, n_experts=8, top_k=2, d_model=256, d_ff=256, d_ff_shared=128),
+    dict(n_tokens=8192, n_experts=8, top_k=2, d_model=256, d_ff=256, d_ff_shared=128, scale_block=0),
+    dict(n_tokens=8300, n_experts=24, top_k=3, d_model=640, d_ff=128, d_ff_shared=384),   # odd stage count
+    dict(n_tokens=8200, n_experts=40, top_k=4, d_model=128, d_ff=256, d_ff_shared=128, scale_block=0),  # 1 stage
+    dict(n_tokens=9000, n_experts=256, top_k=8, d_model=384, d_ff=128, d_ff_shared=256),  # ~280 rows per expert
 ])
 def test_fp8_act_quant_toy(over):
     """1 x 128 activation quantisation with FP8 x FP8 matmuls (MOE_FLAG_FP8_ACT_QUANT): stream and
-    GEMM paths, block and per-channel weight scales, odd block counts, f != f_s, both GEMM tiles."""
+    GEMM paths, block and per-channel weight scales, odd block counts, f != f_s, the 128-row tiles
+    (direct-to-LDS and register-staged) and the 256-row gate/up tile."""
     base = dict(x_dtype="bf16", w_dtype="fp8", scale_block=128, d_ff=128, d_ff_shared=128)
     base.update(over)
     _run_full(get_config("toy", **base), act_quant=True)
