@@ -2874,6 +2874,23 @@ __global__ __launch_bounds__(512) void gate_up_gemm_f8_wide_kernel(
                 const float wlo = BLKW ? lds_read_f32(s0 + kWsc + kt * 4) : 1.f;
                 const float whi = BLKW ? lds_read_f32(s0 + kWsc + 256 + kt * 4) : 1.f;
                 uint4 a0 = lds_read16(la[0] + P * kF8WOp), a1 = lds_read16(la[1] + P * kF8WOp);
+                // the products of sub-tile mi are folded while those of mi + 1 are formed
+                // (two product sets alternate), so the matrix core and the FP32 folds overlap
+                f32x4_t p0[4], p1[4];
+                float sp0 = 0.f, sp1 = 0.f;   // the row scale of the products in p0 / p1
+                auto fold = [&](int mi, const f32x4_t (&pr)[4], float sa) __attribute__((always_inline)) {
+                    const float clo = sa * wlo, chi = sa * whi;
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) {
+                        const float c = ni < 2 ? clo : chi;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[mi][ni][q] = fmaf(pr[ni][q], c, acc[mi][ni][q]);
+                    }
+                    // the empty statements take the sums as operands: the fold happens here,
+                    // not at the end of the stage (which would keep every product live)
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) asm volatile("" : "+v"(acc[mi][ni]));
+                };
 #pragma unroll
                 for (int mi = 0; mi < LV; ++mi) {
                     // the next sub-tile's fragments requested before this one's MFMAs
@@ -2884,24 +2901,23 @@ __global__ __launch_bounds__(512) void gate_up_gemm_f8_wide_kernel(
                     }
                     // sub-tile mi's rows are 16 consecutive rows: slot offset (mi*16 / 32) * 64 + (mi & 1) * 16
                     const float sa = lds_read_f32(ls + P * kF8WScl + (uint32_t)((mi >> 1) * 64 + (mi & 1) * 16) * 4u);
-                    f32x4_t pr[4];
+                    if (mi & 1) {
 #pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) pr[ni] = mfma_f8(bf[ni][0], bf[ni][1], a0, a1);
-                    const float clo = sa * wlo, chi = sa * whi;
+                        for (int ni = 0; ni < 4; ++ni) p1[ni] = mfma_f8(bf[ni][0], bf[ni][1], a0, a1);
+                        sp1 = sa;
+                        fold(mi - 1, p0, sp0);
+                    } else {
 #pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        const float c = ni < 2 ? clo : chi;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) acc[mi][ni][q] = fmaf(pr[ni][q], c, acc[mi][ni][q]);
+                        for (int ni = 0; ni < 4; ++ni) p0[ni] = mfma_f8(bf[ni][0], bf[ni][1], a0, a1);
+                        sp0 = sa;
+                        if (mi > 0) fold(mi - 1, p1, sp1);
                     }
-                    // the fold stays here: the empty statements take the sums as operands, so
-                    // the products need not be kept until the end of the stage (registers)
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) asm volatile("" : "+v"(acc[mi][ni]));
                     a0 = n0;
                     a1 = n1;
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                if ((LV - 1) & 1) fold(LV - 1, p1, sp1);
+                else fold(LV - 1, p0, sp0);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (kt + 1 < nk) {
