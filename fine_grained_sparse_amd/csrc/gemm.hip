@@ -47,12 +47,14 @@
 // A 128 x 256 stage of 128 bytes per row moves 48 KB for 4.2 MFLOP (bf16) or
 // 8.4 MFLOP (FP8).
 //
-// From 8192 tokens with bf16 activations the gate/up product takes 256 x 256
-// tiles of 16 waves (gate_up_gemm_wide_kernel).  The down product (K = f, only
-// eight 64-wide stages per item) with bf16 or per-channel E4M3 weights runs
-// persistent kernels whose DMA rings cross item boundaries:
-// down_gemm_persist_kernel on 128 x 256 items and, with the wide gate/up
-// tiles, down_gemm_wide_persist_kernel on 256 x 256 items.
+// From 8192 tokens the gate/up product takes 256 x 256 tiles: 16 waves with
+// bf16 activations (gate_up_gemm_wide_kernel), 8 waves with 1 x 128 quantised
+// ones (gate_up_gemm_f8_wide_kernel).  The down product (K = f, only eight
+// 64-wide or four 128-wide stages per item) runs persistent kernels whose DMA
+// rings cross item boundaries: down_gemm_persist_kernel on 128 x 256 items
+// (bf16 weights, E4M3 with per-channel or block scales), with the wide gate/up
+// tiles down_gemm_wide_persist_kernel on 256 x 256 items, and for quantised
+// activations down_gemm_f8_persist_kernel (FP8 x FP8, 128 x 256 items).
 #include <atomic>
 
 #include "moe_common.h"
@@ -1456,6 +1458,9 @@ __global__ __launch_bounds__(kThreads) void down_gemm_kernel(
 #endif
 #ifndef FGS_DOWN_WIDE
 #define FGS_DOWN_WIDE 1
+#endif
+#ifndef FGS_DOWN_F8P
+#define FGS_DOWN_F8P 1
 #endif
 // Epilogue helpers of the persistent down kernels.  Inside their item loop a
 // vector, flat or spilled memory access would make the compiler wait for
@@ -3004,6 +3009,237 @@ __global__ __launch_bounds__(512) void gate_up_gemm_f8_wide_kernel(
     }
 }
 
+// ---- persistent FP8 x FP8 down product (1 x 128 quantised H, E4M3 weights with
+// per-channel or 128 x 128 block scales), K (f and f_s) at most 4 blocks of 128,
+// d a multiple of 256.  The ring and the item walk of down_gemm_persist_kernel
+// with 128-wide K stages of E4M3 codes (48 KB: 128 H rows and 256 weight rows
+// of 128 bytes).  With an item's first stage every wave fetches one quarter
+// of its activation scales (K block w / 2, rows 64 (w % 2) ..: 512 values in
+// an LDS slot) and wave 0 its weight scales (both output blocks' K-block
+// scales, or 256 column scales), all ahead of the stage's own DMAs.  All of a
+// stage's fragments are read before its barrier; each 16 x 16 product (one
+// v_mfma_f32_16x16x128_f8f6f4) is folded into the FP32 sum times (row scale)
+// x (block scale) one sub-tile behind the MFMAs, as tile_mma_dma_f8 orders
+// them, so Y matches the one-item kernel bit for bit.
+constexpr int kF8PSlot = 3 * 1024;   // 2 KB activation scales + 1 KB weight scales
+template <bool BLKW>
+__global__ __launch_bounds__(kThreads) void down_gemm_f8_persist_kernel(
+    const uint8_t *__restrict__ hq, const float *__restrict__ hs, int ldh, const uint8_t *__restrict__ wd,
+    const float *__restrict__ sd, const uint8_t *__restrict__ wsd, const float *__restrict__ ssd,
+    const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets,
+    uint16_t *__restrict__ Y, int d, int E, int f, int fs) {
+    static_assert(kAPer == 2 && kBPer == 4, "six operand DMAs per wave and stage");
+    constexpr int NB = 3, kStage = kDmaStageB, G = kAPer + kBPer, kSlots = 4;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * kStage + kSlots * kF8PSlot];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / kWN, wn = wave % kWN, fr = lane & 15, fg = lane >> 4, pos = lane & 7;
+    const int gx = d / kBN, B = kXcdTiles * gx;
+    const int n_items = *n_tiles * gx;
+    const int G_wg = gridDim.x;
+    const int nhb = ldh / 128;
+    const uint32_t s0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;
+    constexpr int kSlotBase = NB * kStage;
+
+    // fetch cursor
+    int fq = 0, fkt = 0, fnk = 0, fbuf = 0, gf = 0;
+    bool fvalid = false;
+    uint32_t a_off[kAPer], b_off[kBPer], sa_off;
+    const uint8_t *b_base = wd;
+    const float *w_scale = sd;   // block scales (2 K-block runs) or 256 column scales of the item
+    int w_cnt = 0;
+    auto load_fetch_item = [&]() {
+        const int item = xcd_map(blockIdx.x + fq * G_wg, B);
+        fvalid = item < n_items;
+        if (!fvalid) return;
+        const int u = item / gx;
+        const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
+        const bool shared = g == E;
+        const int K = shared ? fs : f;
+        const int o0 = (item % gx) * kBN;
+        const int row0 = offsets[g] + m0, m = min(kBM, offsets[g + 1] - row0);
+        const int nkb = K / 128;
+        fnk = nkb;
+        b_base = (shared ? wsd : wd + (size_t)g * d * K);
+        if constexpr (BLKW) {   // [E][d/128][K/128]: output blocks o0/128 and o0/128 + 1 are adjacent
+            w_scale = (shared ? ssd : sd + (size_t)g * (d / 128) * nkb) + (size_t)(o0 / 128) * nkb;
+            w_cnt = 2 * nkb;
+        } else {
+            w_scale = shared ? ssd + o0 : sd + (size_t)g * d + o0;
+        }
+#pragma unroll
+        for (int j = 0; j < kAPer; ++j) {
+            const int r = 8 * (wave * kAPer + j) + (lane >> 3);
+            a_off[j] = (uint32_t)(row0 + (r < m ? r : 0)) * (uint32_t)ldh + (uint32_t)((pos ^ (r & 7)) << 4);
+        }
+#pragma unroll
+        for (int j = 0; j < kBPer; ++j) {
+            const int r = 8 * (wave * kBPer + j) + (lane >> 3);
+            b_off[j] = (uint32_t)(o0 + r) * (uint32_t)K + (uint32_t)((pos ^ (r & 7)) << 4);
+        }
+        // this wave's quarter of the activation scales: K block wave / 2, rows 64 (wave % 2) + lane
+        const int kb = (wave >> 1) < nkb ? (wave >> 1) : 0, r = 64 * (wave & 1) + lane;
+        sa_off = ((uint32_t)(row0 + (r < m ? r : 0)) * (uint32_t)nhb + (uint32_t)kb) * 4u;
+    };
+    auto fetch_next = [&]() {
+        if (!fvalid) return;
+        if (fkt == 0) {   // the item's scales, ahead of the stage's own DMAs
+            uint8_t *slot = smem + kSlotBase + (fq & (kSlots - 1)) * kF8PSlot;
+            dma4s(hs, sa_off, slot + wave * 256);
+            if (wave == 0) {
+                if constexpr (BLKW) dma4s(w_scale, lane < w_cnt ? lane * 4 : 0, slot + 2048);
+                else dma16s(w_scale, lane * 16, slot + 2048);
+            }
+        }
+        uint8_t *buf = smem + fbuf * kStage;
+        const uint8_t *sa = hq + fkt * 128, *sb = b_base + fkt * 128;
+#pragma unroll
+        for (int j = 0; j < kAPer; ++j) dma16s(sa, a_off[j], buf + (wave * kAPer + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < kBPer; ++j) dma16s(sb, b_off[j], buf + kBM * kDmaRowB + (wave * kBPer + j) * 1024);
+        fbuf = fbuf == NB - 1 ? 0 : fbuf + 1;
+        ++gf;
+        if (++fkt == fnk) {
+            fkt = 0;
+            ++fq;
+            load_fetch_item();
+        }
+    };
+    auto wait_stages = [&](int later) {
+        if (later >= 1) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(G));
+        else __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
+    };
+    // fragment addresses in buffer 0: H row wm*64 + lane%16, weight row wn*32 + lane%16 (+ the
+    // column fragment's offset), K chunks 2 (lane/16) and 2 (lane/16) + 1
+    uint32_t la[2], lb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int ch = 2 * fg + c;
+        la[c] = s0 + (wm * 64 + fr) * kDmaRowB + ((ch ^ (fr & 7)) << 4);
+        lb[c] = s0 + kBM * kDmaRowB + (wn * 32 + fr) * kDmaRowB + ((ch ^ (fr & 7)) << 4);
+    }
+
+    load_fetch_item();
+    if (!fvalid) return;
+    fetch_next();
+    fetch_next();
+    wait_stages(gf - 1);   // stage 0 (and the first item's scales) landed
+    lds_barrier();
+    fetch_next();
+    __builtin_amdgcn_sched_barrier(0);
+
+    int gs = 0;
+    for (int q = 0;; ++q) {
+        const int item = xcd_map(blockIdx.x + q * G_wg, B);
+        if (item >= n_items) break;
+        const int u = item / gx;
+        const int g = tiles[2 * u], m0 = tiles[2 * u + 1];
+        const bool shared = g == E;
+        const int nk = (shared ? fs : f) / 128;
+        const int o0 = (item % gx) * kBN;
+        const int row0 = offsets[g] + m0, m = min(kBM, offsets[g + 1] - row0);
+        const uint32_t slot = s0 + kSlotBase + (q & (kSlots - 1)) * kF8PSlot;
+
+        auto run = [&](auto live_c) __attribute__((always_inline)) {
+            constexpr int LV = decltype(live_c)::value;
+            f32x4_t acc[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            int cb = gs % NB;
+#pragma nounroll
+            for (int kt = 0; kt < nk; ++kt) {
+                const int nb = cb == NB - 1 ? 0 : cb + 1;
+                uint4 bf[4][2], af[4][2];
+                float sa[4] = {0.f, 0.f, 0.f, 0.f};
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (LV > 0) {
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                        for (int c = 0; c < 2; ++c)
+                            bf[ni][c] = lds_read16(lb[c] + cb * kStage + (ni < 2 ? ni * 16 : kBN / 2 + (ni - 2) * 16) * kDmaRowB);
+#pragma unroll
+                    for (int mi = 0; mi < LV; ++mi) {
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) af[mi][c] = lds_read16(la[c] + cb * kStage + mi * 16 * kDmaRowB);
+                        sa[mi] = lds_read_f32(slot + (uint32_t)(kt * kBM + wm * 64 + mi * 16 + fr) * 4u);
+                    }
+                }
+                const float wlo = BLKW ? lds_read_f32(slot + 2048 + kt * 4) : 1.f;
+                const float whi = BLKW ? lds_read_f32(slot + 2048 + (nk + kt) * 4) : 1.f;
+                __builtin_amdgcn_sched_barrier(0);
+                const bool last = kt + 1 == nk;
+                const bool more = gf > gs + 1;
+                if (more) {
+                    wait_stages(gf - gs - 2);   // stage gs + 1 landed; a later one may stay in flight
+                    lds_barrier();
+                }
+                if (!last) fetch_next();   // stage gs + NB into buffer cb
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (LV > 0) {
+                    f32x4_t p0[4], p1[4];
+                    auto fold = [&](int mi, const f32x4_t (&pr)[4]) __attribute__((always_inline)) {
+                        const float clo = sa[mi] * wlo, chi = sa[mi] * whi;
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni) {
+                            const float c = ni < 2 ? clo : chi;
+#pragma unroll
+                            for (int qq = 0; qq < 4; ++qq) acc[mi][ni][qq] = fmaf(pr[ni][qq], c, acc[mi][ni][qq]);
+                        }
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni) asm volatile("" : "+v"(acc[mi][ni]));
+                    };
+#pragma unroll
+                    for (int mi = 0; mi < LV; ++mi) {
+                        if (mi & 1) {
+#pragma unroll
+                            for (int ni = 0; ni < 4; ++ni) p1[ni] = mfma_f8(bf[ni][0], bf[ni][1], af[mi][0], af[mi][1]);
+                            fold(mi - 1, p0);
+                        } else {
+#pragma unroll
+                            for (int ni = 0; ni < 4; ++ni) p0[ni] = mfma_f8(bf[ni][0], bf[ni][1], af[mi][0], af[mi][1]);
+                            if (mi > 0) fold(mi - 1, p1);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if ((LV - 1) & 1) fold(LV - 1, p1);
+                    else fold(LV - 1, p0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (last) {
+                    const uint32_t lane_off =
+                        ((uint32_t)(lane & 15) * (uint32_t)d + (uint32_t)(lane >> 4) * 4u) * 2u;
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) {
+                        const int c0 = o0 + b_row_of(wn, ni);
+                        float sc[4] = {1.f, 1.f, 1.f, 1.f};
+                        if constexpr (!BLKW) slot_scales(slot + 2048, b_row_of(wn, ni), lane, sc);
+#pragma unroll
+                        for (int mi = 0; mi < LV; ++mi) {
+                            const int rb = wm * 64 + mi * 16;
+                            if (rb + (lane & 15) < m) store_bf16x4(Y + (size_t)(row0 + rb) * d + c0, lane_off, acc[mi][ni], sc);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (more) fetch_next();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                ++gs;
+                cb = nb;
+            }
+        };
+        const int live = min(4, max(0, (m - wm * 64 + 15) / 16));
+        switch (live) {
+            case 4: run(Live<4>{}); break;
+            case 3: run(Live<3>{}); break;
+            case 2: run(Live<2>{}); break;
+            case 1: run(Live<1>{}); break;
+            default: run(Live<0>{}); break;
+        }
+    }
+}
+
 static bool f8_dma(const Plan &p) {
     return p.d / 128 <= kF8DmaMaxKb && p.f / 128 <= kF8DmaMaxKb && p.fs / 128 <= kF8DmaMaxKb;
 }
@@ -3095,6 +3331,23 @@ hipError_t launch_down_gemm(const Plan &p) {
     const int32_t *tiles = p.bm == kGemmBMWide ? p.tiles2 : p.tiles;
     const int32_t *n_tiles = p.bm == kGemmBMWide ? p.n_tiles2 : p.n_tiles;
     grid.y = (p.bm == kGemmBMWide ? p.max_tiles2 : p.max_tiles) + kXcds * kXcdTiles;
+#if FGS_DOWN_PERSIST && FGS_DOWN_F8P
+    if (p.aq && p.d % kBN == 0 && p.f <= 512 && p.fs <= 512 && p.f % 128 == 0 && p.fs % 128 == 0 &&
+        ((long)p.N * p.k + p.N) * p.ldh < (1L << 32) && (long)p.d * (p.f > p.fs ? p.f : p.fs) < (1L << 32)) {
+        int cus = 0;
+        hipError_t e = cu_count(&cus);
+        if (e != hipSuccess) return e;
+        if (p.flags & MOE_FLAG_FP8_BLOCK128)
+            hipLaunchKernelGGL(down_gemm_f8_persist_kernel<true>, dim3(cus), block, 0, p.stream, p.hq, p.hs, p.ldh,
+                               (const uint8_t *)p.W.w_down, p.W.s_down, (const uint8_t *)p.W.ws_down, p.W.ss_down,
+                               tiles, n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs);
+        else
+            hipLaunchKernelGGL(down_gemm_f8_persist_kernel<false>, dim3(cus), block, 0, p.stream, p.hq, p.hs, p.ldh,
+                               (const uint8_t *)p.W.w_down, p.W.s_down, (const uint8_t *)p.W.ws_down, p.W.ss_down,
+                               tiles, n_tiles, p.offsets, Y, p.d, p.E, p.f, p.fs);
+        return hipGetLastError();
+    }
+#endif
     if (p.aq) {
 #define FGS_DNF(B, D)                                                                                          \
     hipLaunchKernelGGL((down_gemm_f8_kernel<B, D>), grid, block, D ? 0 : kGemmLds, p.stream, p.hq, p.hs, p.ldh,     \

@@ -274,6 +274,29 @@ def test_persistent_down(cfg_name, over):
     _run_full(get_config(cfg_name, **over))
 
 
+@pytest.mark.parametrize("over", [
+    dict(n_tokens=300, d_model=256),                                                  # one stage: items run ahead
+    dict(n_tokens=300, d_model=256, scale_block=0),
+    dict(n_tokens=6000, n_experts=32, top_k=4, d_model=1024, d_ff=384, d_ff_shared=512),   # ~4 items per CU
+    dict(n_tokens=3000, n_experts=32, top_k=4, d_model=768, d_ff=128, d_ff_shared=256, scale_block=0),
+    dict(n_tokens=600, n_experts=64, top_k=8, d_model=512, d_ff=256, d_ff_shared=384),
+])
+def test_persistent_down_act_quant(over):
+    """1 x 128 quantised H with E4M3 weights (block or per-channel scales), d a multiple of 256
+    and K at most 4 blocks: the persistent FP8 x FP8 down product, its ring crossing items of
+    different K, the activation and weight scales staged per item in LDS."""
+    base = dict(x_dtype="bf16", w_dtype="fp8", scale_block=128, d_ff=128, d_ff_shared=128)
+    base.update(over)
+    _run_full(get_config("toy", **base), act_quant=True)
+
+
+@pytest.mark.parametrize("over", [dict(n_tokens=250), dict(n_tokens=1000)])
+def test_persistent_down_act_quant_full(over):
+    """The full layer shape (d = 2560, f = 512, 384 experts) with the released checkpoint's
+    format: about 13 mostly short items per CU at 250 tokens, about 20 at 1000."""
+    _run_full(get_config("fp8block", **over), act_quant=True)
+
+
 @pytest.mark.parametrize("n", [300, 40, 4096, 8192])
 def test_router_full_fp32_weights(n):
     """FP32 router weights that are not bf16 values (mid and lo split terms nonzero) for a scattered
