@@ -3142,14 +3142,14 @@ __global__ __launch_bounds__(kThreads) void down_gemm_f8_persist_kernel(
         if (later >= 1) __builtin_amdgcn_s_waitcnt(FGS_VMCNT(G));
         else __builtin_amdgcn_s_waitcnt(FGS_VMCNT(0));
     };
-    // fragment addresses in buffer 0: H row wm*64 + lane%16, weight row wn*32 + lane%16 (+ the
-    // column fragment's offset), K chunks 2 (lane/16) and 2 (lane/16) + 1
+    // fragment addresses in buffer 0: H row wm*64 + lane%16, weight row wn*64 + lane%16 (+ 16 per
+    // column fragment: the wave's 64 columns are contiguous), K chunks 2 (lane/16) and 2 (lane/16) + 1
     uint32_t la[2], lb[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         const int ch = 2 * fg + c;
         la[c] = s0 + (wm * 64 + fr) * kDmaRowB + ((ch ^ (fr & 7)) << 4);
-        lb[c] = s0 + kBM * kDmaRowB + (wn * 32 + fr) * kDmaRowB + ((ch ^ (fr & 7)) << 4);
+        lb[c] = s0 + kBM * kDmaRowB + (wn * 64 + fr) * kDmaRowB + ((ch ^ (fr & 7)) << 4);
     }
 
     load_fetch_item();
@@ -3192,7 +3192,7 @@ __global__ __launch_bounds__(kThreads) void down_gemm_f8_persist_kernel(
                     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
                         for (int c = 0; c < 2; ++c)
-                            bf[ni][c] = lds_read16(lb[c] + cb * kStage + (ni < 2 ? ni * 16 : kBN / 2 + (ni - 2) * 16) * kDmaRowB);
+                            bf[ni][c] = lds_read16(lb[c] + cb * kStage + ni * 16 * kDmaRowB);
 #pragma unroll
                     for (int mi = 0; mi < LV; ++mi) {
 #pragma unroll
@@ -3200,24 +3200,23 @@ __global__ __launch_bounds__(kThreads) void down_gemm_f8_persist_kernel(
                         sa[mi] = lds_read_f32(slot + (uint32_t)(kt * kBM + wm * 64 + mi * 16 + fr) * 4u);
                     }
                 }
-                const float wlo = BLKW ? lds_read_f32(slot + 2048 + kt * 4) : 1.f;
-                const float whi = BLKW ? lds_read_f32(slot + 2048 + (nk + kt) * 4) : 1.f;
+                // the wave's 64 columns lie in one 128-column output block
+                const float wsc = BLKW ? lds_read_f32(slot + 2048 + ((wn < 2 ? 0 : nk) + kt) * 4) : 1.f;
                 __builtin_amdgcn_sched_barrier(0);
                 const bool last = kt + 1 == nk;
                 const bool more = gf > gs + 1;
-                if (more) {
-                    wait_stages(gf - gs - 2);   // stage gs + 1 landed; a later one may stay in flight
-                    lds_barrier();
-                }
+                if (more) wait_stages(gf - gs - 2);   // stage gs + 1 landed; a later one may stay in flight
+                // every wave has read buffer cb: it may be refilled, or at the item's end
+                // take the output staging
+                if (more || last) lds_barrier();
                 if (!last) fetch_next();   // stage gs + NB into buffer cb
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (LV > 0) {
                     f32x4_t p0[4], p1[4];
                     auto fold = [&](int mi, const f32x4_t (&pr)[4]) __attribute__((always_inline)) {
-                        const float clo = sa[mi] * wlo, chi = sa[mi] * whi;
+                        const float c = sa[mi] * wsc;
 #pragma unroll
                         for (int ni = 0; ni < 4; ++ni) {
-                            const float c = ni < 2 ? clo : chi;
 #pragma unroll
                             for (int qq = 0; qq < 4; ++qq) acc[mi][ni][qq] = fmaf(pr[ni][qq], c, acc[mi][ni][qq]);
                         }
@@ -3242,18 +3241,27 @@ __global__ __launch_bounds__(kThreads) void down_gemm_f8_persist_kernel(
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (last) {
-                    const uint32_t lane_off =
-                        ((uint32_t)(lane & 15) * (uint32_t)d + (uint32_t)(lane >> 4) * 4u) * 2u;
+                    // stage the output through this wave's own 2 KB of buffer cb (its activation
+                    // chunks: every fragment of the stage was read before the barrier, and only
+                    // this wave's next fetch, issued after these stores, writes there again)
+                    const uint32_t ob = s0 + cb * kStage + wave * kAPer * 1024;
+                    const uint32_t lane_off = ((uint32_t)(lane >> 3) * (uint32_t)d + (uint32_t)(lane & 7) * 8u) * 2u;
+                    float sc[4][4];
 #pragma unroll
                     for (int ni = 0; ni < 4; ++ni) {
-                        const int c0 = o0 + b_row_of(wn, ni);
-                        float sc[4] = {1.f, 1.f, 1.f, 1.f};
-                        if constexpr (!BLKW) slot_scales(slot + 2048, b_row_of(wn, ni), lane, sc);
 #pragma unroll
-                        for (int mi = 0; mi < LV; ++mi) {
-                            const int rb = wm * 64 + mi * 16;
-                            if (rb + (lane & 15) < m) store_bf16x4(Y + (size_t)(row0 + rb) * d + c0, lane_off, acc[mi][ni], sc);
-                        }
+                        for (int qq = 0; qq < 4; ++qq) sc[ni][qq] = 1.f;
+                        if constexpr (!BLKW) slot_scales(slot + 2048, wn * 64 + ni * 16, lane, sc[ni]);
+                    }
+#pragma unroll
+                    for (int mi = 0; mi < LV; ++mi) {
+                        const int rb = wm * 64 + mi * 16;
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni) stage_bf16x4(ob, ni, lane, acc[mi][ni], sc[ni]);
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            if (rb + 8 * h + (lane >> 3) < m)
+                                store_staged(ob, h, lane, Y + (size_t)(row0 + rb + 8 * h) * d + o0 + wn * 64, lane_off);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     if (more) fetch_next();
