@@ -1963,7 +1963,8 @@ __global__ __launch_bounds__(1024) void down_gemm_wide_persist_kernel(
     auto fetched = [&]() { return W8 ? gfb : gfa; };
 
     // this lane's fragment addresses in buffer 0 per 32-wide K half h: activation
-    // row wm*64 + lane%16, weight row wn*32 + lane%16, K chunk 4 h + lane/16
+    // row wm*64 + lane%16, weight row wn*64 + lane%16 (the wave's 64 columns are
+    // contiguous), K chunk 4 h + lane/16
     const uint32_t s0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;
     uint32_t la[2], lb[2];
 #pragma unroll
@@ -1971,9 +1972,9 @@ __global__ __launch_bounds__(1024) void down_gemm_wide_persist_kernel(
         const int c = 4 * h + fg;
         la[h] = s0 + kAOff + (wm * 64 + fr) * kDmaRowB + ((c ^ (fr & 7)) << 4);
         if constexpr (W8)
-            lb[h] = s0 + kBOff + (wn * 32 + fr) * kW8RowB + ((((c >> 1) ^ (fr >> 2)) & 3) << 4) + ((c & 1) << 3);
+            lb[h] = s0 + kBOff + (wn * 64 + fr) * kW8RowB + ((((c >> 1) ^ (fr >> 2)) & 3) << 4) + ((c & 1) << 3);
         else
-            lb[h] = s0 + kBOff + (wn * 32 + fr) * kDmaRowB + ((c ^ (fr & 7)) << 4);
+            lb[h] = s0 + kBOff + (wn * 64 + fr) * kDmaRowB + ((c ^ (fr & 7)) << 4);
     }
 
     if constexpr (!W8) load_a();
@@ -2016,7 +2017,7 @@ __global__ __launch_bounds__(1024) void down_gemm_wide_persist_kernel(
                         uint4 bf[4];
 #pragma unroll
                         for (int ni = 0; ni < 4; ++ni) {
-                            const uint32_t rb = (ni < 2 ? ni * 16 : kBN / 2 + (ni - 2) * 16) * kBRowB;
+                            const uint32_t rb = ni * 16 * kBRowB;
                             if constexpr (W8) bf[ni] = e4m3x8_to_bf16x8(lds_read8(pb + rb));
                             else bf[ni] = lds_read16(pb + rb);
                         }
@@ -2072,25 +2073,30 @@ __global__ __launch_bounds__(1024) void down_gemm_wide_persist_kernel(
             // barrier, the stores, and only then the fetches of this barrier
             compute();
             const bool more = fetched() > gs + 1;
-            if (more) {
-                wait_next();
-                lds_barrier();
-            }
+            if (more) wait_next();
+            // every wave is past its reads of buffers ca and cbw (refilled, or here
+            // lending this wave's own 2 KB of activation buffer ca to the output staging)
+            lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            // lane: row wm*64 + mi*16 + lane%16, columns o0 + b_row_of(wn, ni) + 4 (lane/16) .. +3
-            // (the lane index recomputed here rather than kept live through the K loop)
+            // lane: row wm*64 + mi*16 + lane%16, columns o0 + wn*64 + 16 ni + 4 (lane/16) .. +3,
+            // staged per sub-tile row and stored 16 bytes per lane (the lane index recomputed
+            // here rather than kept live through the K loop)
             const int ln = (int)__lane_id();
-            const uint32_t lane_off = ((uint32_t)(ln & 15) * (uint32_t)d + (uint32_t)(ln >> 4) * 4u) * 2u;
+            const uint32_t ob = s0 + kAOff + ca * kABuf + w * kAPerW * 1024;
+            const uint32_t lane_off = ((uint32_t)(ln >> 3) * (uint32_t)d + (uint32_t)(ln & 7) * 8u) * 2u;
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                const int c0 = o0 + b_row_of(wn, ni);
-                float sc[4] = {1.f, 1.f, 1.f, 1.f};
-                if constexpr (W8) slot_scales(s0 + kSOff + (q & 3) * 1024, b_row_of(wn, ni), ln, sc);
+            for (int mi = 0; mi < LV; ++mi) {
+                const int rb = wm * 64 + mi * 16;
 #pragma unroll
-                for (int mi = 0; mi < LV; ++mi) {
-                    const int rb = wm * 64 + mi * 16;
-                    if (rb + (ln & 15) < m) store_bf16x4(Y + (size_t)(row0 + rb) * d + c0, lane_off, acc[mi][ni], sc);
+                for (int ni = 0; ni < 4; ++ni) {
+                    float sc[4] = {1.f, 1.f, 1.f, 1.f};
+                    if constexpr (W8) slot_scales(s0 + kSOff + (q & 3) * 1024, wn * 64 + ni * 16, ln, sc);
+                    stage_bf16x4(ob, ni, ln, acc[mi][ni], sc);
                 }
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    if (rb + 8 * h + (ln >> 3) < m)
+                        store_staged(ob, h, ln, Y + (size_t)(row0 + rb + 8 * h) * d + o0 + wn * 64, lane_off);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (more) fetch_group(true);
