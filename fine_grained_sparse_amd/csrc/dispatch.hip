@@ -334,7 +334,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_scatter_kernel(
 }
 
 hipError_t launch_dispatch(const Plan &p) {
-    if (p.fused_route) return hipSuccess;   // done by the fused top-k kernel
+    if (p.fused_route || p.tail_dispatch) return hipSuccess;   // done by the top-k kernel
     if (p.N <= 64 && p.bm >= p.N) {   // one wave; every group fits one tile
         hipLaunchKernelGGL(dispatch_wave_kernel, dim3(1), dim3(64), 0, p.stream, p.ids, p.N, p.k, p.E, p.offsets,
                            p.exp_off_out, p.tiles, p.n_tiles, p.por, p.rop);

@@ -86,7 +86,7 @@ int check_desc(const moe_desc *d) {
 
 struct Layout {
     size_t partial, ids, tw, blk, offsets, tiles, n_tiles, tiles2, n_tiles2, por, rop, H, Y, w3, rflags, xq, xs, hq,
-        hs, hf, total;
+        hs, hf, route_cnt, total;
     int ks, kslice, nblk, max_tiles, max_tiles2, bm, ldh;
     bool stream, rgemm, aq;
 };
@@ -142,6 +142,7 @@ Layout layout_for(const moe_desc *d) {
     L.hq = take(cur, L.aq ? rows * L.ldh : 0);
     L.hs = take(cur, L.aq ? rows * (L.ldh / 128) * 4 : 0);
     L.hf = take(cur, L.aq && L.stream ? rows * L.ldh * 4 : 0);
+    L.route_cnt = take(cur, 4);
     L.total = cur;
     return L;
 }
@@ -262,6 +263,8 @@ int run_layer(const moe_desc *desc, const void *x, const float *router_w, const 
     p.rflags = L.rgemm ? (int32_t *)(ws + L.rflags) : nullptr;
     p.use_stream = L.stream;
     p.fused_route = L.stream && fused_route_ok(p.N, p.xdt);
+    p.tail_dispatch = L.stream && !p.fused_route && tail_dispatch_ok(p.N, p.bm);
+    p.route_cnt = (int32_t *)(ws + L.route_cnt);
     p.stream = (hipStream_t)stream;
     p.aq = L.aq;
     if (L.aq) {

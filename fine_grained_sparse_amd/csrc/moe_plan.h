@@ -54,6 +54,8 @@ struct Plan {
     float *hf;           // [N*k + N][ldh] FP32 hidden activations (stream path, before quantisation)
     bool use_stream;     // decode-shaped expert path; otherwise the grouped GEMMs
     bool fused_route;    // top-k and dispatch in one kernel (fused_route_ok)
+    bool tail_dispatch;  // the last top-k workgroup lays out the dispatch (tail_dispatch_ok)
+    int32_t *route_cnt;  // [1] top-k workgroups done; zeroed by the router kernel of each call
     hipStream_t stream;
 };
 
@@ -131,6 +133,14 @@ constexpr int kFusedRouteN = FGS_FUSED_ROUTE_N;   // 0 switches the fusion off
 static_assert(kFusedRouteN >= 0 && kFusedRouteN <= 7, "one workgroup of at most 7 waves");
 constexpr int kFusedRouteCap = kFusedRouteN > 0 ? kFusedRouteN : 1;   // array and workgroup bounds
 inline bool fused_route_ok(int N, int xdt) { return N >= 1 && N <= kFusedRouteN && !router_gemm(N, xdt); }
+// Past kFusedRouteN and up to 64 tokens (one wave of dispatch, every group in
+// one tile of the stream path) the top-k runs one workgroup per token as
+// usual, and the workgroup that finishes last (a counter the router kernel of
+// the same call zeroes) lays out the dispatch: one launch less per step.
+#ifndef FGS_TAIL_DISPATCH
+#define FGS_TAIL_DISPATCH 1
+#endif
+inline bool tail_dispatch_ok(int N, int bm) { return FGS_TAIL_DISPATCH && N >= 1 && N <= 64 && bm >= N; }
 // k-slices of the router GEMM: 3 c slices, c per split term (hi, mid, lo),
 // so that a slice never straddles two terms and the slices of all-zero terms
 // can be skipped; c <= 4 divides the d/64 K stages of a term and is raised

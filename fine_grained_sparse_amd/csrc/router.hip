@@ -61,7 +61,8 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4 &a, const uint4 &b, 
 template <int MT, int NT, int KW = 1>
 __global__ __launch_bounds__(256) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ rw, float *__restrict__ partial,
-    int N, int d, int E, int kslice, int n_tb, int n_eb, int n_jobs) {
+    int N, int d, int E, int kslice, int n_tb, int n_eb, int n_jobs, int32_t *route_cnt) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *route_cnt = 0;   // for the top-k's last-workgroup dispatch
     const int lane = threadIdx.x & 63;
     const int kw = KW > 1 ? (int)(threadIdx.x >> 6) : 0;
     const int job = KW > 1 ? (int)blockIdx.x : (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
@@ -158,7 +159,8 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 // Plain FP32 FMA router for FP32 activations: one thread per (token, expert).
 __global__ __launch_bounds__(256) void router_f32_kernel(
     const float *__restrict__ x, const float *__restrict__ rw, float *__restrict__ partial,
-    int N, int d, int E) {
+    int N, int d, int E, int32_t *route_cnt) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *route_cnt = 0;   // for the top-k's last-workgroup dispatch
     long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (long)N * E) return;
     int t = (int)(idx / E), e = (int)(idx % E);
@@ -180,7 +182,7 @@ hipError_t launch_router(const Plan &p) {
         long total = (long)p.N * p.E;
         dim3 grid((unsigned)((total + 255) / 256));
         hipLaunchKernelGGL(router_f32_kernel, grid, dim3(256), 0, p.stream,
-                           (const float *)p.x, p.rw, p.partial, p.N, p.d, p.E);
+                           (const float *)p.x, p.rw, p.partial, p.N, p.d, p.E, p.route_cnt);
         return hipGetLastError();
     }
     if (router_gemm(p.N, p.xdt)) return launch_router_gemm(p, p.w3);
@@ -196,17 +198,17 @@ hipError_t launch_router(const Plan &p) {
         // (N = 32, d = 2560: router 6.3 us with one wave, 5.1 with two, 4.8 with four)
         if (p.kslice % 128 == 0)
             hipLaunchKernelGGL((router_mfma_kernel<2, 1, 4>), dim3(n_jobs), dim3(256), 0, p.stream,
-                               x, p.rw, p.partial, p.N, p.d, p.E, p.kslice, n_tb, n_eb, n_jobs);
+                               x, p.rw, p.partial, p.N, p.d, p.E, p.kslice, n_tb, n_eb, n_jobs, p.route_cnt);
         else if (p.kslice % 64 == 0)
             hipLaunchKernelGGL((router_mfma_kernel<2, 1, 2>), dim3(n_jobs), dim3(128), 0, p.stream,
-                               x, p.rw, p.partial, p.N, p.d, p.E, p.kslice, n_tb, n_eb, n_jobs);
+                               x, p.rw, p.partial, p.N, p.d, p.E, p.kslice, n_tb, n_eb, n_jobs, p.route_cnt);
         else
             hipLaunchKernelGGL((router_mfma_kernel<2, 1>), dim3(n_jobs), dim3(64), 0, p.stream,
-                               x, p.rw, p.partial, p.N, p.d, p.E, p.kslice, n_tb, n_eb, n_jobs);
+                               x, p.rw, p.partial, p.N, p.d, p.E, p.kslice, n_tb, n_eb, n_jobs, p.route_cnt);
     } else {
         dim3 grid((n_jobs + 3) / 4);
         hipLaunchKernelGGL((router_mfma_kernel<4, 4>), grid, dim3(256), 0, p.stream,
-                           x, p.rw, p.partial, p.N, p.d, p.E, p.kslice, n_tb, n_eb, n_jobs);
+                           x, p.rw, p.partial, p.N, p.d, p.E, p.kslice, n_tb, n_eb, n_jobs, p.route_cnt);
     }
     return hipGetLastError();
 }

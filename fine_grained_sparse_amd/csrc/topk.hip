@@ -249,6 +249,37 @@ __global__ __launch_bounds__(64 * kFusedRouteCap) void topk_dispatch_kernel(
     dispatch_small(sids, N, k, E, g_offsets, g_exp_off, tiles, n_tiles, por, rop);
 }
 
+// Top-k of one token per workgroup (one wave, router_mfma partial sums, no
+// split-term flags) with the dispatch laid out by the workgroup that finishes
+// last: each workgroup publishes its ids (release fence), counts itself on
+// route_cnt (zeroed by this call's router kernel), and the one that brings
+// the count to N reads every token's ids after an acquire fence and runs
+// dispatch_small.  No workgroup waits for another.
+template <int VPL>
+__global__ __launch_bounds__(64) void topk_tail_kernel(
+    const float *__restrict__ partial, int ks, const float *__restrict__ bias, float *__restrict__ logits_out,
+    int32_t *ids, float *__restrict__ tw, float *__restrict__ gap, int N, int E, int k, bool renorm,
+    int32_t *route_cnt, int32_t *g_offsets, int32_t *g_exp_off, int32_t *tiles, int32_t *n_tiles, int32_t *por,
+    int32_t *rop) {
+    const int lane = threadIdx.x, t = blockIdx.x;
+    float bv[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        const int e = lane + 64 * v;
+        bv[v] = bias[e < E ? e : 0];
+    }
+    float h[VPL];
+    sum_slices<VPL>(partial + (size_t)t * E, (size_t)N * E, ks, lane, E, h);
+    select_token<VPL>(h, bv, lane, t, E, k, renorm, logits_out, ids, tw, gap);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    int done = 0;
+    if (lane == 0) done = __hip_atomic_fetch_add(route_cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    done = __shfl(done, 0, kWave);
+    if (done != N - 1) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    dispatch_small(ids, N, k, E, g_offsets, g_exp_off, tiles, n_tiles, por, rop);
+}
+
 hipError_t launch_topk(const Plan &p) {
     // one token per wave; small batches put each wave in a workgroup of its own,
     // so the selections spread over as many CUs (N = 32: 6.0 against 7.1 us
@@ -268,6 +299,20 @@ hipError_t launch_topk(const Plan &p) {
         else if (vpl <= 8) FGS_TOPKD(8);
         else FGS_TOPKD(16);
 #undef FGS_TOPKD
+        return hipGetLastError();
+    }
+    if (p.tail_dispatch) {   // one wave per token, the last one lays out the dispatch
+#define FGS_TOPKT(V)                                                                                        \
+    hipLaunchKernelGGL((topk_tail_kernel<V>), dim3(p.N), dim3(64), 0, p.stream, p.partial, p.ks, p.rb, p.logits, \
+                       p.ids, p.tw, p.gap, p.N, p.E, p.k, (p.flags & MOE_FLAG_RENORMALIZE) != 0, p.route_cnt,     \
+                       p.offsets, p.exp_off_out, p.tiles, p.n_tiles, p.por, p.rop)
+        if (vpl <= 1) FGS_TOPKT(1);
+        else if (vpl <= 2) FGS_TOPKT(2);
+        else if (vpl <= 4) FGS_TOPKT(4);
+        else if (vpl <= 6) FGS_TOPKT(6);
+        else if (vpl <= 8) FGS_TOPKT(8);
+        else FGS_TOPKT(16);
+#undef FGS_TOPKT
         return hipGetLastError();
     }
 #define FGS_TOPK2(V, F)                                                                             \
