@@ -59,9 +59,11 @@ def test_toy(n):
     _run_full(get_config("toy", n_tokens=n))
 
 
-@pytest.mark.parametrize("n", [1, 2, 7, 32, 64, 65, 130, 192])
+@pytest.mark.parametrize("n", [1, 2, 5, 7, 32, 64, 65, 130, 192])
 def test_decode_full_shape(n):
-    """Full-size layer on the stream path (above 64 tokens: several 64-row tiles per group)."""
+    """Full-size layer on the stream path (above 64 tokens: several 64-row tiles per group); up to
+    4 tokens top-k and dispatch share one workgroup, from 5 to 64 the last top-k workgroup lays out
+    the dispatch, above that the dispatch kernels run on their own."""
     _run_full(get_config("decode", n_tokens=n))
 
 
