@@ -95,6 +95,16 @@ def test_toy_variants(over, n):
     _run_full(get_config("toy", **(dict(over, n_tokens=n) if n else over)))
 
 
+@pytest.mark.parametrize("over", [
+    dict(n_tokens=40, top_k=1), dict(n_tokens=40, top_k=8), dict(n_tokens=9, n_experts=6, top_k=6),
+    dict(n_tokens=64, n_experts=1024, top_k=8), dict(n_tokens=33, x_dtype="bf16"), dict(n_tokens=5, x_dtype="bf16"),
+])
+def test_tail_dispatch_variants(over):
+    """5 to 64 tokens on the stream path: the dispatch is laid out by the last top-k workgroup to
+    finish (k = 1 and 8, every expert selected, 1024 experts, FP32 and bf16 x)."""
+    _run_full(get_config("toy", **over))
+
+
 def test_accumulate_into_residual():
     _run_full(get_config("toy", x_dtype="bf16", n_tokens=50), residual=True)
     _run_full(get_config("toy", n_tokens=20), residual=True)
