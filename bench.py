@@ -20,7 +20,9 @@ sample of the same workload (one thread and all threads).
 
 The default run (no --workload, no --tokens) also measures the other
 workloads and puts them in `sub_records`: the prefill chunk (N=8192, the
-metric's MFMA half), FP8 weights (N=4096), skewed Zipf routing (N=16384),
+metric's MFMA half), FP8 weights (N=4096), the released checkpoint's format
+(128 x 128 block-scaled E4M3 weights with 1 x 128 activation quantisation,
+N=4096), skewed Zipf routing (N=16384, also with activation quantisation),
 decode batches of 1 and 8 tokens, and the all-hot probe (every token routed to
 the same six experts: the grouped GEMMs' compute ceiling).
 """
@@ -43,10 +45,11 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 METRIC = "MoE-layer tokens/s + % HBM roofline (decode N<=64), % MFMA peak (prefill)"
 WORKLOADS = ["decode", "prefill", "fp8", "fp8block", "zipf", "hot", "toy"]
 
-# sub-records of the default run: (name, workload, token override, steps, warmup)
-SUB_RECORDS = [("prefill", "prefill", None, 50, 5), ("fp8", "fp8", None, 50, 5), ("zipf", "zipf", None, 30, 5),
-               ("decode_N1", "decode", 1, 400, 40), ("decode_N8", "decode", 8, 300, 30),
-               ("hot", "hot", None, 30, 5)]
+# sub-records of the default run: (name, workload, token override, steps, warmup, 1 x 128 activation quantisation)
+SUB_RECORDS = [("prefill", "prefill", None, 50, 5, False), ("fp8", "fp8", None, 50, 5, False),
+               ("fp8block_aq", "fp8block", None, 50, 5, True), ("zipf", "zipf", None, 30, 5, False),
+               ("zipf_aq", "zipf", None, 30, 5, True), ("decode_N1", "decode", 1, 400, 40, False),
+               ("decode_N8", "decode", 8, 300, 30, False), ("hot", "hot", None, 30, 5, False)]
 
 
 def parse():
@@ -487,11 +490,12 @@ def main():
 
     if default_run and not args.no_sub:
         subs = {}
-        for name, wl, ntok, steps, warm in SUB_RECORDS:
+        for name, wl, ntok, steps, warm, aq in SUB_RECORDS:
             scfg = get_config(wl) if ntok is None else get_config(wl, n_tokens=ntok)
             sl = default_layers(scfg)
             try:
-                subs[name] = sub_record(measure(scfg, steps, warm, sl, stride=args.event_stride, graph=False))
+                subs[name] = sub_record(measure(scfg, steps, warm, sl, act_quant=aq, stride=args.event_stride,
+                                                graph=False))
             except Exception as exc:   # one workload failing is reported, not fatal to the line
                 subs[name] = {"error": f"{type(exc).__name__}: {exc}"}
             log(f"sub-record {name}: {json.dumps(subs[name])[:200]}")
